@@ -1,0 +1,169 @@
+"""fp64 CPU oracle for conv2d -> BatchNorm -> SiLU.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path never does. It
+shares no code with the HIP library (``conv2d_batchnorm_silu_amd``) and does
+not import it.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, no contraction); this
+module builds it with gcc and wraps it with ctypes. Every function takes the
+exact values the GPU path reads (fp16 or fp32 arrays) and widens them to fp64,
+which is exact.
+
+What each function follows:
+  * ``conv2d`` -- the convolution of "Fusing an Epilogue" (teenygrad docs),
+    section "The problem": cross-correlation, symmetric zero padding,
+    NHWC x, OHWI w, NHWC output.
+  * ``batchnorm`` -- same section: batch norm as a per-channel multiply and
+    add, written in its unfolded inference form
+    gamma * (t - mean) / sqrt(var + eps) + beta.
+  * ``silu`` -- same section: v * sigmoid(v) with the logistic sigmoid.
+  * ``conv_bn_silu`` / ``conv_bn_silu_at`` -- same page, section "The shape
+    of it": the three applied in order to every output element.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lock = threading.Lock()
+_lib = None
+
+_dp = ctypes.POINTER(ctypes.c_double)
+_llp = ctypes.POINTER(ctypes.c_longlong)
+
+
+def build(force: bool = True) -> str:
+    """Compile ``oracle.c`` into ``liboracle.so`` with gcc (no fast-math, no
+    floating-point contraction)."""
+    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
+        return _LIB
+    tmp = _LIB + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
+           "-std=c99", "-Wall", "-Werror", "-o", tmp, _SRC, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    with _lock:
+        if _lib is None:
+            build(force=False)
+            lib = ctypes.CDLL(_LIB)
+            i = ctypes.c_int
+            lib.oracle_out_extent.restype = ctypes.c_longlong
+            lib.oracle_out_extent.argtypes = [ctypes.c_longlong] * 4
+            lib.oracle_conv2d.restype = i
+            lib.oracle_conv2d.argtypes = [_dp, _dp] + [i] * 9 + [_dp, i]
+            lib.oracle_batchnorm.restype = None
+            lib.oracle_batchnorm.argtypes = [_dp, ctypes.c_longlong, i, _dp, _dp, _dp, _dp,
+                                             ctypes.c_double, _dp]
+            lib.oracle_silu.restype = None
+            lib.oracle_silu.argtypes = [_dp, ctypes.c_longlong, _dp]
+            lib.oracle_conv_bn_silu.restype = i
+            lib.oracle_conv_bn_silu.argtypes = ([_dp, _dp] + [i] * 9 + [_dp] * 4
+                                                + [ctypes.c_double, _dp, i])
+            lib.oracle_conv_bn_silu_at.restype = i
+            lib.oracle_conv_bn_silu_at.argtypes = ([_dp, _dp] + [i] * 9 + [_dp] * 4
+                                                   + [ctypes.c_double, _llp, ctypes.c_longlong, _dp])
+            _lib = lib
+    return _lib
+
+
+def _f64(a) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(a), dtype=np.float64)
+
+
+def _ptr(a: np.ndarray):
+    return a.ctypes.data_as(_dp)
+
+
+def default_threads() -> int:
+    return max(1, min(os.cpu_count() or 1, 64))
+
+
+def out_extent(n_in: int, k: int, stride: int, pad: int) -> int:
+    """floor((n_in + 2 pad - k) / stride) + 1, or 0 when the window does not fit."""
+    return int(_load().oracle_out_extent(n_in, k, stride, pad))
+
+
+def _geom(x, w, stride, pad):
+    N, H, W, C_in = x.shape
+    C_out, kh, kw, C_in_w = w.shape
+    if C_in_w != C_in:
+        raise ValueError("C_in of x and w differ")
+    P, Q = out_extent(H, kh, stride, pad), out_extent(W, kw, stride, pad)
+    if P == 0 or Q == 0:
+        raise ValueError("window larger than the padded input")
+    return N, H, W, C_in, C_out, kh, kw, P, Q
+
+
+def conv2d(x, w, stride: int, pad: int, threads: int | None = None) -> np.ndarray:
+    """Convolution alone. x [N,H,W,C_in], w [C_out,kh,kw,C_in] -> [N,P,Q,C_out] fp64."""
+    x, w = _f64(x), _f64(w)
+    N, H, W, C_in, C_out, kh, kw, P, Q = _geom(x, w, stride, pad)
+    out = np.empty((N, P, Q, C_out), np.float64)
+    rc = _load().oracle_conv2d(_ptr(x), _ptr(w), N, H, W, C_in, C_out, kh, kw, stride, pad,
+                               _ptr(out), threads or default_threads())
+    if rc:
+        raise ValueError("oracle_conv2d rejected the arguments (%d)" % rc)
+    return out
+
+
+def batchnorm(t, gamma, beta, mean, var, eps: float) -> np.ndarray:
+    """Inference batch norm over the last (channel) axis, unfolded form."""
+    t = _f64(t)
+    C = t.shape[-1]
+    g, b, m, v = (_f64(a).reshape(C) for a in (gamma, beta, mean, var))
+    out = np.empty_like(t)
+    _load().oracle_batchnorm(_ptr(t), t.size // C, C, _ptr(g), _ptr(b), _ptr(m), _ptr(v),
+                             float(eps), _ptr(out))
+    return out
+
+
+def silu(t) -> np.ndarray:
+    """v * sigmoid(v), elementwise."""
+    t = _f64(t)
+    out = np.empty_like(t)
+    _load().oracle_silu(_ptr(t), t.size, _ptr(out))
+    return out
+
+
+def conv_bn_silu(x, w, gamma, beta, mean, var, eps: float, stride: int, pad: int,
+                 threads: int | None = None) -> np.ndarray:
+    """The whole path: silu(batchnorm(conv2d(x, w))), fp64 [N,P,Q,C_out]."""
+    x, w = _f64(x), _f64(w)
+    N, H, W, C_in, C_out, kh, kw, P, Q = _geom(x, w, stride, pad)
+    g, b, m, v = (_f64(a).reshape(C_out) for a in (gamma, beta, mean, var))
+    out = np.empty((N, P, Q, C_out), np.float64)
+    rc = _load().oracle_conv_bn_silu(_ptr(x), _ptr(w), N, H, W, C_in, C_out, kh, kw, stride, pad,
+                                     _ptr(g), _ptr(b), _ptr(m), _ptr(v), float(eps), _ptr(out),
+                                     threads or default_threads())
+    if rc:
+        raise ValueError("oracle_conv_bn_silu rejected the arguments (%d)" % rc)
+    return out
+
+
+def conv_bn_silu_at(x, w, gamma, beta, mean, var, eps: float, stride: int, pad: int,
+                    flat_idx) -> np.ndarray:
+    """The whole path at selected flat indices into the [N,P,Q,C_out] output."""
+    x, w = _f64(x), _f64(w)
+    N, H, W, C_in, C_out, kh, kw, P, Q = _geom(x, w, stride, pad)
+    g, b, m, v = (_f64(a).reshape(C_out) for a in (gamma, beta, mean, var))
+    idx = np.ascontiguousarray(np.asarray(flat_idx), dtype=np.int64)
+    out = np.empty(idx.shape, np.float64)
+    rc = _load().oracle_conv_bn_silu_at(_ptr(x), _ptr(w), N, H, W, C_in, C_out, kh, kw, stride,
+                                        pad, _ptr(g), _ptr(b), _ptr(m), _ptr(v), float(eps),
+                                        idx.ctypes.data_as(_llp), idx.size, _ptr(out))
+    if rc:
+        raise ValueError("oracle_conv_bn_silu_at rejected the arguments (%d)" % rc)
+    return out

@@ -1,0 +1,278 @@
+"""Pins for the fp64 CPU oracle, against things other than the oracle itself.
+
+Each pin is chosen so a plausible slip in the oracle (a dropped tap or
+channel, a flipped kernel, a swapped kh/kw, asymmetric padding, eps outside
+the root, a wrong sign in the sigmoid) fails at least one test:
+  * brute force on tiny shapes with an explicitly padded copy and a different
+    loop nest (channels outermost, math.fsum);
+  * closed forms (all-ones inputs count in-bounds taps; one-hot inputs read
+    the filter back in place; a centred delta filter is the identity);
+  * library routines for special cases (1x1 conv is a matmul; torch's CPU
+    conv2d / batch_norm / silu in fp64);
+  * linearity, the BatchNorm fold identity, the BatchNorm identity case;
+  * SiLU facts: SiLU(0) = 0, SiLU(-v) = SiLU(v) - v, and its minimum
+    -W(1/e) at v = -1 - W(1/e) (W = Lambert W).
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from conv2d_batchnorm_silu_amd.inputs import WORKLOADS, make_inputs
+
+
+def _rand(rng, shape):
+    return rng.standard_normal(shape)
+
+
+def _brute_conv(x, w, stride, pad):
+    """Reference written independently: pad x with zeros explicitly, then loop
+    output channel outermost and sum every window with math.fsum."""
+    N, H, W, C = x.shape
+    K, kh, kw, _ = w.shape
+    xp = np.zeros((N, H + 2 * pad, W + 2 * pad, C))
+    xp[:, pad:pad + H, pad:pad + W, :] = x
+    P = (H + 2 * pad - kh) // stride + 1
+    Q = (W + 2 * pad - kw) // stride + 1
+    out = np.zeros((N, P, Q, K))
+    for k in range(K):
+        for n in range(N):
+            for p in range(P):
+                for q in range(Q):
+                    win = xp[n, p * stride:p * stride + kh, q * stride:q * stride + kw, :]
+                    out[n, p, q, k] = math.fsum((win * w[k]).ravel().tolist())
+    return out
+
+
+def _tiny_shapes(count, seed):
+    rng = np.random.default_rng(seed)
+    shapes = []
+    while len(shapes) < count:
+        kh = int(rng.choice([1, 2, 3, 5]))
+        kw = int(rng.choice([1, 2, 3, 5]))
+        s = int(rng.choice([1, 2, 3]))
+        p = int(rng.choice([0, 1, 2]))
+        H, W = int(rng.integers(1, 8)), int(rng.integers(1, 8))
+        if H + 2 * p < kh or W + 2 * p < kw:
+            continue
+        shapes.append((int(rng.integers(1, 3)), H, W, int(rng.integers(1, 6)),
+                       int(rng.integers(1, 6)), kh, kw, s, p))
+    return shapes
+
+
+@pytest.mark.parametrize("shape", _tiny_shapes(160, 7))
+def test_conv_matches_brute_force(shape):
+    N, H, W, C_in, C_out, kh, kw, s, p = shape
+    rng = np.random.default_rng(hash(shape) & 0xFFFF)
+    x = _rand(rng, (N, H, W, C_in))
+    w = _rand(rng, (C_out, kh, kw, C_in))
+    got = oracle.conv2d(x, w, s, p, threads=2)
+    ref = _brute_conv(x, w, s, p)
+    assert got.shape == ref.shape
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def _taps_in_bounds(o, stride, pad, k, n_in):
+    return sum(1 for r in range(k) if 0 <= o * stride - pad + r < n_in)
+
+
+@pytest.mark.parametrize("name", ["tiny_f32_3x3", "stem3x3s2_k16", "conv7x7_c64_k64"])
+def test_conv_all_ones_counts_taps(name):
+    wl = WORKLOADS[name]
+    # Small batch, full spatial geometry of the workload.
+    H, W, C = wl.H, wl.W, min(wl.C_in, 4)
+    x = np.ones((1, H, W, C))
+    w = np.ones((2, wl.kh, wl.kw, C))
+    got = oracle.conv2d(x, w, wl.stride, wl.pad)
+    assert got.shape == (1, wl.P, wl.Q, 2)
+    for p in range(wl.P):
+        rows = _taps_in_bounds(p, wl.stride, wl.pad, wl.kh, H)
+        for q in range(wl.Q):
+            cols = _taps_in_bounds(q, wl.stride, wl.pad, wl.kw, W)
+            assert got[0, p, q, 0] == got[0, p, q, 1] == C * rows * cols
+
+
+def test_conv_all_ones_known_values():
+    # 224x224 RGB, 3x3, stride 2, pad 1: corner window holds 2x2 taps, interior 3x3.
+    got = oracle.conv2d(np.ones((1, 224, 224, 3)), np.ones((1, 3, 3, 3)), 2, 1)
+    assert got[0, 0, 0, 0] == 12 and got[0, 5, 7, 0] == 27 and got[0, 111, 111, 0] == 27
+    # 56x56x64, 7x7, pad 3: corner 4x4 taps, interior 7x7.
+    got = oracle.conv2d(np.ones((1, 56, 56, 64)), np.ones((1, 7, 7, 64)), 1, 3)
+    assert got[0, 0, 0, 0] == 1024 and got[0, 20, 20, 0] == 64 * 49 and got[0, 55, 0, 0] == 1024
+
+
+@pytest.mark.parametrize("kh,kw,s,p", [(3, 3, 1, 1), (2, 3, 2, 1), (5, 1, 1, 2), (3, 5, 3, 2)])
+def test_conv_one_hot_reads_filter_in_place(kh, kw, s, p):
+    rng = np.random.default_rng(11)
+    N, H, W, C_in, C_out = 2, 7, 8, 3, 4
+    w = _rand(rng, (C_out, kh, kw, C_in))
+    n0, h0, w0, c0 = 1, 4, 3, 2
+    x = np.zeros((N, H, W, C_in))
+    x[n0, h0, w0, c0] = 1.0
+    got = oracle.conv2d(x, w, s, p)
+    P, Q = got.shape[1:3]
+    for n, pp, qq, k in itertools.product(range(N), range(P), range(Q), range(C_out)):
+        r, t = h0 - pp * s + p, w0 - qq * s + p
+        want = w[k, r, t, c0] if (n == n0 and 0 <= r < kh and 0 <= t < kw) else 0.0
+        assert got[n, pp, qq, k] == want
+
+
+def test_conv_centred_delta_is_identity():
+    rng = np.random.default_rng(3)
+    C = 5
+    x = _rand(rng, (2, 9, 6, C))
+    w = np.zeros((C, 3, 3, C))
+    for c in range(C):
+        w[c, 1, 1, c] = 1.0
+    np.testing.assert_array_equal(oracle.conv2d(x, w, 1, 1), x)
+
+
+@pytest.mark.parametrize("C_in,C_out", [(64, 256), (3, 16), (17, 33)])
+def test_conv_1x1_is_matmul(C_in, C_out):
+    rng = np.random.default_rng(C_in)
+    x = _rand(rng, (3, 5, 7, C_in))
+    w = _rand(rng, (C_out, 1, 1, C_in))
+    got = oracle.conv2d(x, w, 1, 0)
+    ref = (x.reshape(-1, C_in) @ w.reshape(C_out, C_in).T).reshape(3, 5, 7, C_out)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_conv_linearity():
+    rng = np.random.default_rng(5)
+    x1, x2 = _rand(rng, (2, 6, 7, 4)), _rand(rng, (2, 6, 7, 4))
+    w1, w2 = _rand(rng, (3, 3, 3, 4)), _rand(rng, (3, 3, 3, 4))
+    a, b = 0.75, -1.5
+    lhs = oracle.conv2d(a * x1 + b * x2, w1, 2, 1)
+    rhs = a * oracle.conv2d(x1, w1, 2, 1) + b * oracle.conv2d(x2, w1, 2, 1)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+    lhs = oracle.conv2d(x1, a * w1 + b * w2, 2, 1)
+    rhs = a * oracle.conv2d(x1, w1, 2, 1) + b * oracle.conv2d(x1, w2, 2, 1)
+    np.testing.assert_allclose(lhs, rhs, rtol=1e-12, atol=1e-12)
+
+
+def test_against_torch_cpu_fp64():
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    for name in ["tiny_f32_3x3"]:
+        wl = WORKLOADS[name]
+        d = make_inputs(wl)
+        got = oracle.conv_bn_silu(d["x"], d["w"], d["gamma"], d["beta"], d["mean"], d["var"],
+                                  float(d["eps"]), wl.stride, wl.pad)
+        xt = torch.from_numpy(d["x"].astype(np.float64)).permute(0, 3, 1, 2)
+        wt = torch.from_numpy(d["w"].astype(np.float64)).permute(0, 3, 1, 2)
+        t = F.conv2d(xt, wt, stride=wl.stride, padding=wl.pad)
+        t = F.batch_norm(t, torch.from_numpy(d["mean"].astype(np.float64)),
+                         torch.from_numpy(d["var"].astype(np.float64)),
+                         torch.from_numpy(d["gamma"].astype(np.float64)),
+                         torch.from_numpy(d["beta"].astype(np.float64)),
+                         training=False, eps=float(d["eps"]))
+        ref = F.silu(t).permute(0, 2, 3, 1).numpy()
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # Non-square windows and strides, fp64 random data.
+    rng = np.random.default_rng(9)
+    for (kh, kw, s, p) in [(3, 5, 2, 2), (7, 7, 1, 3), (1, 1, 2, 0)]:
+        x = _rand(rng, (2, 11, 10, 6))
+        w = _rand(rng, (5, kh, kw, 6))
+        ref = F.conv2d(torch.from_numpy(x).permute(0, 3, 1, 2),
+                       torch.from_numpy(w).permute(0, 3, 1, 2), stride=s, padding=p)
+        np.testing.assert_allclose(oracle.conv2d(x, w, s, p), ref.permute(0, 2, 3, 1).numpy(),
+                                   rtol=1e-12, atol=1e-12)
+
+
+def test_batchnorm_identity_case():
+    rng = np.random.default_rng(2)
+    t = _rand(rng, (50, 6))
+    var = rng.uniform(0.5, 2.0, 6)
+    mean = _rand(rng, 6)
+    eps = 1e-5
+    gamma = np.sqrt(var + eps)
+    out = oracle.batchnorm(t, gamma, mean, mean, var, eps)
+    np.testing.assert_allclose(out, t, rtol=0, atol=4e-15 * (1 + np.abs(t).max() + np.abs(mean).max()))
+
+
+def test_batchnorm_fold_identity():
+    """The per-channel fold scale = gamma/sqrt(var+eps), bias = beta - mean*scale
+    gives the same values as the unfolded form (to fp64 rounding)."""
+    rng = np.random.default_rng(4)
+    C = 9
+    t = _rand(rng, (40, C)) * 3
+    gamma, beta = rng.uniform(0.5, 1.5, C), _rand(rng, C)
+    mean, var = _rand(rng, C), rng.uniform(0.5, 2.0, C)
+    eps = 1e-5
+    scale = gamma / np.sqrt(var + eps)
+    bias = beta - mean * scale
+    np.testing.assert_allclose(oracle.batchnorm(t, gamma, beta, mean, var, eps), t * scale + bias,
+                               rtol=1e-13, atol=1e-13)
+
+
+def test_batchnorm_against_torch():
+    torch = pytest.importorskip("torch")
+    import torch.nn.functional as F
+    rng = np.random.default_rng(6)
+    t = _rand(rng, (3, 4, 5, 7))
+    g, b, m, v = rng.uniform(0.5, 1.5, 7), _rand(rng, 7), _rand(rng, 7), rng.uniform(0.5, 2, 7)
+    ref = F.batch_norm(torch.from_numpy(t).permute(0, 3, 1, 2), torch.from_numpy(m),
+                       torch.from_numpy(v), torch.from_numpy(g), torch.from_numpy(b),
+                       training=False, eps=1e-3).permute(0, 2, 3, 1).numpy()
+    np.testing.assert_allclose(oracle.batchnorm(t, g, b, m, v, 1e-3), ref, rtol=1e-13, atol=1e-13)
+
+
+def test_silu_facts():
+    assert oracle.silu(np.array([0.0]))[0] == 0.0
+    v = np.linspace(-30, 30, 6001)
+    s = oracle.silu(v)
+    np.testing.assert_allclose(oracle.silu(-v), s - v, rtol=0, atol=1e-13)
+    from scipy.special import lambertw
+    w1e = float(lambertw(1.0 / math.e).real)
+    vmin = -1.0 - w1e
+    smin = oracle.silu(np.array([vmin]))[0]
+    assert abs(smin - (-w1e)) < 1e-15
+    assert s.min() >= smin - 1e-15
+    big = np.array([40.0, 100.0, 700.0])
+    np.testing.assert_allclose(oracle.silu(big) / big, 1.0, rtol=1e-15)
+    neg = oracle.silu(np.array([-800.0, -1e4]))
+    assert np.all(neg == 0.0) and not np.any(np.isnan(neg))
+    # Logistic form, checked against torch in fp64.
+    torch = pytest.importorskip("torch")
+    ref = torch.nn.functional.silu(torch.from_numpy(v)).numpy()
+    np.testing.assert_allclose(s, ref, rtol=1e-14, atol=1e-15)
+
+
+def test_fused_equals_composition_and_sampling():
+    wl = WORKLOADS["tiny_f32_3x3"]
+    d = make_inputs(wl)
+    args = (d["gamma"], d["beta"], d["mean"], d["var"], float(d["eps"]))
+    fused = oracle.conv_bn_silu(d["x"], d["w"], *args, wl.stride, wl.pad)
+    comp = oracle.silu(oracle.batchnorm(oracle.conv2d(d["x"], d["w"], wl.stride, wl.pad), *args))
+    np.testing.assert_array_equal(fused, comp)
+    idx = np.array([0, 1, 17, 255, 1000, fused.size - 1])
+    np.testing.assert_array_equal(
+        oracle.conv_bn_silu_at(d["x"], d["w"], *args, wl.stride, wl.pad, idx), fused.ravel()[idx])
+
+
+def test_thread_count_does_not_change_results():
+    rng = np.random.default_rng(8)
+    x = _rand(rng, (3, 13, 11, 5))
+    w = _rand(rng, (6, 3, 3, 5))
+    outs = [oracle.conv2d(x, w, 1, 1, threads=t) for t in (1, 2, 3, 8)]
+    for o in outs[1:]:
+        np.testing.assert_array_equal(o, outs[0])
+
+
+def test_out_extent_of_workloads():
+    want = {"tiny_f32_3x3": 16, "conv1x1_c64_k256": 56, "conv3x3_c128_k128": 28,
+            "stem3x3s2_k16": 112, "stem3x3s2_k24": 112, "conv7x7_c64_k64": 56}
+    for name, P in want.items():
+        wl = WORKLOADS[name]
+        assert oracle.out_extent(wl.H, wl.kh, wl.stride, wl.pad) == P == wl.P
+    assert oracle.out_extent(2, 5, 1, 1) == 0
+    assert oracle.out_extent(2, 5, 1, 2) == 2
+
+
+def test_rejects_bad_geometry():
+    with pytest.raises(ValueError):
+        oracle.conv2d(np.zeros((1, 2, 2, 1)), np.zeros((1, 5, 5, 1)), 1, 0)
+    with pytest.raises(ValueError):
+        oracle.conv2d(np.zeros((1, 4, 4, 2)), np.zeros((1, 3, 3, 3)), 1, 0)
