@@ -12,7 +12,7 @@ from __future__ import annotations
 
 _BINDING_NAMES = {
     "ConvBnSilu", "bn_fold", "library", "Kernel", "Dtype", "TgError", "status_string",
-    "kernel_name", "library_path", "build_library", "exported_symbols",
+    "kernel_name", "library_path", "build_library", "exported_symbols", "Table", "dispatch_choose",
 }
 
 

@@ -1,0 +1,342 @@
+// api.hip -- plan, validation, dispatch table and the C entry points declared
+// in include/tg_conv_bn_silu.h.
+//
+// Dispatch follows "Fusing an Epilogue" (teenygrad docs), section "Three
+// kernels for one operation": several kernels for one operation, chosen by
+// shape with thresholds that somebody measured and wrote down, and a tile
+// size derived from the layer shape and the machine's compute-unit count.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <new>
+
+#include "tg_conv_bn_silu.h"
+#include "tg_internal.hpp"
+
+using namespace tg;
+
+struct tg_conv_bn_silu_plan {
+    ConvGeom g;
+    tg_dtype dtype;
+    int kernel;      // TG_KERNEL_SCALAR / TILED / IGEMM (resolved)
+    bool unfused;
+    bool forced;     // kernel was requested explicitly (alignment errors instead of fallback)
+    int igemm_cfg;   // index into the igemm variant table
+    TiledCfg tiled;
+    size_t ws_bytes;  // unfused only
+};
+
+namespace {
+
+// MI355X: 256 compute units in 8 XCDs. Tile choice is a function of the shape
+// and of this count only, so plans are reproducible on any host.
+const int kCUs = 256;
+
+// Measured on MI355X (gfx950): sustained fp16 MFMA rate per SIMD, in FLOP per
+// clock, and the rates of the memory paths the cost model uses.
+const double kClock = 2.4e9;
+const double kMfmaFlopPerClkSimd = 871.0;  // 16x16x32 f16, 2.14 PFLOP/s on the whole chip
+const double kLdsBytesPerClkCu = 213.0;     // ds_read_b128, conflict-free
+const double kHbmBytesPerSec = 5.0e12;      // mixed read/write streaming
+const double kL2FillBytesPerClkCu = 64.0;
+
+bool env_flag(const char* name) {
+    const char* v = getenv(name);
+    return v && v[0] && strcmp(v, "0") != 0;
+}
+
+int env_int(const char* name, int dflt) {
+    const char* v = getenv(name);
+    if (!v || !v[0]) return dflt;
+    return atoi(v);
+}
+
+long long out_extent(long long in, long long k, long long stride, long long pad) {
+    if (in + 2 * pad < k) return 0;
+    return (in + 2 * pad - k) / stride + 1;
+}
+
+tg_status make_geom(int N, int H, int W, int C_in, int C_out, int kh, int kw, int stride, int pad,
+                    ConvGeom* g) {
+    if (N < 1 || H < 1 || W < 1 || C_in < 1 || C_out < 1 || kh < 1 || kw < 1 || stride < 1 ||
+        pad < 0)
+        return TG_ERR_INVALID_ARGUMENT;
+    long long P = out_extent(H, kh, stride, pad), Q = out_extent(W, kw, stride, pad);
+    if (P < 1 || Q < 1) return TG_ERR_INVALID_ARGUMENT;
+    const long long lim = (1LL << 31) - 1;
+    long long nx = (long long)N * H * W * C_in;
+    long long nw = (long long)C_out * kh * kw * C_in;
+    long long ny = (long long)N * P * Q * C_out;
+    if (nx > lim || nw > lim || ny > lim) return TG_ERR_UNSUPPORTED;
+    // Padded extents and strided offsets stay far below 2^31 as well.
+    if ((long long)H + 2LL * pad > lim / 4 || (long long)W + 2LL * pad > lim / 4)
+        return TG_ERR_UNSUPPORTED;
+    g->N = N; g->H = H; g->W = W; g->C_in = C_in; g->C_out = C_out;
+    g->kh = kh; g->kw = kw; g->stride = stride; g->pad = pad;
+    g->P = (int)P; g->Q = (int)Q;
+    g->M = (int)(N * P * Q);
+    g->K = kh * kw * C_in;
+    return TG_OK;
+}
+
+bool igemm_serves(const ConvGeom& g, tg_dtype dt) { return dt == TG_F16 && g.C_in % 8 == 0; }
+
+bool tiled_serves(const ConvGeom& g, tg_dtype dt, TiledCfg* c) {
+    TiledCfg tmp;
+    return dt == TG_F16 && tiled_plan(g, c ? c : &tmp);
+}
+
+// Estimated time of an igemm variant: the busiest CU's MFMA work (scaled up
+// when the wave tile reads LDS faster than LDS delivers) against the memory
+// time (compulsory HBM bytes plus the L2 -> LDS operand fill of every tile).
+double igemm_cost(const ConvGeom& g, const IgemmCfg& c) {
+    long long tiles_m = (g.M + c.BM - 1) / c.BM, tiles_n = (g.C_out + c.BN - 1) / c.BN;
+    long long tiles = tiles_m * tiles_n;
+    long long kpad = (g.K + c.BK - 1) / c.BK * c.BK;
+    long long per_cu = (tiles + kCUs - 1) / kCUs;
+    int FM = c.BM / c.WM / 16, FN = c.BN / c.WN / 16;
+    double mfma_clk = 16384.0 / kMfmaFlopPerClkSimd;  // one 16x16x32 instruction
+    double lds_need = 4.0 * (FM + FN) * 1024.0 / (FM * FN * mfma_clk);  // B/clk per CU
+    double lds_factor = lds_need > kLdsBytesPerClkCu ? lds_need / kLdsBytesPerClkCu : 1.0;
+    double t_mfma = per_cu * (double)c.BM * c.BN * kpad * 2.0 /
+                    (4.0 * kMfmaFlopPerClkSimd * kClock) * lds_factor;
+    double hbm = 2.0 * ((double)g.N * g.H * g.W * g.C_in + (double)g.M * g.C_out +
+                        (double)g.C_out * g.K);
+    double fill = (double)tiles * (c.BM + c.BN) * kpad * 2.0;
+    double t_mem = hbm / kHbmBytesPerSec + fill / (kCUs * kL2FillBytesPerClkCu * kClock);
+    return t_mfma > t_mem ? t_mfma : t_mem;
+}
+
+int choose_igemm_cfg(const ConvGeom& g) {
+    int forced = env_int("TG_IGEMM_CFG", -1);
+    if (forced >= 0 && forced < igemm_num_cfgs()) return forced;
+    int best = 0;
+    double best_cost = 1e300;
+    for (int i = 0; i < igemm_num_cfgs(); ++i) {
+        const IgemmCfg& c = igemm_cfg(i);
+        double cost = igemm_cost(g, c);
+        // Ties (within 2%) go to the wider channel tile: fewer re-reads of x.
+        if (cost < best_cost * 0.98 ||
+            (cost < best_cost * 1.02 && c.BN > igemm_cfg(best).BN)) {
+            best = i;
+            best_cost = cost < best_cost ? cost : best_cost;
+        }
+    }
+    return best;
+}
+
+tg_kernel dispatch(const ConvGeom& g, tg_dtype dt, tg_dispatch table) {
+    if (table == TG_DISPATCH_PAGES) {
+        // The page's table: GEMM for 1x1 convolutions with at least 32 output
+        // channels, tiled above 16 output channels, scalar otherwise. A kernel
+        // that cannot serve the shape passes it to the next rule.
+        if (g.kh == 1 && g.kw == 1 && g.C_out >= 32 && igemm_serves(g, dt)) return TG_KERNEL_IGEMM;
+        if (g.C_out > 16 && tiled_serves(g, dt, nullptr)) return TG_KERNEL_TILED;
+        return TG_KERNEL_SCALAR;
+    }
+    // MI355X table (thresholds measured with the dispatch sweep; see the
+    // provenance notes in the repository's design document).
+    if (dt == TG_F32) return TG_KERNEL_SCALAR;
+    if (igemm_serves(g, dt) && g.C_out >= 16 && g.K >= 32) return TG_KERNEL_IGEMM;
+    if (tiled_serves(g, dt, nullptr)) return TG_KERNEL_TILED;
+    return TG_KERNEL_SCALAR;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in, int C_out, int kh,
+                      int kw, int stride, int pad, tg_dtype dtype, tg_kernel kernel,
+                      tg_dispatch table) {
+    if (!out) return TG_ERR_INVALID_ARGUMENT;
+    *out = nullptr;
+    ConvGeom g;
+    tg_status st = make_geom(N, H, W, C_in, C_out, kh, kw, stride, pad, &g);
+    if (st != TG_OK) return st;
+    if (dtype != TG_F16 && dtype != TG_F32) return TG_ERR_UNSUPPORTED;
+    if (table != TG_DISPATCH_MI355X && table != TG_DISPATCH_PAGES) return TG_ERR_UNSUPPORTED;
+    int kv = (int)kernel;
+    bool unfused = (kv & TG_UNFUSED) != 0;
+    int base = kv & ~TG_UNFUSED;
+    if (base < TG_KERNEL_AUTO || base > TG_KERNEL_IGEMM) return TG_ERR_UNSUPPORTED;
+
+    tg_conv_bn_silu_plan p;
+    memset(&p, 0, sizeof(p));
+    p.g = g;
+    p.dtype = dtype;
+    p.unfused = unfused;
+    p.forced = base != TG_KERNEL_AUTO;
+    p.kernel = p.forced ? base : (int)dispatch(g, dtype, table);
+    if (p.kernel == TG_KERNEL_IGEMM) {
+        if (!igemm_serves(g, dtype)) return TG_ERR_UNSUPPORTED;
+        p.igemm_cfg = choose_igemm_cfg(g);
+    } else if (p.kernel == TG_KERNEL_TILED) {
+        if (!tiled_serves(g, dtype, &p.tiled)) return TG_ERR_UNSUPPORTED;
+    }
+    size_t ysz = (size_t)g.M * g.C_out * (dtype == TG_F16 ? 2 : 4);
+    p.ws_bytes = unfused ? 2 * round256(ysz) : 0;
+
+    tg_conv_bn_silu_plan* h = new (std::nothrow) tg_conv_bn_silu_plan(p);
+    if (!h) return TG_ERR_UNSUPPORTED;
+    if (env_flag("TG_LOG")) {
+        char buf[256];
+        tg_conv_bn_silu_describe(h, buf, sizeof(buf));
+        fprintf(stderr, "[tgconv] %s\n", buf);
+    }
+    *out = h;
+    return TG_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+tg_status tg_conv_bn_silu_create(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
+                                 int C_out, int kh, int kw, int stride, int pad, tg_dtype dtype,
+                                 tg_kernel kernel) {
+    return create_impl(out, N, H, W, C_in, C_out, kh, kw, stride, pad, dtype, kernel,
+                       TG_DISPATCH_MI355X);
+}
+
+tg_status tg_conv_bn_silu_create_with_table(tg_conv_bn_silu_plan** out, int N, int H, int W,
+                                            int C_in, int C_out, int kh, int kw, int stride,
+                                            int pad, tg_dtype dtype, tg_kernel kernel,
+                                            tg_dispatch table) {
+    return create_impl(out, N, H, W, C_in, C_out, kh, kw, stride, pad, dtype, kernel, table);
+}
+
+tg_status tg_conv_bn_silu_destroy(tg_conv_bn_silu_plan* plan) {
+    delete plan;
+    return TG_OK;
+}
+
+tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, const void* w,
+                              const float* bn_scale, const float* bn_bias, void* y,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    if (!plan || !x || !w || !bn_scale || !bn_bias || !y) return TG_ERR_INVALID_ARGUMENT;
+    const ConvGeom& g = plan->g;
+    hipStream_t s = (hipStream_t)stream;
+    bool f32 = plan->dtype == TG_F32;
+    int kernel = plan->kernel;
+    if (kernel != TG_KERNEL_SCALAR && !(aligned16(x) && aligned16(w) && aligned16(y))) {
+        if (plan->forced) return TG_ERR_ALIGNMENT;
+        kernel = TG_KERNEL_SCALAR;
+    }
+    void* conv_out = y;
+    void* t2 = nullptr;
+    if (plan->unfused) {
+        if (!workspace || workspace_bytes < plan->ws_bytes) return TG_ERR_WORKSPACE;
+        size_t ysz = (size_t)g.M * g.C_out * (f32 ? 4 : 2);
+        conv_out = workspace;
+        t2 = (char*)workspace + round256(ysz);
+        if (kernel != TG_KERNEL_SCALAR && !aligned16(workspace)) {
+            if (plan->forced) return TG_ERR_ALIGNMENT;
+            kernel = TG_KERNEL_SCALAR;
+        }
+    }
+    bool identity = plan->unfused;
+    hipError_t e;
+    switch (kernel) {
+        case TG_KERNEL_IGEMM:
+            e = launch_igemm(g, plan->igemm_cfg, identity, x, w, bn_scale, bn_bias, conv_out, s);
+            break;
+        case TG_KERNEL_TILED:
+            e = launch_tiled(g, plan->tiled, identity, x, w, bn_scale, bn_bias, conv_out, s);
+            break;
+        default:
+            e = launch_scalar(g, f32, identity, x, w, bn_scale, bn_bias, conv_out, s);
+            break;
+    }
+    if (e != hipSuccess) return TG_ERR_HIP;
+    if (plan->unfused) {
+        long long total = (long long)g.M * g.C_out;
+        e = launch_bn_apply(f32, conv_out, bn_scale, bn_bias, t2, total, g.C_out, s);
+        if (e != hipSuccess) return TG_ERR_HIP;
+        e = launch_silu_apply(f32, t2, y, total, s);
+        if (e != hipSuccess) return TG_ERR_HIP;
+    }
+    return TG_OK;
+}
+
+tg_status tg_bn_fold(const float* gamma, const float* beta, const float* mean, const float* var,
+                     float eps, int C_out, float* bn_scale, float* bn_bias, void* stream) {
+    if (!gamma || !beta || !mean || !var || !bn_scale || !bn_bias || C_out < 1 || !(eps >= 0.0f))
+        return TG_ERR_INVALID_ARGUMENT;
+    hipError_t e = launch_bn_fold(gamma, beta, mean, var, eps, C_out, bn_scale, bn_bias,
+                                  (hipStream_t)stream);
+    return e == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
+tg_status tg_conv_bn_silu_query(const tg_conv_bn_silu_plan* plan, int* P, int* Q,
+                                tg_kernel* chosen, size_t* workspace_bytes) {
+    if (!plan) return TG_ERR_INVALID_ARGUMENT;
+    if (P) *P = plan->g.P;
+    if (Q) *Q = plan->g.Q;
+    if (chosen) *chosen = (tg_kernel)(plan->kernel | (plan->unfused ? TG_UNFUSED : 0));
+    if (workspace_bytes) *workspace_bytes = plan->ws_bytes;
+    return TG_OK;
+}
+
+tg_status tg_conv_bn_silu_describe(const tg_conv_bn_silu_plan* plan, char* buf, size_t len) {
+    if (!plan || !buf) return TG_ERR_INVALID_ARGUMENT;
+    if (len == 0) return TG_OK;
+    const ConvGeom& g = plan->g;
+    char k[160];
+    if (plan->kernel == TG_KERNEL_IGEMM) {
+        const IgemmCfg& c = igemm_cfg(plan->igemm_cfg);
+        int tm = (g.M + c.BM - 1) / c.BM, tn = (g.C_out + c.BN - 1) / c.BN;
+        snprintf(k, sizeof(k), "igemm cfg=%d BM=%d BN=%d BK=%d waves=%dx%d grid=%d", plan->igemm_cfg,
+                 c.BM, c.BN, c.BK, c.WM, c.WN, tm * tn);
+    } else if (plan->kernel == TG_KERNEL_TILED) {
+        int bands = (g.P + plan->tiled.R - 1) / plan->tiled.R;
+        snprintf(k, sizeof(k), "tiled R=%d lds=%d grid=%d", plan->tiled.R, plan->tiled.lds_bytes,
+                 g.N * bands);
+    } else {
+        snprintf(k, sizeof(k), "scalar grid=%d", (g.M * g.C_out + 255) / 256);
+    }
+    snprintf(buf, len, "%s%s %s N=%d H=%d W=%d C_in=%d C_out=%d k=%dx%d s=%d p=%d -> %dx%d",
+             plan->unfused ? "unfused:" : "", k, plan->dtype == TG_F16 ? "f16" : "f32", g.N, g.H,
+             g.W, g.C_in, g.C_out, g.kh, g.kw, g.stride, g.pad, g.P, g.Q);
+    return TG_OK;
+}
+
+tg_status tg_dispatch_choose(int N, int H, int W, int C_in, int C_out, int kh, int kw, int stride,
+                             int pad, tg_dtype dtype, tg_dispatch table, tg_kernel* chosen) {
+    if (!chosen) return TG_ERR_INVALID_ARGUMENT;
+    ConvGeom g;
+    tg_status st = make_geom(N, H, W, C_in, C_out, kh, kw, stride, pad, &g);
+    if (st != TG_OK) return st;
+    if (dtype != TG_F16 && dtype != TG_F32) return TG_ERR_UNSUPPORTED;
+    if (table != TG_DISPATCH_MI355X && table != TG_DISPATCH_PAGES) return TG_ERR_UNSUPPORTED;
+    *chosen = dispatch(g, dtype, table);
+    return TG_OK;
+}
+
+const char* tg_status_string(tg_status s) {
+    switch (s) {
+        case TG_OK: return "ok";
+        case TG_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case TG_ERR_UNSUPPORTED: return "unsupported";
+        case TG_ERR_ALIGNMENT: return "pointer not 16-byte aligned";
+        case TG_ERR_WORKSPACE: return "workspace missing or too small";
+        case TG_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+const char* tg_kernel_name(tg_kernel k) {
+    int kv = (int)k;
+    bool unf = (kv & TG_UNFUSED) != 0;
+    switch (kv & ~TG_UNFUSED) {
+        case TG_KERNEL_AUTO: return unf ? "unfused(auto)" : "auto";
+        case TG_KERNEL_SCALAR: return unf ? "unfused(scalar)" : "conv2d_bn_silu_scalar";
+        case TG_KERNEL_TILED: return unf ? "unfused(tiled)" : "conv2d_bn_silu_tiled";
+        case TG_KERNEL_IGEMM: return unf ? "unfused(igemm)" : "conv2d_bn_silu_igemm";
+    }
+    return "unknown kernel";
+}
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// scalar.hip -- conv2d_bn_silu_scalar: one output element per lane.
+//
+// "Fusing an Epilogue" (teenygrad docs), section "Three kernels for one
+// operation": the scalar kernel has no setup cost and serves small shapes;
+// here it is also the kernel that serves every shape and both dtypes.
+//
+// Lane -> (n, p, q, k) with k fastest, so the C_out lanes that share an
+// output pixel read the same x values (one fetch serves them all) and the y
+// stores of a wavefront are contiguous in NHWC.
+#include "tg_device.hpp"
+#include "tg_internal.hpp"
+
+namespace tg {
+
+template <typename T, int EPI>
+__global__ __launch_bounds__(256) void conv2d_bn_silu_scalar(
+    const T* __restrict__ x, const T* __restrict__ w, const float* __restrict__ scale,
+    const float* __restrict__ bias, T* __restrict__ y, ConvGeom g, int total) {
+    int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= total) return;
+    int k = idx % g.C_out;
+    int pix = idx / g.C_out;
+    int q = pix % g.Q;
+    int t = pix / g.Q;
+    int p = t % g.P;
+    int n = t / g.P;
+    int h0 = p * g.stride - g.pad, w0 = q * g.stride - g.pad;
+    float acc = 0.0f;
+    for (int r = 0; r < g.kh; ++r) {
+        int ih = h0 + r;
+        if ((unsigned)ih >= (unsigned)g.H) continue;
+        for (int s = 0; s < g.kw; ++s) {
+            int iw = w0 + s;
+            if ((unsigned)iw >= (unsigned)g.W) continue;
+            const T* xp = x + ((n * g.H + ih) * g.W + iw) * g.C_in;
+            const T* wp = w + ((k * g.kh + r) * g.kw + s) * g.C_in;
+            for (int c = 0; c < g.C_in; ++c) acc = __builtin_fmaf(to_f32(xp[c]), to_f32(wp[c]), acc);
+        }
+    }
+    float sc = 0.0f, bi = 0.0f;
+    if (EPI == EPI_FUSED) {
+        sc = scale[k];
+        bi = bias[k];
+    }
+    y[idx] = from_f32<T>(epilogue<EPI>(acc, sc, bi));
+}
+
+hipError_t launch_scalar(const ConvGeom& g, bool f32, bool identity, const void* x, const void* w,
+                         const float* scale, const float* bias, void* y, hipStream_t s) {
+    int total = g.M * g.C_out;  // < 2^31, checked at plan time
+    dim3 grid((total + 255) / 256), block(256);
+    if (f32) {
+        if (identity)
+            hipLaunchKernelGGL((conv2d_bn_silu_scalar<float, EPI_IDENTITY>), grid, block, 0, s,
+                               (const float*)x, (const float*)w, scale, bias, (float*)y, g, total);
+        else
+            hipLaunchKernelGGL((conv2d_bn_silu_scalar<float, EPI_FUSED>), grid, block, 0, s,
+                               (const float*)x, (const float*)w, scale, bias, (float*)y, g, total);
+    } else {
+        if (identity)
+            hipLaunchKernelGGL((conv2d_bn_silu_scalar<f16, EPI_IDENTITY>), grid, block, 0, s,
+                               (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, total);
+        else
+            hipLaunchKernelGGL((conv2d_bn_silu_scalar<f16, EPI_FUSED>), grid, block, 0, s,
+                               (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, total);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace tg

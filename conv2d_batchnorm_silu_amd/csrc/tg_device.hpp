@@ -1,0 +1,59 @@
+// tg_device.hpp -- device-side helpers shared by the gfx950 kernels.
+//
+// The epilogue every fused kernel applies to its fp32 accumulator while it is
+// still in registers ("Fusing an Epilogue", teenygrad docs, section "The shape
+// of it"): v = acc * scale[k] + bias[k] (inference BatchNorm folded per output
+// channel), then y = v * sigmoid(v) (SiLU), then one cast and one store.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tg {
+
+typedef _Float16 f16;
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Epilogue selector: FUSED applies BatchNorm + SiLU; IDENTITY stores the raw
+// convolution (the first kernel of the unfused three-kernel baseline).
+enum Epilogue { EPI_FUSED = 0, EPI_IDENTITY = 1 };
+
+// sigmoid(v) = 1 / (1 + e^-v), with e^-v = 2^(-v * log2 e) on the hardware
+// exp2 (v_exp_f32) and the hardware reciprocal (v_rcp_f32). For v below about
+// -88 the exponential is +inf and the reciprocal 0, so silu(v) is -0 (no NaN);
+// for large v the exponential underflows to 0 and silu(v) = v.
+__device__ __forceinline__ float silu_f32(float v) {
+    const float kNegLog2e = -1.4426950408889634f;
+    float e = __builtin_amdgcn_exp2f(v * kNegLog2e);
+    return v * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+template <int EPI>
+__device__ __forceinline__ float epilogue(float acc, float scale, float bias) {
+    if (EPI == EPI_FUSED) return silu_f32(__builtin_fmaf(acc, scale, bias));
+    return acc;
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v) { return (float)v; }
+template <typename T> __device__ __forceinline__ T from_f32(float v) { return (T)v; }  // RNE
+
+__device__ __forceinline__ int imin(int a, int b) { return a < b ? a : b; }
+
+// Workgroups are handed to the 8 XCDs round-robin (workgroup b runs on XCD
+// b % 8). Remap so that each XCD receives one contiguous range of logical
+// tiles: neighbouring tiles (which share halo rows of x, or the same x rows
+// for different channel tiles) then meet in the same L2. Bijective on
+// [0, total) for any total.
+__device__ __forceinline__ int xcd_contiguous_tile(int b, int total) {
+    const int kXcds = 8;
+    int xcd = b % kXcds, local = b / kXcds;
+    int per = total / kXcds, rem = total % kXcds;
+    return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+}
+
+}  // namespace tg

@@ -1,0 +1,51 @@
+// tg_internal.hpp -- host-side types shared by the plan/ABI code and the
+// kernel launchers. Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace tg {
+
+// Convolution geometry. Every element count of x, w and y is below 2^31
+// (checked at plan creation), so int offsets suffice inside the kernels.
+struct ConvGeom {
+    int N, H, W, C_in, C_out, kh, kw, stride, pad;
+    int P, Q;  // output extent
+    int M;     // N * P * Q output pixels
+    int K;     // kh * kw * C_in reduction length
+};
+
+// Implicit-GEMM tile variants compiled into the library (see igemm.hip).
+// BM pixels x BN channels per workgroup of 256 threads (4 wavefronts arranged
+// WM x WN); the reduction is staged through LDS BK halves at a time.
+struct IgemmCfg {
+    int BM, BN, BK, WM, WN;
+};
+int igemm_num_cfgs();
+const IgemmCfg& igemm_cfg(int i);
+
+// Tiled direct kernel parameters chosen at plan time.
+struct TiledCfg {
+    int R;          // output rows per workgroup
+    int WPad;       // staged input columns per row, (Q-1)*stride + kw
+    int lds_bytes;  // dynamic LDS per workgroup
+};
+// Largest band that fits; returns false when the shape cannot be served.
+bool tiled_plan(const ConvGeom& g, TiledCfg* out);
+
+hipError_t launch_scalar(const ConvGeom& g, bool f32, bool identity, const void* x, const void* w,
+                         const float* scale, const float* bias, void* y, hipStream_t s);
+hipError_t launch_tiled(const ConvGeom& g, const TiledCfg& c, bool identity, const void* x,
+                        const void* w, const float* scale, const float* bias, void* y,
+                        hipStream_t s);
+hipError_t launch_igemm(const ConvGeom& g, int cfg, bool identity, const void* x, const void* w,
+                        const float* scale, const float* bias, void* y, hipStream_t s);
+hipError_t launch_bn_apply(bool f32, const void* t1, const float* scale, const float* bias, void* t2,
+                           long long total, int C, hipStream_t s);
+hipError_t launch_silu_apply(bool f32, const void* t2, void* y, long long total, hipStream_t s);
+hipError_t launch_bn_fold(const float* gamma, const float* beta, const float* mean,
+                          const float* var, float eps, int C, float* scale, float* bias,
+                          hipStream_t s);
+
+}  // namespace tg

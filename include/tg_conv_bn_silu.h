@@ -1,0 +1,151 @@
+/*
+ * tg_conv_bn_silu.h -- C ABI of the fused conv2d + BatchNorm + SiLU library
+ * for AMD Instinct MI355X (gfx950). Library: libtgconv.so.
+ *
+ * The operation ("Fusing an Epilogue", teenygrad docs, sections "The problem"
+ * and "The shape of it"): a 2-D convolution whose output, while still in
+ * registers, is scaled and shifted per output channel (inference BatchNorm
+ * folded to one scale and one bias per channel) and passed through
+ * SiLU(v) = v * sigmoid(v), then stored once:
+ *
+ *   acc[n,p,q,k] = sum_{r<kh, s<kw, c<C_in} x[n, p*stride-pad+r, q*stride-pad+s, c] * w[k,r,s,c]
+ *                  (x is zero outside [0,H) x [0,W); cross-correlation, no flip)
+ *   v            = acc * bn_scale[k] + bn_bias[k]
+ *   y[n,p,q,k]   = v * sigmoid(v)
+ *
+ * with P = floor((H + 2*pad - kh)/stride) + 1, Q = floor((W + 2*pad - kw)/stride) + 1.
+ *
+ * Layouts (all dense, no strides): x NHWC [N][H][W][C_in]; w OHWI
+ * [C_out][kh][kw][C_in] (channels-last filters, stored that way once at load
+ * time -- "When the fusion you want is impossible, fuse into the producer",
+ * layout-conversion paragraph); y NHWC [N][P][Q][C_out]; bn_scale, bn_bias
+ * fp32 [C_out]. x, w and y share one dtype (fp16 or fp32); accumulation and
+ * the epilogue are fp32; fp16 results are rounded to nearest even.
+ *
+ * Ownership: the caller owns every device buffer. A plan owns host memory
+ * only; create/destroy never touch device memory. Entry points never abort
+ * and never print (set TG_LOG=1 in the environment to log dispatch choices
+ * to stderr). run() and bn_fold() are asynchronous on the given stream (a
+ * hipStream_t passed as void*, NULL = the null stream) and do not
+ * synchronise; launch failures are reported as TG_ERR_HIP.
+ *
+ * Thread safety: a plan is immutable after create; concurrent run() calls
+ * with one plan on different streams are allowed. y must not alias x, w,
+ * bn_scale, bn_bias or the workspace (not checked).
+ */
+#ifndef TG_CONV_BN_SILU_H
+#define TG_CONV_BN_SILU_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct tg_conv_bn_silu_plan tg_conv_bn_silu_plan; /* opaque, host memory */
+
+typedef enum {
+    TG_OK = 0,
+    TG_ERR_INVALID_ARGUMENT = 1, /* NULL pointer, non-positive size, window larger than padded input */
+    TG_ERR_UNSUPPORTED = 2,      /* valid, but not served by the requested kernel or too large */
+    TG_ERR_ALIGNMENT = 3,        /* a forced vector kernel got a pointer that is not 16-byte aligned */
+    TG_ERR_WORKSPACE = 4,        /* unfused baseline: workspace missing or too small */
+    TG_ERR_HIP = 5               /* a HIP runtime call or kernel launch failed */
+} tg_status;
+
+typedef enum { TG_F16 = 0, TG_F32 = 1 } tg_dtype;
+
+/* Kernel selection ("Fusing an Epilogue", section "Three kernels for one
+ * operation": one scalar, one spatially tiled, one GEMM-shaped kernel, picked
+ * by shape). A value may be OR-ed with TG_UNFUSED to run the three-kernel
+ * baseline instead: that conv kernel with an identity epilogue writing t1,
+ * then a BatchNorm kernel t1 -> t2, then a SiLU kernel t2 -> y ("The problem"
+ * section of the same page). */
+typedef enum {
+    TG_KERNEL_AUTO = 0,   /* the dispatch table decides (see tg_dispatch_choose) */
+    TG_KERNEL_SCALAR = 1, /* one output element per lane; any shape, fp16 and fp32 */
+    TG_KERNEL_TILED = 2,  /* direct conv on an output-row band staged in LDS; fp16,
+                             C_out <= 64, padded input row band must fit in LDS */
+    TG_KERNEL_IGEMM = 3,  /* implicit GEMM on fp16 MFMA with the epilogue in registers;
+                             fp16, C_in % 8 == 0 */
+    TG_UNFUSED = 0x100    /* flag: run conv, bn and silu as three kernels */
+} tg_kernel;
+
+/* Dispatch tables. TG_DISPATCH_MI355X (default) holds thresholds measured on
+ * MI355X. TG_DISPATCH_PAGES reproduces the thresholds the teenygrad page
+ * writes down ("Three kernels for one operation"): GEMM for 1x1 convolutions
+ * with at least 32 output channels, else tiled for more than 16 output
+ * channels, else scalar (reading the thresholds as counts of output channels). */
+typedef enum { TG_DISPATCH_MI355X = 0, TG_DISPATCH_PAGES = 1 } tg_dispatch;
+
+/* Build a plan for one shape. Host only: validates, computes P and Q, picks
+ * the kernel (TG_KERNEL_AUTO: the default dispatch table) and its tile and
+ * grid. Returns TG_ERR_INVALID_ARGUMENT for out == NULL, any size < 1,
+ * pad < 0 or a window larger than the padded input; TG_ERR_UNSUPPORTED when
+ * any of x, w, y has 2^31 or more elements, when a forced kernel does not
+ * serve the shape or dtype, or for an unknown dtype/kernel value. On error
+ * *out is set to NULL. For tuning sweeps only, the environment variable
+ * TG_IGEMM_CFG=<i> forces the i-th compiled implicit-GEMM tile variant. */
+tg_status tg_conv_bn_silu_create(tg_conv_bn_silu_plan **out, int N, int H, int W, int C_in,
+                                 int C_out, int kh, int kw, int stride, int pad, tg_dtype dtype,
+                                 tg_kernel kernel);
+
+/* Same as create, choosing the AUTO kernel from the given dispatch table. */
+tg_status tg_conv_bn_silu_create_with_table(tg_conv_bn_silu_plan **out, int N, int H, int W,
+                                            int C_in, int C_out, int kh, int kw, int stride,
+                                            int pad, tg_dtype dtype, tg_kernel kernel,
+                                            tg_dispatch table);
+
+/* Run the planned operation on `stream`. x, w, y: device pointers in the
+ * plan's dtype and the layouts above; bn_scale, bn_bias: device fp32
+ * [C_out] (from tg_bn_fold). workspace/workspace_bytes: device scratch for the
+ * unfused baseline only (two intermediates t1 and t2 of y's size; see
+ * tg_conv_bn_silu_query), ignored and may be NULL/0 for fused kernels.
+ * Errors: TG_ERR_INVALID_ARGUMENT for a NULL plan or data pointer;
+ * TG_ERR_ALIGNMENT when a forced tiled/igemm plan gets x, w or y not 16-byte
+ * aligned (an AUTO plan falls back to the scalar kernel instead);
+ * TG_ERR_WORKSPACE when the unfused workspace is NULL or too small;
+ * TG_ERR_HIP when a launch fails. Nothing is launched on error. */
+tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan *plan, const void *x, const void *w,
+                              const float *bn_scale, const float *bn_bias, void *y,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/* Free a plan. NULL is a no-op. */
+tg_status tg_conv_bn_silu_destroy(tg_conv_bn_silu_plan *plan);
+
+/* Fold inference BatchNorm into one scale and one bias per output channel,
+ * once per weight load ("When the fusion you want is impossible, fuse into
+ * the producer", section "The general form": do once at load time what would
+ * otherwise repeat per use): scale = gamma / sqrt(var + eps),
+ * bias = beta - mean * scale, in fp32 on the device. All pointers are device
+ * fp32 [C_out]; bn_scale/bn_bias must not alias the inputs. Errors:
+ * TG_ERR_INVALID_ARGUMENT for NULL pointers, C_out < 1 or eps < 0;
+ * TG_ERR_HIP on launch failure. Asynchronous on `stream`. */
+tg_status tg_bn_fold(const float *gamma, const float *beta, const float *mean, const float *var,
+                     float eps, int C_out, float *bn_scale, float *bn_bias, void *stream);
+
+/* Describe a plan: output extent, the kernel run() will launch (for aligned
+ * pointers; may include TG_UNFUSED) and the workspace it needs. Any out
+ * pointer may be NULL. TG_ERR_INVALID_ARGUMENT for a NULL plan. */
+tg_status tg_conv_bn_silu_query(const tg_conv_bn_silu_plan *plan, int *P, int *Q,
+                                tg_kernel *chosen, size_t *workspace_bytes);
+
+/* Human-readable summary of the plan's kernel, tile and grid, written into
+ * buf (always NUL-terminated when len > 0). */
+tg_status tg_conv_bn_silu_describe(const tg_conv_bn_silu_plan *plan, char *buf, size_t len);
+
+/* The dispatch table alone, as a host-only function: which fused kernel the
+ * given table picks for this shape and dtype (never TG_KERNEL_AUTO). Same
+ * validation as create. */
+tg_status tg_dispatch_choose(int N, int H, int W, int C_in, int C_out, int kh, int kw, int stride,
+                             int pad, tg_dtype dtype, tg_dispatch table, tg_kernel *chosen);
+
+/* Static strings; never NULL. */
+const char *tg_status_string(tg_status s);
+const char *tg_kernel_name(tg_kernel k);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TG_CONV_BN_SILU_H */

@@ -1,0 +1,160 @@
+"""The C ABI on the host: the library loads, exports every function the
+header declares, validates its arguments and makes its dispatch decisions --
+all without touching a GPU (no call here reaches a kernel launch)."""
+import ctypes
+
+import pytest
+
+from conv2d_batchnorm_silu_amd import binding as B
+from conv2d_batchnorm_silu_amd.inputs import WORKLOADS
+
+OK, INVAL, UNSUP, ALIGN, WS, HIPERR = range(6)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return B.library()
+
+
+def _create(lib, *shape, dtype=0, kernel=0, table=0):
+    h = ctypes.c_void_p()
+    st = lib.tg_conv_bn_silu_create_with_table(ctypes.byref(h), *shape, dtype, kernel, table)
+    return st, h
+
+
+def test_exports_every_declared_symbol(lib):
+    names = B.exported_symbols()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert "tg_conv_bn_silu_create" in names and "tg_bn_fold" in names
+
+
+@pytest.mark.parametrize("bad", [
+    (0, 8, 8, 3, 4, 3, 3, 1, 1), (1, 0, 8, 3, 4, 3, 3, 1, 1), (1, 8, 8, 0, 4, 3, 3, 1, 1),
+    (1, 8, 8, 3, 0, 3, 3, 1, 1), (1, 8, 8, 3, 4, 0, 3, 1, 1), (1, 8, 8, 3, 4, 3, 3, 0, 1),
+    (1, 8, 8, 3, 4, 3, 3, 1, -1), (1, 2, 8, 3, 4, 5, 3, 1, 1), (1, 8, 1, 3, 4, 3, 3, 1, 0)])
+def test_create_rejects_invalid(lib, bad):
+    st, h = _create(lib, *bad)
+    assert st == INVAL and not h.value
+
+
+def test_create_null_out(lib):
+    assert lib.tg_conv_bn_silu_create(None, 1, 8, 8, 3, 4, 3, 3, 1, 1, 0, 0) == INVAL
+
+
+def test_create_unsupported(lib):
+    # 2^31 output elements
+    assert _create(lib, 2048, 1024, 1024, 1, 1, 1, 1, 1, 0)[0] == UNSUP
+    # unknown dtype, kernel, table
+    assert _create(lib, 1, 8, 8, 8, 8, 3, 3, 1, 1, dtype=7)[0] == UNSUP
+    assert _create(lib, 1, 8, 8, 8, 8, 3, 3, 1, 1, kernel=9)[0] == UNSUP
+    assert _create(lib, 1, 8, 8, 8, 8, 3, 3, 1, 1, table=5)[0] == UNSUP
+    # igemm needs fp16 and C_in % 8 == 0
+    assert _create(lib, 1, 8, 8, 3, 8, 3, 3, 1, 1, kernel=3)[0] == UNSUP
+    assert _create(lib, 1, 8, 8, 8, 8, 3, 3, 1, 1, dtype=1, kernel=3)[0] == UNSUP
+    # tiled is fp16 only and needs C_out <= 64
+    assert _create(lib, 1, 8, 8, 8, 8, 3, 3, 1, 1, dtype=1, kernel=2)[0] == UNSUP
+    assert _create(lib, 1, 8, 8, 8, 65, 3, 3, 1, 1, kernel=2)[0] == UNSUP
+
+
+def test_query_and_describe(lib):
+    for wl in WORKLOADS.values():
+        st, h = _create(lib, wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride, wl.pad,
+                        dtype=0 if wl.dtype == "f16" else 1)
+        assert st == OK
+        P, Q, k, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()
+        assert lib.tg_conv_bn_silu_query(h, ctypes.byref(P), ctypes.byref(Q), ctypes.byref(k),
+                                         ctypes.byref(ws)) == OK
+        assert (P.value, Q.value) == (wl.P, wl.Q) and ws.value == 0
+        assert k.value in (1, 2, 3)
+        buf = ctypes.create_string_buffer(256)
+        assert lib.tg_conv_bn_silu_describe(h, buf, 256) == OK
+        assert ("%dx%d" % (wl.P, wl.Q)).encode() in buf.value
+        assert lib.tg_conv_bn_silu_destroy(h) == OK
+    assert lib.tg_conv_bn_silu_query(None, None, None, None, None) == INVAL
+    assert lib.tg_conv_bn_silu_destroy(None) == OK
+
+
+def test_unfused_workspace_size(lib):
+    wl = WORKLOADS["conv1x1_c64_k256"]
+    st, h = _create(lib, wl.N, wl.H, wl.W, wl.C_in, wl.C_out, 1, 1, 1, 0, kernel=0x100)
+    assert st == OK
+    k, ws = ctypes.c_int(), ctypes.c_size_t()
+    lib.tg_conv_bn_silu_query(h, None, None, ctypes.byref(k), ctypes.byref(ws))
+    ybytes = wl.N * wl.P * wl.Q * wl.C_out * 2
+    assert ws.value == 2 * ((ybytes + 255) // 256 * 256)
+    assert k.value == (3 | 0x100)
+    lib.tg_conv_bn_silu_destroy(h)
+
+
+def test_pages_dispatch_table():
+    """The page's thresholds: GEMM for 1x1 with >= 32 output channels, tiled
+    above 16 output channels, scalar otherwise (tiled only where it can serve
+    the shape)."""
+    want = {"tiny_f32_3x3": B.Kernel.SCALAR, "conv1x1_c64_k256": B.Kernel.IGEMM,
+            "stem3x3s2_k16": B.Kernel.SCALAR, "stem3x3s2_k24": B.Kernel.TILED,
+            # tiled holds the filter bank in LDS: 3x3x128 and 7x7x64 banks do not fit
+            "conv3x3_c128_k128": B.Kernel.SCALAR, "conv7x7_c64_k64": B.Kernel.SCALAR}
+    for name, k in want.items():
+        wl = WORKLOADS[name]
+        dt = B.Dtype.F16 if wl.dtype == "f16" else B.Dtype.F32
+        got = B.dispatch_choose(wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride,
+                                wl.pad, dt, B.Table.PAGES)
+        assert got == k, name
+    # boundary cases of the thresholds
+    ch = lambda co, k=1, ci=16: B.dispatch_choose(2, 16, 16, ci, co, k, k, 1, k // 2,
+                                                  B.Dtype.F16, B.Table.PAGES)
+    assert ch(32) == B.Kernel.IGEMM and ch(31) == B.Kernel.TILED
+    assert ch(17) == B.Kernel.TILED and ch(16) == B.Kernel.SCALAR
+    assert ch(32, k=3) == B.Kernel.TILED
+
+
+def test_mi355x_dispatch_table():
+    for name, wl in WORKLOADS.items():
+        dt = B.Dtype.F16 if wl.dtype == "f16" else B.Dtype.F32
+        got = B.dispatch_choose(wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride,
+                                wl.pad, dt, B.Table.MI355X)
+        if wl.dtype == "f32":
+            assert got == B.Kernel.SCALAR
+        elif wl.C_in % 8 == 0:
+            assert got == B.Kernel.IGEMM, name
+        else:
+            assert got in (B.Kernel.TILED, B.Kernel.IGEMM, B.Kernel.SCALAR), name
+
+
+def test_run_argument_errors_before_any_launch(lib):
+    st, h = _create(lib, 2, 16, 16, 16, 32, 3, 3, 1, 1, kernel=3)
+    assert st == OK
+    a = 1 << 20  # aligned fake addresses: never dereferenced on these paths
+    run = lib.tg_conv_bn_silu_run
+    assert run(None, a, a, a, a, a, None, 0, None) == INVAL
+    assert run(h, None, a, a, a, a, None, 0, None) == INVAL
+    assert run(h, a, a, a, a, None, None, 0, None) == INVAL
+    assert run(h, a + 2, a, a, a, a, None, 0, None) == ALIGN
+    assert run(h, a, a + 4, a, a, a, None, 0, None) == ALIGN
+    assert run(h, a, a, a, a, a + 8, None, 0, None) == ALIGN
+    lib.tg_conv_bn_silu_destroy(h)
+    st, h = _create(lib, 2, 16, 16, 16, 32, 3, 3, 1, 1, kernel=0x100)
+    assert st == OK
+    assert run(h, a, a, a, a, a, None, 0, None) == WS
+    assert run(h, a, a, a, a, a, a, 10, None) == WS
+    lib.tg_conv_bn_silu_destroy(h)
+
+
+def test_bn_fold_argument_errors(lib):
+    a = 1 << 20
+    f = lib.tg_bn_fold
+    assert f(None, a, a, a, 1e-5, 4, a, a, None) == INVAL
+    assert f(a, a, a, a, 1e-5, 0, a, a, None) == INVAL
+    assert f(a, a, a, a, -1.0, 4, a, a, None) == INVAL
+    assert f(a, a, a, a, float("nan"), 4, a, a, None) == INVAL
+
+
+def test_strings(lib):
+    for s in range(6):
+        assert B.status_string(s)
+    assert B.status_string(99) == "unknown status"
+    assert B.kernel_name(3) == "conv2d_bn_silu_igemm"
+    assert B.kernel_name(3 | 0x100) == "unfused(igemm)"
+    assert B.kernel_name(77) == "unknown kernel"
