@@ -23,7 +23,10 @@ struct tg_conv_bn_silu_plan {
     int kernel;      // TG_KERNEL_SCALAR / TILED / IGEMM (resolved)
     bool unfused;
     bool forced;     // kernel was requested explicitly (alignment errors instead of fallback)
-    int igemm_cfg;   // index into the igemm variant table
+    int igemm_cfg;   // index into the igemm variant table (-1: register-weights variant)
+    int rw_grid;     // persistent grid of the register-weights variant
+    int rw_nf, rw_cs, rw_ncw;  // its weight fragments per wave, waves per block, waves per WG
+    bool rw_nt;      // non-temporal y stores in the register-weights variant
     TiledCfg tiled;
     size_t ws_bytes;  // unfused only
 };
@@ -172,7 +175,17 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
     p.kernel = p.forced ? base : (int)dispatch(g, dtype, table);
     if (p.kernel == TG_KERNEL_IGEMM) {
         if (!igemm_serves(g, dtype)) return TG_ERR_UNSUPPORTED;
-        p.igemm_cfg = choose_igemm_cfg(g);
+        if (igemm_rw_serves(g) && env_int("TG_IGEMM_RW", 1) != 0 && env_int("TG_IGEMM_CFG", -1) < 0) {
+            p.igemm_cfg = -1;
+            igemm_rw_choose(g, &p.rw_nf, &p.rw_cs, &p.rw_ncw);
+            p.rw_nf = env_int("TG_RW_NF", p.rw_nf);
+            p.rw_cs = env_int("TG_RW_CS", p.rw_cs);
+            p.rw_ncw = env_int("TG_RW_NCW", p.rw_ncw);
+            p.rw_grid = igemm_rw_grid(g, kCUs * env_int("TG_RW_WG_PER_CU", 1));
+            p.rw_nt = env_int("TG_NT", 1) != 0;
+        } else {
+            p.igemm_cfg = choose_igemm_cfg(g);
+        }
     } else if (p.kernel == TG_KERNEL_TILED) {
         if (!tiled_serves(g, dtype, &p.tiled)) return TG_ERR_UNSUPPORTED;
     }
@@ -241,7 +254,15 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, c
     hipError_t e;
     switch (kernel) {
         case TG_KERNEL_IGEMM:
-            e = launch_igemm(g, plan->igemm_cfg, identity, x, w, bn_scale, bn_bias, conv_out, s);
+            if (plan->igemm_cfg < 0 && env_int("TG_STREAM", 0) > 0)
+                e = launch_igemm_stream(g, env_int("TG_STREAM", 16), plan->rw_nt, identity, x, w,
+                                        bn_scale, bn_bias, conv_out, s);
+            else if (plan->igemm_cfg < 0)
+                e = launch_igemm_rw(g, plan->rw_grid, plan->rw_nf, plan->rw_cs, plan->rw_ncw,
+                                    plan->rw_nt, identity, x, w, bn_scale, bn_bias, conv_out, s);
+            else
+                e = launch_igemm(g, plan->igemm_cfg, identity, x, w, bn_scale, bn_bias, conv_out,
+                                 s);
             break;
         case TG_KERNEL_TILED:
             e = launch_tiled(g, plan->tiled, identity, x, w, bn_scale, bn_bias, conv_out, s);
@@ -285,7 +306,10 @@ tg_status tg_conv_bn_silu_describe(const tg_conv_bn_silu_plan* plan, char* buf, 
     if (len == 0) return TG_OK;
     const ConvGeom& g = plan->g;
     char k[160];
-    if (plan->kernel == TG_KERNEL_IGEMM) {
+    if (plan->kernel == TG_KERNEL_IGEMM && plan->igemm_cfg < 0) {
+        snprintf(k, sizeof(k), "igemm_rw (weights in VGPRs) nf=%d cs=%d ncw=%d grid=%d%s",
+                 plan->rw_nf, plan->rw_cs, plan->rw_ncw, plan->rw_grid, plan->rw_nt ? " nt" : "");
+    } else if (plan->kernel == TG_KERNEL_IGEMM) {
         const IgemmCfg& c = igemm_cfg(plan->igemm_cfg);
         int tm = (g.M + c.BM - 1) / c.BM, tn = (g.C_out + c.BN - 1) / c.BN;
         snprintf(k, sizeof(k), "igemm cfg=%d BM=%d BN=%d BK=%d waves=%dx%d grid=%d", plan->igemm_cfg,

@@ -41,6 +41,16 @@ hipError_t launch_tiled(const ConvGeom& g, const TiledCfg& c, bool identity, con
                         hipStream_t s);
 hipError_t launch_igemm(const ConvGeom& g, int cfg, bool identity, const void* x, const void* w,
                         const float* scale, const float* bias, void* y, hipStream_t s);
+// Register-resident-weights implicit GEMM (igemm_rw.hip): K <= 64, C_out <= 256.
+bool igemm_rw_serves(const ConvGeom& g);
+void igemm_rw_choose(const ConvGeom& g, int* nf, int* cs, int* ncw);
+int igemm_rw_grid(const ConvGeom& g, int slots);
+hipError_t launch_igemm_rw(const ConvGeom& g, int grid, int nf, int cs, int ncw, bool nt,
+                           bool identity, const void* x, const void* w, const float* scale,
+                           const float* bias, void* y, hipStream_t s);
+hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, bool nt, bool identity,
+                               const void* x, const void* w, const float* scale,
+                               const float* bias, void* y, hipStream_t s);
 hipError_t launch_bn_apply(bool f32, const void* t1, const float* scale, const float* bias, void* t2,
                            long long total, int C, hipStream_t s);
 hipError_t launch_silu_apply(bool f32, const void* t2, void* y, long long total, hipStream_t s);
