@@ -24,6 +24,7 @@ struct tg_conv_bn_silu_plan {
     bool unfused;
     bool forced;     // kernel was requested explicitly (alignment errors instead of fallback)
     int igemm_cfg;   // index into the igemm variant table (-1: register-weights variant)
+    int dma_cfg;     // >= 0: direct-to-LDS pipelined variant with this tile
     int rw_grid;     // persistent grid of the register-weights variant
     int rw_nf, rw_cs, rw_ncw;  // its weight fragments per wave, waves per block, waves per WG
     bool rw_nt;      // non-temporal y stores in the register-weights variant
@@ -112,6 +113,31 @@ double igemm_cost(const ConvGeom& g, const IgemmCfg& c) {
     return t_mfma > t_mem ? t_mfma : t_mem;
 }
 
+// Estimated time of a direct-to-LDS igemm tile: one workgroup per CU at a
+// time, so the busiest CU runs ceil(tiles / CUs) tiles back to back; the
+// wave tile's LDS read rate scales the MFMA time when it exceeds LDS speed.
+double igemm_dma_cost(const ConvGeom& g, const IgemmCfg& c) {
+    long long tiles = (long long)((g.M + c.BM - 1) / c.BM) * ((g.C_out + c.BN - 1) / c.BN);
+    long long per_cu = (tiles + kCUs - 1) / kCUs;
+    int FM = c.BM / c.WM / 16, FN = c.BN / c.WN / 16;
+    double mfma_clk = 16384.0 / kMfmaFlopPerClkSimd;
+    double lds_need = 4.0 * (FM + FN) * 1024.0 / (FM * FN * mfma_clk);
+    double lds_factor = lds_need > kLdsBytesPerClkCu ? lds_need / kLdsBytesPerClkCu : 1.0;
+    return per_cu * (double)c.BM * c.BN * g.K * lds_factor;
+}
+
+int choose_igemm_dma_cfg(const ConvGeom& g) {
+    int forced = env_int("TG_DMA_CFG", -1);
+    if (forced >= 0 && forced < igemm_dma_num_cfgs()) return forced;
+    int best = 0;
+    double best_cost = 1e300;
+    for (int i = 0; i < igemm_dma_num_cfgs(); ++i) {
+        double c = igemm_dma_cost(g, igemm_dma_cfg(i));
+        if (c < best_cost) { best = i; best_cost = c; }
+    }
+    return best;
+}
+
 int choose_igemm_cfg(const ConvGeom& g) {
     int forced = env_int("TG_IGEMM_CFG", -1);
     if (forced >= 0 && forced < igemm_num_cfgs()) return forced;
@@ -172,6 +198,7 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
     p.dtype = dtype;
     p.unfused = unfused;
     p.forced = base != TG_KERNEL_AUTO;
+    p.dma_cfg = -1;
     p.kernel = p.forced ? base : (int)dispatch(g, dtype, table);
     if (p.kernel == TG_KERNEL_IGEMM) {
         if (!igemm_serves(g, dtype)) return TG_ERR_UNSUPPORTED;
@@ -183,6 +210,10 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
             p.rw_ncw = env_int("TG_RW_NCW", p.rw_ncw);
             p.rw_grid = igemm_rw_grid(g, kCUs * env_int("TG_RW_WG_PER_CU", 1));
             p.rw_nt = env_int("TG_NT", 1) != 0;
+        } else if (igemm_dma_serves(g) && env_int("TG_IGEMM_DMA", 1) != 0 &&
+                   env_int("TG_IGEMM_CFG", -1) < 0) {
+            p.igemm_cfg = 0;
+            p.dma_cfg = choose_igemm_dma_cfg(g);
         } else {
             p.igemm_cfg = choose_igemm_cfg(g);
         }
@@ -257,6 +288,9 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, c
             if (plan->igemm_cfg < 0 && env_int("TG_STREAM", 0) > 0)
                 e = launch_igemm_stream(g, env_int("TG_STREAM", 16), plan->rw_nt, identity, x, w,
                                         bn_scale, bn_bias, conv_out, s);
+            else if (plan->dma_cfg >= 0)
+                e = launch_igemm_dma(g, plan->dma_cfg, identity, x, w, bn_scale, bn_bias, conv_out,
+                                     s);
             else if (plan->igemm_cfg < 0)
                 e = launch_igemm_rw(g, plan->rw_grid, plan->rw_nf, plan->rw_cs, plan->rw_ncw,
                                     plan->rw_nt, identity, x, w, bn_scale, bn_bias, conv_out, s);
@@ -309,6 +343,11 @@ tg_status tg_conv_bn_silu_describe(const tg_conv_bn_silu_plan* plan, char* buf, 
     if (plan->kernel == TG_KERNEL_IGEMM && plan->igemm_cfg < 0) {
         snprintf(k, sizeof(k), "igemm_rw (weights in VGPRs) nf=%d cs=%d ncw=%d grid=%d%s",
                  plan->rw_nf, plan->rw_cs, plan->rw_ncw, plan->rw_grid, plan->rw_nt ? " nt" : "");
+    } else if (plan->kernel == TG_KERNEL_IGEMM && plan->dma_cfg >= 0) {
+        const IgemmCfg& c = igemm_dma_cfg(plan->dma_cfg);
+        int tm = (g.M + c.BM - 1) / c.BM, tn = (g.C_out + c.BN - 1) / c.BN;
+        snprintf(k, sizeof(k), "igemm_dma cfg=%d BM=%d BN=%d BK=64 waves=%dx%d grid=%d",
+                 plan->dma_cfg, c.BM, c.BN, c.WM, c.WN, tm * tn);
     } else if (plan->kernel == TG_KERNEL_IGEMM) {
         const IgemmCfg& c = igemm_cfg(plan->igemm_cfg);
         int tm = (g.M + c.BM - 1) / c.BM, tn = (g.C_out + c.BN - 1) / c.BN;

@@ -51,6 +51,13 @@ hipError_t launch_igemm_rw(const ConvGeom& g, int grid, int nf, int cs, int ncw,
 hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, bool nt, bool identity,
                                const void* x, const void* w, const float* scale,
                                const float* bias, void* y, hipStream_t s);
+// Direct-to-LDS pipelined implicit GEMM (igemm_dma.hip): C_in % 64 == 0.
+bool igemm_dma_serves(const ConvGeom& g);
+int igemm_dma_num_cfgs();
+const IgemmCfg& igemm_dma_cfg(int i);
+hipError_t launch_igemm_dma(const ConvGeom& g, int cfg, bool identity, const void* x,
+                            const void* w, const float* scale, const float* bias, void* y,
+                            hipStream_t s);
 hipError_t launch_bn_apply(bool f32, const void* t1, const float* scale, const float* bias, void* t2,
                            long long total, int C, hipStream_t s);
 hipError_t launch_silu_apply(bool f32, const void* t2, void* y, long long total, hipStream_t s);
