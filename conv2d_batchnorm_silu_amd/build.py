@@ -23,8 +23,12 @@ ARCH = "gfx950"
 
 # Packed FP32 instructions are switched off for all device code: the compiler
 # would otherwise form them from ordinary float arithmetic.
+# MFMA results are kept in ordinary VGPRs (gfx950 MFMA may write either file):
+# the epilogue then reads its accumulators without one v_accvgpr_read per
+# value, which is a sixth of the fused epilogue's VALU work.
 HIPCC_FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
                "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-Xarch_device", "-mllvm=-amdgpu-mfma-vgpr-form",
                "-Wall", "-Wno-unused-function", "-I", INCLUDE, "-I", CSRC]
 
 

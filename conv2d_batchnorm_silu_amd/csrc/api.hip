@@ -25,6 +25,8 @@ struct tg_conv_bn_silu_plan {
     bool forced;     // kernel was requested explicitly (alignment errors instead of fallback)
     int igemm_cfg;   // index into the igemm variant table (-1: register-weights variant)
     int dma_cfg;     // >= 0: direct-to-LDS pipelined variant with this tile
+    int tm_rows;     // > 0: tiled kernel runs on the matrix cores with bands of this many rows
+    int tm_pipe_grid;  // > 0: ... in its persistent pipelined form with this grid
     int rw_grid;     // persistent grid of the register-weights variant
     int rw_nf, rw_cs, rw_ncw;  // its weight fragments per wave, waves per block, waves per WG
     bool rw_nt;      // non-temporal y stores in the register-weights variant
@@ -219,6 +221,13 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
         }
     } else if (p.kernel == TG_KERNEL_TILED) {
         if (!tiled_serves(g, dtype, &p.tiled)) return TG_ERR_UNSUPPORTED;
+        if (tiled_mfma_serves(g) && env_int("TG_TILED_MFMA", 1) != 0) {
+            p.tm_rows = env_int("TG_TM_ROWS", tiled_mfma_rows(g));
+            if (tiled_mfma_pipe_serves(g) && env_int("TG_TM_PIPE", 1) != 0) {
+                p.tm_rows = env_int("TG_TM_ROWS", 2);
+                p.tm_pipe_grid = kCUs * env_int("TG_TM_WG_PER_CU", 4);
+            }
+        }
     }
     size_t ysz = (size_t)g.M * g.C_out * (dtype == TG_F16 ? 2 : 4);
     p.ws_bytes = unfused ? 2 * round256(ysz) : 0;
@@ -299,7 +308,14 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, c
                                  s);
             break;
         case TG_KERNEL_TILED:
-            e = launch_tiled(g, plan->tiled, identity, x, w, bn_scale, bn_bias, conv_out, s);
+            if (plan->tm_pipe_grid > 0)
+                e = launch_tiled_mfma_pipe(g, plan->tm_rows, plan->tm_pipe_grid, identity, x, w,
+                                           bn_scale, bn_bias, conv_out, s);
+            else if (plan->tm_rows > 0)
+                e = launch_tiled_mfma(g, plan->tm_rows, identity, x, w, bn_scale, bn_bias,
+                                      conv_out, s);
+            else
+                e = launch_tiled(g, plan->tiled, identity, x, w, bn_scale, bn_bias, conv_out, s);
             break;
         default:
             e = launch_scalar(g, f32, identity, x, w, bn_scale, bn_bias, conv_out, s);
@@ -353,6 +369,12 @@ tg_status tg_conv_bn_silu_describe(const tg_conv_bn_silu_plan* plan, char* buf, 
         int tm = (g.M + c.BM - 1) / c.BM, tn = (g.C_out + c.BN - 1) / c.BN;
         snprintf(k, sizeof(k), "igemm cfg=%d BM=%d BN=%d BK=%d waves=%dx%d grid=%d", plan->igemm_cfg,
                  c.BM, c.BN, c.BK, c.WM, c.WN, tm * tn);
+    } else if (plan->kernel == TG_KERNEL_TILED && plan->tm_pipe_grid > 0) {
+        snprintf(k, sizeof(k), "tiled_mfma_pipe R=%d grid=%d", plan->tm_rows,
+                 plan->tm_pipe_grid);
+    } else if (plan->kernel == TG_KERNEL_TILED && plan->tm_rows > 0) {
+        int bands = (g.P + plan->tm_rows - 1) / plan->tm_rows;
+        snprintf(k, sizeof(k), "tiled_mfma R=%d grid=%d", plan->tm_rows, g.N * bands);
     } else if (plan->kernel == TG_KERNEL_TILED) {
         int bands = (g.P + plan->tiled.R - 1) / plan->tiled.R;
         snprintf(k, sizeof(k), "tiled R=%d lds=%d grid=%d", plan->tiled.R, plan->tiled.lds_bytes,

@@ -198,10 +198,7 @@ __global__ __launch_bounds__(256, 1) void conv2d_bn_silu_igemm_dma(
         float sc[4], bi[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int o = n0 + cb + e;
-            const bool ok = (EPI == EPI_FUSED) && o < g.C_out;
-            sc[e] = ok ? scale[o] : 0.f;
-            bi[e] = ok ? bias[o] : 0.f;
+            epi_consts<EPI>(scale, bias, n0 + cb + e, g.C_out, sc[e], bi[e]);
         }
 #pragma unroll
         for (int j = 0; j < S::FM; ++j) {

@@ -37,11 +37,8 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_scalar(
             for (int c = 0; c < g.C_in; ++c) acc = __builtin_fmaf(to_f32(xp[c]), to_f32(wp[c]), acc);
         }
     }
-    float sc = 0.0f, bi = 0.0f;
-    if (EPI == EPI_FUSED) {
-        sc = scale[k];
-        bi = bias[k];
-    }
+    float sc, bi;
+    epi_consts<EPI>(scale, bias, k, g.C_out, sc, bi);
     y[idx] = from_f32<T>(epilogue<EPI>(acc, sc, bi));
 }
 

@@ -27,15 +27,48 @@ enum Epilogue { EPI_FUSED = 0, EPI_IDENTITY = 1 };
 // exp2 (v_exp_f32) and the hardware reciprocal (v_rcp_f32). For v below about
 // -88 the exponential is +inf and the reciprocal 0, so silu(v) is -0 (no NaN);
 // for large v the exponential underflows to 0 and silu(v) = v.
+constexpr float kLog2e = 1.4426950408889634f;
+
 __device__ __forceinline__ float silu_f32(float v) {
-    const float kNegLog2e = -1.4426950408889634f;
-    float e = __builtin_amdgcn_exp2f(v * kNegLog2e);
+    float e = __builtin_amdgcn_exp2f(-v * kLog2e);
     return v * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// The fused epilogue in five VALU operations. Kernels load each channel's
+// BatchNorm scale and bias once and keep s2 = scale*log2(e), b2 =
+// bias*log2(e) (epi_consts); then, with v = acc*scale + bias,
+//   v2 = fma(acc, s2, b2)            = v * log2(e)
+//   e  = 2^(-v2)                     = e^(-v)        (negation is free)
+//   d  = fma(e, log2(e), log2(e))    = (1 + e^(-v)) * log2(e)
+//   y  = v2 * rcp(d)                 = v / (1 + e^(-v)) = v * sigmoid(v).
+// The identity epilogue (first kernel of the unfused baseline) returns acc.
+// s2, b2 of output channel o (zero past C_out). The index is clamped instead
+// of branching around the load, so all of a kernel's constant loads are in
+// flight together and its prologue waits for one memory latency, not one per
+// channel. The identity epilogue loads nothing.
 template <int EPI>
-__device__ __forceinline__ float epilogue(float acc, float scale, float bias) {
-    if (EPI == EPI_FUSED) return silu_f32(__builtin_fmaf(acc, scale, bias));
+__device__ __forceinline__ void epi_consts(const float* __restrict__ scale,
+                                           const float* __restrict__ bias, int o, int C_out,
+                                           float& s2, float& b2) {
+    if (EPI != EPI_FUSED) {
+        s2 = b2 = 0.0f;
+        return;
+    }
+    const bool ok = o < C_out;
+    const int oc = ok ? o : C_out - 1;
+    const float s = scale[oc], b = bias[oc];
+    s2 = ok ? s * kLog2e : 0.0f;
+    b2 = ok ? b * kLog2e : 0.0f;
+}
+
+template <int EPI>
+__device__ __forceinline__ float epilogue(float acc, float s2, float b2) {
+    if (EPI == EPI_FUSED) {
+        float v2 = __builtin_fmaf(acc, s2, b2);
+        float e = __builtin_amdgcn_exp2f(-v2);
+        float d = __builtin_fmaf(e, kLog2e, kLog2e);
+        return v2 * __builtin_amdgcn_rcpf(d);
+    }
     return acc;
 }
 

@@ -58,6 +58,16 @@ const IgemmCfg& igemm_dma_cfg(int i);
 hipError_t launch_igemm_dma(const ConvGeom& g, int cfg, bool identity, const void* x,
                             const void* w, const float* scale, const float* bias, void* y,
                             hipStream_t s);
+// Tiled direct conv on MFMA (tiled_mfma.hip): K <= 32, C_out <= 32.
+bool tiled_mfma_serves(const ConvGeom& g);
+int tiled_mfma_rows(const ConvGeom& g);
+hipError_t launch_tiled_mfma(const ConvGeom& g, int R, bool identity, const void* x,
+                             const void* w, const float* scale, const float* bias, void* y,
+                             hipStream_t s);
+bool tiled_mfma_pipe_serves(const ConvGeom& g);
+hipError_t launch_tiled_mfma_pipe(const ConvGeom& g, int R, int grid, bool identity,
+                                  const void* x, const void* w, const float* scale,
+                                  const float* bias, void* y, hipStream_t s);
 hipError_t launch_bn_apply(bool f32, const void* t1, const float* scale, const float* bias, void* t2,
                            long long total, int C, hipStream_t s);
 hipError_t launch_silu_apply(bool f32, const void* t2, void* y, long long total, hipStream_t s);

@@ -111,8 +111,8 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_tiled(
             half8_t h;
 #pragma unroll
             for (int j = 0; j < CG; ++j) {
-                float sc = EPI == EPI_FUSED ? scale[o0 + j] : 0.f;
-                float bi = EPI == EPI_FUSED ? bias[o0 + j] : 0.f;
+                float sc, bi;
+                epi_consts<EPI>(scale, bias, o0 + j, g.C_out, sc, bi);
                 h[j] = (f16)epilogue<EPI>(acc[j], sc, bi);
             }
             *(half8_t*)yp = h;
@@ -120,8 +120,8 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_tiled(
 #pragma unroll
             for (int j = 0; j < CG; ++j) {
                 if (o0 + j < g.C_out) {
-                    float sc = EPI == EPI_FUSED ? scale[o0 + j] : 0.f;
-                    float bi = EPI == EPI_FUSED ? bias[o0 + j] : 0.f;
+                    float sc, bi;
+                    epi_consts<EPI>(scale, bias, o0 + j, g.C_out, sc, bi);
                     yp[j] = (f16)epilogue<EPI>(acc[j], sc, bi);
                 }
             }
