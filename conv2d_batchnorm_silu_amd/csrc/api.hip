@@ -30,6 +30,8 @@ struct tg_conv_bn_silu_plan {
     int rw_grid;     // persistent grid of the register-weights variant
     int rw_nf, rw_cs, rw_ncw;  // its weight fragments per wave, waves per block, waves per WG
     bool rw_nt;      // non-temporal y stores in the register-weights variant
+    int cu_waves;    // > 0: one-workgroup-per-CU variant with this many wavefronts
+    int cu_pd;       // ... and this input prefetch depth
     TiledCfg tiled;
     size_t ws_bytes;  // unfused only
 };
@@ -204,14 +206,26 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
     p.kernel = p.forced ? base : (int)dispatch(g, dtype, table);
     if (p.kernel == TG_KERNEL_IGEMM) {
         if (!igemm_serves(g, dtype)) return TG_ERR_UNSUPPORTED;
-        if (igemm_rw_serves(g) && env_int("TG_IGEMM_RW", 1) != 0 && env_int("TG_IGEMM_CFG", -1) < 0) {
+        if (igemm_rw_serves(g) && env_int("TG_IGEMM_RW", 1) != 0 &&
+            env_int("TG_IGEMM_CFG", -1) < 0) {
             p.igemm_cfg = -1;
             igemm_rw_choose(g, &p.rw_nf, &p.rw_cs, &p.rw_ncw);
             p.rw_nf = env_int("TG_RW_NF", p.rw_nf);
             p.rw_cs = env_int("TG_RW_CS", p.rw_cs);
             p.rw_ncw = env_int("TG_RW_NCW", p.rw_ncw);
+            if (!igemm_rw_valid(g, p.rw_nf, p.rw_cs, p.rw_ncw))  // override does not fit
+                igemm_rw_choose(g, &p.rw_nf, &p.rw_cs, &p.rw_ncw);
             p.rw_grid = igemm_rw_grid(g, kCUs * env_int("TG_RW_WG_PER_CU", 1));
             p.rw_nt = env_int("TG_NT", 1) != 0;
+            // TG_CU: wavefronts per 64-channel slice of the one-workgroup-per-CU
+            // kernel (0 disables it); 3 (12 wavefronts for 256 channels)
+            // measured best on MI355X for the 1x1 C_in=64 layer. The
+            // register-weights kernel stays the fallback for BatchNorm vectors
+            // that are not 16-byte aligned.
+            if (igemm_cu_serves(g) && env_int("TG_CU", 3) > 0) {
+                p.cu_waves = igemm_cu_waves(g, env_int("TG_CU", 3));
+                p.cu_pd = env_int("TG_CU_PD", 2);
+            }
         } else if (igemm_dma_serves(g) && env_int("TG_IGEMM_DMA", 1) != 0 &&
                    env_int("TG_IGEMM_CFG", -1) < 0) {
             p.igemm_cfg = 0;
@@ -294,7 +308,10 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, c
     hipError_t e;
     switch (kernel) {
         case TG_KERNEL_IGEMM:
-            if (plan->igemm_cfg < 0 && env_int("TG_STREAM", 0) > 0)
+            if (plan->cu_waves > 0 && aligned16(bn_scale) && aligned16(bn_bias))
+                e = launch_igemm_cu(g, plan->cu_waves, plan->cu_pd, plan->rw_nt, identity, x, w,
+                                    bn_scale, bn_bias, conv_out, s);
+            else if (plan->igemm_cfg < 0 && env_int("TG_STREAM", 0) > 0)
                 e = launch_igemm_stream(g, env_int("TG_STREAM", 16), plan->rw_nt, identity, x, w,
                                         bn_scale, bn_bias, conv_out, s);
             else if (plan->dma_cfg >= 0)
@@ -321,7 +338,10 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, c
             e = launch_scalar(g, f32, identity, x, w, bn_scale, bn_bias, conv_out, s);
             break;
     }
-    if (e != hipSuccess) return TG_ERR_HIP;
+    if (e != hipSuccess) {
+        if (env_flag("TG_LOG")) fprintf(stderr, "[tgconv] launch failed: %s\n", hipGetErrorString(e));
+        return TG_ERR_HIP;
+    }
     if (plan->unfused) {
         long long total = (long long)g.M * g.C_out;
         e = launch_bn_apply(f32, conv_out, bn_scale, bn_bias, t2, total, g.C_out, s);
@@ -356,7 +376,11 @@ tg_status tg_conv_bn_silu_describe(const tg_conv_bn_silu_plan* plan, char* buf, 
     if (len == 0) return TG_OK;
     const ConvGeom& g = plan->g;
     char k[160];
-    if (plan->kernel == TG_KERNEL_IGEMM && plan->igemm_cfg < 0) {
+    if (plan->kernel == TG_KERNEL_IGEMM && plan->cu_waves > 0) {
+        int nb = (g.M + 15) / 16;
+        snprintf(k, sizeof(k), "igemm_cu (one workgroup per CU) waves=%d pd=%d grid=%d%s",
+                 plan->cu_waves, plan->cu_pd, nb < 256 ? nb : 256, plan->rw_nt ? " nt" : "");
+    } else if (plan->kernel == TG_KERNEL_IGEMM && plan->igemm_cfg < 0) {
         snprintf(k, sizeof(k), "igemm_rw (weights in VGPRs) nf=%d cs=%d ncw=%d grid=%d%s",
                  plan->rw_nf, plan->rw_cs, plan->rw_ncw, plan->rw_grid, plan->rw_nt ? " nt" : "");
     } else if (plan->kernel == TG_KERNEL_IGEMM && plan->dma_cfg >= 0) {

@@ -66,6 +66,39 @@ __device__ __forceinline__ void wait_rounds_pending(int k) {
     }
 }
 
+// Direct-to-LDS 16-byte buffer load (lane l's bytes land at lds + 16*l;
+// offsets past num_records read as zeros), written as inline assembly so the
+// compiler does not see an LDS write it must wait for: the caller orders it
+// with explicit vmcnt waits. rsrc = {base_lo, base_hi, num_records, flags};
+// lds must be wave-uniform.
+__device__ __forceinline__ void lds_dma16(u32x4_t rsrc, unsigned voff, unsigned lds) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(lds)
+                 : "memory");
+}
+
+__device__ __forceinline__ u32x4_t raw_buffer_rsrc(const void* base, unsigned bytes) {
+    const unsigned long long a = (unsigned long long)base;
+    u32x4_t r;
+    r[0] = (unsigned)a;
+    r[1] = (unsigned)(a >> 32) & 0xffffu;  // stride 0, no swizzle
+    r[2] = bytes;
+    r[3] = 0x00020000u;                    // same descriptor flags as the loader wave
+    return r;
+}
+
+// Orders one wave's LDS writes before its following LDS reads of other lanes'
+// data. The LDS executes a wave's operations in issue order, so only the
+// compiler must be kept from moving accesses across this point. (A wavefront-
+// scope fence would do the same but also waits for outstanding nontemporal
+// stores.)
+__device__ __forceinline__ void wave_lds_sync() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Output channel computed by row i of weight fragment f (see header).
 __device__ __forceinline__ int rw_sigma(int f, int i) {
     return 32 * (f >> 1) + 8 * (i >> 2) + 4 * (f & 1) + (i & 3);
@@ -256,7 +289,7 @@ __global__ __launch_bounds__((NCW + 1) * 64) void conv2d_bn_silu_igemm_rw(
 // pieces of each pixel row. With four or more such wavefronts per SIMD, the
 // waits on the shared load/store counter of one wavefront are covered by the
 // others.
-template <int NF, int KS, int EPI, bool NT, bool XDMA>
+template <int NF, int KS, int EPI, bool NT, bool XDMA, int PD>
 __global__ __launch_bounds__(256) void conv2d_bn_silu_igemm_stream(
     const f16* __restrict__ x, const f16* __restrict__ w, const float* __restrict__ scale,
     const float* __restrict__ bias, f16* __restrict__ y, ConvGeom g, int nblocks, int ngroups) {
@@ -267,8 +300,10 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_igemm_stream(
     constexpr int RPS = 64 / LPRW;    // tile rows per store instruction
     static_assert(64 % LPRW == 0 && 16 % RPS == 0, "store split");
     __shared__ __attribute__((aligned(16))) f16 tile[4][16 * TROW];
-    // Full-line x staging (XDMA): per wave two buffers of 16 pixels x 64 k.
-    __shared__ __attribute__((aligned(16))) f16 xst[XDMA ? 4 : 1][2][16 * 64];
+    // Full-line x staging (XDMA): per wave PD buffers of 16 pixels x 64 k,
+    // block it + PD fetched into the buffer block it was read from.
+    static_assert(!XDMA || (PD >= 1 && 4 * PD - 2 <= 63), "prefetch depth");
+    __shared__ __attribute__((aligned(16))) f16 xst[XDMA ? 4 : 1][XDMA ? PD : 1][16 * 64];
 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int lr = lane & 15, lg = lane >> 4;
@@ -331,8 +366,7 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_igemm_stream(
     // 64 k = one 128-byte line, lane l -> pixel 8h + l/8, piece (l%8) ^ swz,
     // slot l%8, with swz = ((8h + l/8) >> 1) & 7 (conflict-free fragment reads).
     const unsigned xbytes = (unsigned)g.N * g.H * g.W * g.C_in * 2u;
-    const __amdgpu_buffer_rsrc_t xrs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)x, (short)0, (int)xbytes, 0x00020000);
+    const u32x4_t xrs = raw_buffer_rsrc(x, xbytes);
     auto fetch_dma = [&](int blk, int buf) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
@@ -345,9 +379,9 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_igemm_stream(
                 // pixel m's K = C_in values are contiguous at m * C_in.
                 off = (unsigned)((m * g.C_in + piece * 8) * 2);
             }
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                xrs, (__attribute__((address_space(3))) void*)&xst[XDMA ? wave : 0][buf][h * 512],
-                16, off, 0, 0, 0);
+            const unsigned la = (unsigned)(uintptr_t)(
+                (__attribute__((address_space(3))) f16*)&xst[XDMA ? wave : 0][buf][h * 512]);
+            lds_dma16(xrs, off, __builtin_amdgcn_readfirstlane(la));
         }
     };
     const int ocs = (lane % LPRW) * 8;        // channel within the slice, store phase
@@ -355,11 +389,23 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_igemm_stream(
     const bool vec_store = (g.C_out & 7) == 0;
     half8_t xc[KS], xn_[KS];
     int blk = stream;
-    if (XDMA) fetch_dma(blk, 0); else fetch(blk, xc);
+    if (XDMA) {
+#pragma unroll
+        for (int d = 0; d < PD; ++d) fetch_dma(blk + d * nstreams, d);
+    } else {
+        fetch(blk, xc);
+    }
     for (int it = 0; blk < nblocks; blk += nstreams, ++it) {
+        const int B = it % PD;
         if (XDMA) {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            const f16* xb = &xst[wave][it & 1][0];
+            // Wait for this block's two direct-to-LDS loads only, not for the
+            // stores issued after them. Every iteration issues exactly two
+            // loads (after its MFMAs) and two stores (C_out % CW == 0 and a
+            // full block; only a wave's last block may be partial), so the
+            // loads of block it are followed by 2*(PD-1-it) + 4*it operations
+            // when it < PD (prologue fetch) and by 2 + 4*(PD-1) afterwards.
+            if (it < PD) wait_vmcnt<2 * (PD - 1)>(); else wait_vmcnt<4 * PD - 2>();
+            const f16* xb = &xst[wave][B][0];
 #pragma unroll
             for (int s = 0; s < KS; ++s) {
                 const int pc = 4 * s + lg;
@@ -374,7 +420,7 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_igemm_stream(
 #pragma unroll
             for (int f = 0; f < NF; ++f)
                 acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[f][s], xc[s], acc[f], 0, 0, 0);
-        if (XDMA) fetch_dma(blk + nstreams, (it & 1) ^ 1);
+        if (XDMA) fetch_dma(blk + PD * nstreams, B);
         else fetch(blk + nstreams, xn_);  // after the MFMAs have consumed xc
 #pragma unroll
         for (int j = 0; j < NF / 2; ++j) {
@@ -386,9 +432,7 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_igemm_stream(
             }
             *(half8_t*)(tl + lr * TROW + 32 * j + 8 * lg) = h;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_lds_sync();
 #pragma unroll
         for (int i = 0; i < 16 / RPS; ++i) {
             const int row = orow + RPS * i;
@@ -408,9 +452,7 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_igemm_stream(
                 }
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        wave_lds_sync();
         if (!XDMA) {
 #pragma unroll
             for (int s = 0; s < KS; ++s) xc[s] = xn_[s];
@@ -435,19 +477,25 @@ hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, bool nt, boo
     int grid = (int)(waves / 4);
     int ks = g.K <= 32 ? 1 : 2;
     const bool xdma_ok = g.kh == 1 && g.kw == 1 && g.stride == 1 && g.pad == 0 && ks == 2 &&
-                         g.C_in == 64;
-    const bool xdma = xdma_ok && getenv("TG_XDMA") && atoi(getenv("TG_XDMA")) != 0;
+                         g.C_in == 64 && g.C_out % CW == 0;
+    // TG_XDMA=d (1..4) selects the full-line staging path with prefetch depth d.
+    int pd = 0;
+    if (xdma_ok && getenv("TG_XDMA")) pd = atoi(getenv("TG_XDMA"));
+    if (pd < 0 || pd > 4) pd = 0;
 #define TG_ST_LAUNCH(KSV, EPI, NTV)                                                              \
     do {                                                                                         \
-        if (xdma)                                                                                \
-            hipLaunchKernelGGL((conv2d_bn_silu_igemm_stream<NF, KSV, EPI, NTV, true>), dim3(grid), \
-                               dim3(256), 0, s, (const f16*)x, (const f16*)w, scale, bias,        \
-                               (f16*)y, g, nblocks, ngroups);                                   \
-        else                                                                                     \
-            hipLaunchKernelGGL((conv2d_bn_silu_igemm_stream<NF, KSV, EPI, NTV, false>), dim3(grid), \
-                               dim3(256), 0, s, (const f16*)x, (const f16*)w, scale, bias,        \
-                               (f16*)y, g, nblocks, ngroups);                                   \
+        switch (pd) {                                                                            \
+            case 1: TG_ST_KERNEL(KSV, EPI, NTV, true, 1); break;                                \
+            case 2: TG_ST_KERNEL(KSV, EPI, NTV, true, 2); break;                                \
+            case 3: TG_ST_KERNEL(KSV, EPI, NTV, true, 3); break;                                \
+            case 4: TG_ST_KERNEL(KSV, EPI, NTV, true, 4); break;                                \
+            default: TG_ST_KERNEL(KSV, EPI, NTV, false, 1); break;                              \
+        }                                                                                        \
     } while (0)
+#define TG_ST_KERNEL(KSV, EPI, NTV, XD, PDV)                                                     \
+    hipLaunchKernelGGL((conv2d_bn_silu_igemm_stream<NF, KSV, EPI, NTV, XD, PDV>), dim3(grid),    \
+                       dim3(256), 0, s, (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g,   \
+                       nblocks, ngroups)
     if (ks == 1) {
         if (identity) { if (nt) TG_ST_LAUNCH(1, EPI_IDENTITY, true); else TG_ST_LAUNCH(1, EPI_IDENTITY, false); }
         else { if (nt) TG_ST_LAUNCH(1, EPI_FUSED, true); else TG_ST_LAUNCH(1, EPI_FUSED, false); }
@@ -455,6 +503,7 @@ hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, bool nt, boo
         if (identity) { if (nt) TG_ST_LAUNCH(2, EPI_IDENTITY, true); else TG_ST_LAUNCH(2, EPI_IDENTITY, false); }
         else { if (nt) TG_ST_LAUNCH(2, EPI_FUSED, true); else TG_ST_LAUNCH(2, EPI_FUSED, false); }
     }
+#undef TG_ST_KERNEL
 #undef TG_ST_LAUNCH
     return hipGetLastError();
 }
@@ -468,6 +517,16 @@ bool igemm_rw_serves(const ConvGeom& g) {
 #define TG_RW_CFGS(X)                                                                \
     X(4, 1, 1, 4) X(4, 2, 1, 4) X(4, 1, 2, 4) X(4, 2, 2, 4) X(4, 1, 4, 8) X(4, 2, 4, 8) \
     X(8, 1, 2, 4) X(8, 2, 2, 4) X(4, 2, 4, 4) X(4, 2, 2, 8)
+
+bool igemm_rw_valid(const ConvGeom& g, int nf, int cs, int ncw) {
+    const int ks = g.K <= 32 ? 1 : 2;
+    if (nf * 16 * cs < g.C_out) return false;
+#define X(NF_, KS_, CS_, NCW_) \
+    if (nf == NF_ && ks == KS_ && cs == CS_ && ncw == NCW_) return true;
+    TG_RW_CFGS(X)
+#undef X
+    return false;
+}
 
 void igemm_rw_choose(const ConvGeom& g, int* nf, int* cs, int* ncw) {
     if (g.C_out <= 64) { *nf = 4; *cs = 1; *ncw = 4; }

@@ -44,6 +44,7 @@ hipError_t launch_igemm(const ConvGeom& g, int cfg, bool identity, const void* x
 // Register-resident-weights implicit GEMM (igemm_rw.hip): K <= 64, C_out <= 256.
 bool igemm_rw_serves(const ConvGeom& g);
 void igemm_rw_choose(const ConvGeom& g, int* nf, int* cs, int* ncw);
+bool igemm_rw_valid(const ConvGeom& g, int nf, int cs, int ncw);
 int igemm_rw_grid(const ConvGeom& g, int slots);
 hipError_t launch_igemm_rw(const ConvGeom& g, int grid, int nf, int cs, int ncw, bool nt,
                            bool identity, const void* x, const void* w, const float* scale,
@@ -51,6 +52,15 @@ hipError_t launch_igemm_rw(const ConvGeom& g, int grid, int nf, int cs, int ncw,
 hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, bool nt, bool identity,
                                const void* x, const void* w, const float* scale,
                                const float* bias, void* y, hipStream_t s);
+
+// One persistent workgroup per compute unit (igemm_cu.hip): 1x1, stride 1,
+// unpadded, C_in == 64, C_out a multiple of 64 up to 256. nwaves is a
+// multiple of C_out/64 (at most 16); pd is the input prefetch depth (1..3).
+bool igemm_cu_serves(const ConvGeom& g);
+int igemm_cu_waves(const ConvGeom& g, int per_group);
+hipError_t launch_igemm_cu(const ConvGeom& g, int nwaves, int pd, bool nt, bool identity,
+                           const void* x, const void* w, const float* scale, const float* bias,
+                           void* y, hipStream_t s);
 // Direct-to-LDS pipelined implicit GEMM (igemm_dma.hip): C_in % 64 == 0.
 bool igemm_dma_serves(const ConvGeom& g);
 int igemm_dma_num_cfgs();

@@ -1,0 +1,154 @@
+"""GPU parity of every kernel variant that the dispatcher does not pick by
+default for some shape, each selected through its environment switch (read
+when a plan is created) and checked against the fp64 oracle:
+
+  * the one-workgroup-per-CU 1x1 kernel (TG_CU = wavefronts per 64-channel
+    slice, TG_CU_PD = input prefetch depth), over C_out = 64..256, ragged
+    pixel tails, fewer blocks than compute units and the full headline layer;
+  * the streaming 1x1 kernel with and without full-line input staging
+    (TG_STREAM, TG_XDMA = prefetch depth);
+  * the register-weights kernel's non-default splits and plain stores;
+  * the band-staged MFMA kernel without its persistent pipeline
+    (TG_TM_PIPE=0), and the VALU tiled kernel (TG_TILED_MFMA=0);
+  * the classic implicit GEMM (TG_IGEMM_RW=0, TG_IGEMM_DMA=0) and the
+    direct-to-LDS one (TG_IGEMM_RW=0).
+"""
+import pytest
+
+from conv2d_batchnorm_silu_amd import binding as B
+from conv2d_batchnorm_silu_amd.inputs import WORKLOADS, Workload
+
+from gpu_cases import check_workload, note
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.library()
+
+
+def _plan(wl, kernel="igemm"):
+    return B.ConvBnSilu(wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride, wl.pad,
+                        wl.dtype, kernel)
+
+
+ONE_BY_ONE = [
+    Workload("c64_k256_tail", 41, 1, 13, 17, 64, 256, 1, 1, 1, 0, "f16"),
+    Workload("c64_k64", 42, 2, 11, 9, 64, 64, 1, 1, 1, 0, "f16"),
+    Workload("c64_k128", 43, 1, 21, 23, 64, 128, 1, 1, 1, 0, "f16"),
+    Workload("c64_k192", 44, 3, 7, 5, 64, 192, 1, 1, 1, 0, "f16"),
+    Workload("c64_k256_m9", 45, 1, 3, 3, 64, 256, 1, 1, 1, 0, "f16"),
+    Workload("c64_k256_m16", 46, 1, 4, 4, 64, 256, 1, 1, 1, 0, "f16"),
+    Workload("c64_k256_many", 47, 4, 40, 40, 64, 256, 1, 1, 1, 0, "f16",
+             ("uniform", -3.0, 3.0)),
+]
+
+CU_CFGS = [("2", "1"), ("2", "2"), ("2", "3"), ("3", "2"), ("4", "1"), ("4", "2"), ("1", "2")]
+
+
+@pytest.mark.parametrize("per_group,pd", CU_CFGS, ids=["r%s_pd%s" % c for c in CU_CFGS])
+@pytest.mark.parametrize("wl", ONE_BY_ONE, ids=[w.name for w in ONE_BY_ONE])
+def test_cu_kernel(monkeypatch, wl, per_group, pd):
+    monkeypatch.setenv("TG_CU", per_group)
+    monkeypatch.setenv("TG_CU_PD", pd)
+    assert "igemm_cu" in _plan(wl).describe()
+    check_workload(wl, "igemm")
+    check_workload(wl, "unfused")
+
+
+@pytest.mark.parametrize("per_group,pd", [("2", "2"), ("3", "2"), ("4", "2")])
+def test_cu_kernel_headline(monkeypatch, per_group, pd):
+    monkeypatch.setenv("TG_CU", per_group)
+    monkeypatch.setenv("TG_CU_PD", pd)
+    wl = WORKLOADS["conv1x1_c64_k256"]
+    assert "igemm_cu" in _plan(wl, "auto").describe()
+    check_workload(wl, "auto")
+
+
+def test_cu_kernel_not_for_other_shapes(monkeypatch):
+    monkeypatch.setenv("TG_CU", "2")
+    for wl in (Workload("c32", 48, 1, 9, 9, 32, 256, 1, 1, 1, 0, "f16"),
+               Workload("k96", 49, 1, 9, 9, 64, 96, 1, 1, 1, 0, "f16"),
+               Workload("s2", 50, 1, 9, 9, 64, 256, 1, 1, 2, 0, "f16")):
+        note("%s -> %s" % (wl.name, _plan(wl).describe()))
+        assert "igemm_cu" not in _plan(wl).describe()
+        check_workload(wl, "igemm")
+
+
+@pytest.mark.parametrize("env", [
+    {"TG_STREAM": "8"},
+    {"TG_STREAM": "8", "TG_XDMA": "1"},
+    {"TG_STREAM": "8", "TG_XDMA": "2"},
+    {"TG_STREAM": "12", "TG_XDMA": "4"},
+    {"TG_STREAM": "8", "TG_NT": "0"},
+], ids=lambda e: "_".join("%s%s" % (k[3:].lower(), v) for k, v in e.items()))
+def test_stream_kernel(monkeypatch, env):
+    monkeypatch.setenv("TG_CU", "0")
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    for wl in ONE_BY_ONE[:4] + [Workload("c32_k96", 51, 2, 7, 9, 32, 96, 1, 1, 1, 0, "f16")]:
+        check_workload(wl, "igemm")
+
+
+@pytest.mark.parametrize("env", [
+    {"TG_RW_NF": "8", "TG_RW_CS": "2", "TG_RW_NCW": "4"},
+    {"TG_RW_NF": "4", "TG_RW_CS": "1", "TG_RW_NCW": "4"},
+    {"TG_NT": "0"},
+    {"TG_RW_WG_PER_CU": "2"},
+], ids=lambda e: "_".join("%s%s" % (k[3:].lower(), v) for k, v in e.items()))
+def test_register_weights_kernel(monkeypatch, env):
+    monkeypatch.setenv("TG_CU", "0")
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    for wl in ONE_BY_ONE[:4] + [Workload("c8_2x2", 52, 1, 9, 11, 8, 40, 2, 2, 1, 0, "f16")]:
+        assert "igemm_rw" in _plan(wl).describe()
+        check_workload(wl, "igemm")
+
+
+def test_cu_kernel_falls_back_for_unaligned_batchnorm_vectors():
+    """The one-workgroup-per-CU kernel fetches scale and bias with 16-byte
+    loads; with vectors offset by one float the register-weights kernel runs."""
+    wl = ONE_BY_ONE[0]
+    from gpu_cases import compare, fold, oracle_full, to_device
+    from conv2d_batchnorm_silu_amd.inputs import make_inputs
+    d = make_inputs(wl)
+    t = to_device(d)
+    s, b = fold(t)
+    sbuf = torch.empty(wl.C_out + 1, dtype=torch.float32, device="cuda")
+    bbuf = torch.empty(wl.C_out + 1, dtype=torch.float32, device="cuda")
+    sbuf[1:].copy_(s)
+    bbuf[1:].copy_(b)
+    plan = _plan(wl)
+    assert "igemm_cu" in plan.describe()
+    note("unaligned BN vectors: %s" % plan.describe())
+    y = plan.run(t["x"], t["w"], sbuf[1:], bbuf[1:])
+    torch.cuda.synchronize()
+    compare(y.cpu().numpy(), oracle_full(wl, d), "f16", "cu fallback, unaligned scale/bias")
+
+
+@pytest.mark.parametrize("env", [{"TG_TM_PIPE": "0"}, {"TG_TM_PIPE": "0", "TG_TM_ROWS": "4"},
+                                 {"TG_TM_ROWS": "4"}, {"TG_TILED_MFMA": "0"}],
+                         ids=["nopipe", "nopipe_r4", "pipe_r4", "valu"])
+def test_tiled_variants(monkeypatch, env):
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    for wl in (WORKLOADS["stem3x3s2_k16"].scaled(N=2), WORKLOADS["stem3x3s2_k24"].scaled(N=1),
+               Workload("stem_odd", 53, 1, 37, 29, 3, 24, 3, 3, 2, 1, "f16")):
+        check_workload(wl, "tiled")
+
+
+@pytest.mark.parametrize("env", [{"TG_IGEMM_RW": "0"}, {"TG_IGEMM_RW": "0", "TG_IGEMM_DMA": "0"}],
+                         ids=["dma", "classic"])
+def test_igemm_variants(monkeypatch, env):
+    monkeypatch.setenv("TG_CU", "0")
+    for k, v in env.items():
+        monkeypatch.setenv(k, v)
+    for wl in (WORKLOADS["conv3x3_c128_k128"].scaled(N=1, H=17, W=15),
+               WORKLOADS["conv7x7_c64_k64"].scaled(N=1, H=13, W=11),
+               ONE_BY_ONE[0], ONE_BY_ONE[2]):
+        check_workload(wl, "igemm")
