@@ -32,6 +32,7 @@ struct tg_conv_bn_silu_plan {
     bool rw_nt;      // non-temporal y stores in the register-weights variant
     int cu_waves;    // > 0: one-workgroup-per-CU variant with this many wavefronts
     int cu_pd;       // ... and this input prefetch depth
+    int patch_cfg;   // >= 0: patch-staged implicit GEMM with this tile
     TiledCfg tiled;
     size_t ws_bytes;  // unfused only
 };
@@ -127,7 +128,10 @@ double igemm_dma_cost(const ConvGeom& g, const IgemmCfg& c) {
     double mfma_clk = 16384.0 / kMfmaFlopPerClkSimd;
     double lds_need = 4.0 * (FM + FN) * 1024.0 / (FM * FN * mfma_clk);
     double lds_factor = lds_need > kLdsBytesPerClkCu ? lds_need / kLdsBytesPerClkCu : 1.0;
-    return per_cu * (double)c.BM * c.BN * g.K * lds_factor;
+    // Two K-groups (two waves per SIMD) overlap fragment reads with MFMAs:
+    // 12-14% faster on the 3x3 and 7x7 layers measured on MI355X.
+    double overlap = c.WK == 2 ? 0.88 : 1.0;
+    return per_cu * (double)c.BM * c.BN * g.K * lds_factor * overlap;
 }
 
 int choose_igemm_dma_cfg(const ConvGeom& g) {
@@ -203,6 +207,7 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
     p.unfused = unfused;
     p.forced = base != TG_KERNEL_AUTO;
     p.dma_cfg = -1;
+    p.patch_cfg = -1;
     p.kernel = p.forced ? base : (int)dispatch(g, dtype, table);
     if (p.kernel == TG_KERNEL_IGEMM) {
         if (!igemm_serves(g, dtype)) return TG_ERR_UNSUPPORTED;
@@ -226,6 +231,12 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
                 p.cu_waves = igemm_cu_waves(g, env_int("TG_CU", 3));
                 p.cu_pd = env_int("TG_CU_PD", 2);
             }
+        } else if (igemm_patch_serves(g) && env_int("TG_IGEMM_PATCH", 1) != 0 &&
+                   env_int("TG_IGEMM_CFG", -1) < 0) {
+            // TG_PATCH_CFG forces a tile (if it fits this shape's LDS need).
+            p.igemm_cfg = 0;
+            int forced = env_int("TG_PATCH_CFG", -1);
+            p.patch_cfg = igemm_patch_fits(g, forced) ? forced : igemm_patch_choose(g);
         } else if (igemm_dma_serves(g) && env_int("TG_IGEMM_DMA", 1) != 0 &&
                    env_int("TG_IGEMM_CFG", -1) < 0) {
             p.igemm_cfg = 0;
@@ -314,6 +325,9 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, c
             else if (plan->igemm_cfg < 0 && env_int("TG_STREAM", 0) > 0)
                 e = launch_igemm_stream(g, env_int("TG_STREAM", 16), plan->rw_nt, identity, x, w,
                                         bn_scale, bn_bias, conv_out, s);
+            else if (plan->patch_cfg >= 0)
+                e = launch_igemm_patch(g, plan->patch_cfg, identity, x, w, bn_scale, bn_bias,
+                                       conv_out, s);
             else if (plan->dma_cfg >= 0)
                 e = launch_igemm_dma(g, plan->dma_cfg, identity, x, w, bn_scale, bn_bias, conv_out,
                                      s);
@@ -383,11 +397,17 @@ tg_status tg_conv_bn_silu_describe(const tg_conv_bn_silu_plan* plan, char* buf, 
     } else if (plan->kernel == TG_KERNEL_IGEMM && plan->igemm_cfg < 0) {
         snprintf(k, sizeof(k), "igemm_rw (weights in VGPRs) nf=%d cs=%d ncw=%d grid=%d%s",
                  plan->rw_nf, plan->rw_cs, plan->rw_ncw, plan->rw_grid, plan->rw_nt ? " nt" : "");
+    } else if (plan->kernel == TG_KERNEL_IGEMM && plan->patch_cfg >= 0) {
+        int BM, BN, WM, WN, WK;
+        igemm_patch_describe(plan->patch_cfg, &BM, &BN, &WM, &WN, &WK);
+        int tiles = g.N * ((g.P * g.Q + BM - 1) / BM) * ((g.C_out + BN - 1) / BN);
+        snprintf(k, sizeof(k), "igemm_patch cfg=%d BM=%d BN=%d waves=%dx%dx%d grid=%d",
+                 plan->patch_cfg, BM, BN, WK, WM, WN, tiles);
     } else if (plan->kernel == TG_KERNEL_IGEMM && plan->dma_cfg >= 0) {
         const IgemmCfg& c = igemm_dma_cfg(plan->dma_cfg);
         int tm = (g.M + c.BM - 1) / c.BM, tn = (g.C_out + c.BN - 1) / c.BN;
-        snprintf(k, sizeof(k), "igemm_dma cfg=%d BM=%d BN=%d BK=64 waves=%dx%d grid=%d",
-                 plan->dma_cfg, c.BM, c.BN, c.WM, c.WN, tm * tn);
+        snprintf(k, sizeof(k), "igemm_dma cfg=%d BM=%d BN=%d BK=64 waves=%dx%dx%d grid=%d",
+                 plan->dma_cfg, c.BM, c.BN, c.WK, c.WM, c.WN, tm * tn);
     } else if (plan->kernel == TG_KERNEL_IGEMM) {
         const IgemmCfg& c = igemm_cfg(plan->igemm_cfg);
         int tm = (g.M + c.BM - 1) / c.BM, tn = (g.C_out + c.BN - 1) / c.BN;

@@ -16,6 +16,11 @@
 //   * A RING-stage ring keeps RING-1 chunks in flight; one workgroup barrier
 //     per chunk. The main loop issues no stores, so waiting for the oldest
 //     chunk's loads is an exact vmcnt wait.
+//   * WK = 2 runs two groups of four waves, each taking one 32-deep half of
+//     every chunk, so each SIMD holds two waves and one wave's fragment reads
+//     overlap the other's MFMAs (with one wave per SIMD the two alternate).
+//     The two partial tiles are summed through LDS before the epilogue; the
+//     sum is over the complete K, as the nonlinear epilogue requires.
 //   * Epilogue: fp32 BatchNorm + SiLU on the accumulators, fp16 cast, then
 //     the tile goes through LDS so each store instruction writes whole
 //     128-byte lines of NHWC rows.
@@ -37,27 +42,35 @@ __device__ __forceinline__ void dma_wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// BM pixels x BN channels per workgroup of 4 waves arranged WM x WN;
-// FM x FN 16x16 blocks per wave; RING LDS stages of one 64-deep chunk.
-template <int BM, int BN, int WM, int WN, int RING>
+// BM pixels x BN channels per workgroup of 4*WK waves: WK groups of 4 waves
+// arranged WM x WN; FM x FN 16x16 blocks per wave; RING LDS stages of one
+// 64-deep chunk.
+template <int BM, int BN, int WM, int WN, int RING, int WK>
 struct DmaShape {
-    static_assert(WM * WN == 4, "four waves");
+    static_assert(WM * WN == 4, "four waves per K-group");
+    static_assert(WK == 1 || WK == 2, "one or two K-groups");
     static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tiles of 16x16 blocks");
     static_assert(BM % 16 == 0 && BN % 16 == 0, "16-row swizzle groups");
+    static constexpr int NW = 4 * WK;                // waves per workgroup
     static constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
     static constexpr int XI = BM / 8, WI = BN / 8;   // load instructions per chunk
-    static constexpr int LI = (XI + WI + 3) / 4;     // per wave (padded with repeats)
+    static constexpr int LI = (XI + WI + NW - 1) / NW;  // per wave (padded with repeats)
     static constexpr int STAGE = (BM + BN) * 64;     // halves per stage
     static constexpr int OROW = BN + 8;              // output tile row (halves)
-    static constexpr int SMEM = RING * STAGE > BM * OROW ? RING * STAGE : BM * OROW;
+    // K-group 1's partial accumulators (fp32, lane-major per 16x16 block),
+    // then the output tile; both overlay the ring after the main loop.
+    static constexpr int RED = WK == 2 ? 4 * FN * FM * 64 * 4 * 2 : 0;  // halves
+    static constexpr int OUT_AT = RED;
+    static constexpr int EPI_SMEM = RED + BM * OROW;
+    static constexpr int SMEM = RING * STAGE > EPI_SMEM ? RING * STAGE : EPI_SMEM;
     static_assert(LI * (RING - 1) <= 63, "vmcnt range");
 };
 
-template <int BM, int BN, int WM, int WN, int RING, int EPI>
-__global__ __launch_bounds__(256, 1) void conv2d_bn_silu_igemm_dma(
+template <int BM, int BN, int WM, int WN, int RING, int WK, int EPI>
+__global__ __launch_bounds__(256 * WK, 1) void conv2d_bn_silu_igemm_dma(
     const f16* __restrict__ x, const f16* __restrict__ w, const float* __restrict__ scale,
     const float* __restrict__ bias, f16* __restrict__ y, ConvGeom g, int tiles_m, int tiles_n) {
-    using S = DmaShape<BM, BN, WM, WN, RING>;
+    using S = DmaShape<BM, BN, WM, WN, RING, WK>;
     extern __shared__ __attribute__((aligned(16))) f16 dma_smem[];
 
     const int tile = xcd_contiguous_tile(blockIdx.x, tiles_m * tiles_n);
@@ -67,7 +80,8 @@ __global__ __launch_bounds__(256, 1) void conv2d_bn_silu_igemm_dma(
     // Wave-uniform by construction; readfirstlane lets the compiler keep the
     // load-assignment choices below (buffer and LDS destination) scalar.
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int wm = wave / WN, wn = wave - (wave / WN) * WN;
+    const int kg = wave >> 2, w4 = wave & 3;  // K-group, wave within it
+    const int wm = w4 / WN, wn = w4 - (w4 / WN) * WN;
     const int lr = lane & 15, lg = lane >> 4;
     const int PQ = g.P * g.Q;
     const int cchunks = g.C_in / 64;          // chunks per filter tap
@@ -82,7 +96,7 @@ __global__ __launch_bounds__(256, 1) void conv2d_bn_silu_igemm_dma(
     // Load assignment: instruction j (of XI x-instructions then WI
     // w-instructions) covers rows 8*(j')..8*(j')+7; lane l takes row
     // 8*j' + l/8 and piece (l%8) ^ ((row % 16) >> 1), written to slot l%8.
-    // Each wave issues LI instructions j = wave + 4*i (clamped: repeats of
+    // Each wave issues LI instructions j = wave + NW*i (clamped: repeats of
     // the last instruction write identical data to the same place).
     const int prow = lane >> 3, pslot = lane & 7;
     int base_x[S::LI], h0[S::LI], w0[S::LI], piece[S::LI];
@@ -90,7 +104,7 @@ __global__ __launch_bounds__(256, 1) void conv2d_bn_silu_igemm_dma(
     int srow0[S::LI];   // wave-uniform: first stage row of the instruction
 #pragma unroll
     for (int i = 0; i < S::LI; ++i) {
-        int j = wave + 4 * i;
+        int j = wave + S::NW * i;
         if (j > S::XI + S::WI - 1) j = S::XI + S::WI - 1;
         const bool isx = j < S::XI;
         const int row0 = (isx ? j : j - S::XI) * 8;         // first tile row (uniform)
@@ -168,7 +182,8 @@ __global__ __launch_bounds__(256, 1) void conv2d_bn_silu_igemm_dma(
         if (issued < nk) issue(issued++);
         const f16* st = dma_smem + (kc % RING) * S::STAGE;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+        for (int kk = 0; kk < 2 / WK; ++kk) {
+            const int ks = WK == 2 ? kg : kk;  // 32-deep half of the chunk
             const int pc = ks * 4 + lg;  // 16-byte piece of the 128-byte chunk row
             half8_t a[S::FN], b[S::FM];
 #pragma unroll
@@ -190,8 +205,27 @@ __global__ __launch_bounds__(256, 1) void conv2d_bn_silu_igemm_dma(
     }
     dma_barrier();  // all waves done with the ring: reuse it for the output tile
 
+    if (WK == 2) {
+        // Sum the two K-groups' partial tiles: group 1 parks its accumulators
+        // in LDS (each lane 16 contiguous bytes per block), group 0 adds them.
+        float4_t* red = (float4_t*)dma_smem + w4 * S::FN * S::FM * 64 + lane;
+        if (kg == 1) {
+#pragma unroll
+            for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+                for (int j = 0; j < S::FM; ++j) red[(i * S::FM + j) * 64] = acc[i][j];
+        }
+        dma_barrier();
+        if (kg == 1) goto store_phase;
+#pragma unroll
+        for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+            for (int j = 0; j < S::FM; ++j) acc[i][j] += red[(i * S::FM + j) * 64];
+    }
+
+    {
     // Epilogue: lane holds channels cb..cb+3 of pixel pr for each block.
-    f16* out = dma_smem;
+    f16* out = dma_smem + S::OUT_AT;
 #pragma unroll
     for (int i = 0; i < S::FN; ++i) {
         const int cb = wn * S::FN * 16 + i * 16 + lg * 4;
@@ -209,36 +243,46 @@ __global__ __launch_bounds__(256, 1) void conv2d_bn_silu_igemm_dma(
             *(half4_t*)(out + pr * S::OROW + cb) = h;
         }
     }
-    dma_barrier();
+    }
 
+store_phase:
+    dma_barrier();
+    {
+    const f16* out = dma_smem + S::OUT_AT;
     constexpr int CV = BN / 8;  // 16-byte pieces per tile row
     if ((g.C_out & 7) == 0) {
-        for (int v = threadIdx.x; v < BM * CV; v += 256) {
+        for (int v = threadIdx.x; v < BM * CV; v += 64 * S::NW) {
             const int row = v / CV, cv = v - (v / CV) * CV;
             const int m = m0 + row, o = n0 + cv * 8;
             if (m < g.M && o < g.C_out)
                 *(half8_t*)(y + m * g.C_out + o) = *(const half8_t*)(out + row * S::OROW + cv * 8);
         }
     } else {
-        for (int v = threadIdx.x; v < BM * BN; v += 256) {
+        for (int v = threadIdx.x; v < BM * BN; v += 64 * S::NW) {
             const int row = v / BN, cc = v - (v / BN) * BN;
             const int m = m0 + row, o = n0 + cc;
             if (m < g.M && o < g.C_out) y[m * g.C_out + o] = out[row * S::OROW + cc];
         }
     }
+    }
 }
 
 // ---- variants ------------------------------------------------------------
-#define TG_DMA_CFGS(X)        \
-    X(128, 128, 2, 2, 4)      \
-    X(112, 128, 1, 4, 4)      \
-    X(208, 64, 1, 4, 4)       \
-    X(224, 64, 2, 2, 4)       \
-    X(128, 64, 2, 2, 4)       \
-    X(64, 64, 2, 2, 4)
+#define TG_DMA_CFGS(X)           \
+    X(128, 128, 2, 2, 4, 1)      \
+    X(112, 128, 1, 4, 4, 1)      \
+    X(208, 64, 1, 4, 4, 1)       \
+    X(224, 64, 2, 2, 4, 1)       \
+    X(128, 64, 2, 2, 4, 1)       \
+    X(64, 64, 2, 2, 4, 1)        \
+    X(128, 128, 2, 2, 4, 2)      \
+    X(112, 128, 1, 4, 4, 2)      \
+    X(208, 64, 1, 4, 4, 2)       \
+    X(224, 64, 2, 2, 4, 2)       \
+    X(128, 64, 2, 2, 4, 2)
 
 static const IgemmCfg kDmaCfgs[] = {
-#define X(bm, bn, wm, wn, ring) {bm, bn, 64, wm, wn},
+#define X(bm, bn, wm, wn, ring, wk) {bm, bn, 64, wm, wn, wk},
     TG_DMA_CFGS(X)
 #undef X
 };
@@ -251,14 +295,15 @@ bool igemm_dma_serves(const ConvGeom& g) {
     return g.C_in % 64 == 0 && xbytes < (1LL << 31) && wbytes < (1LL << 31);
 }
 
-template <int BM, int BN, int WM, int WN, int RING>
+template <int BM, int BN, int WM, int WN, int RING, int WK>
 static hipError_t dma_launch_one(const ConvGeom& g, bool identity, const void* x, const void* w,
                                  const float* scale, const float* bias, void* y, hipStream_t s) {
-    using S = DmaShape<BM, BN, WM, WN, RING>;
+    using S = DmaShape<BM, BN, WM, WN, RING, WK>;
     const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.C_out + BN - 1) / BN;
     const size_t lds = (size_t)S::SMEM * 2;
-    auto k = identity ? conv2d_bn_silu_igemm_dma<BM, BN, WM, WN, RING, EPI_IDENTITY>
-                      : conv2d_bn_silu_igemm_dma<BM, BN, WM, WN, RING, EPI_FUSED>;
+    static_assert(S::SMEM * 2 <= 160 * 1024, "LDS budget");
+    auto k = identity ? conv2d_bn_silu_igemm_dma<BM, BN, WM, WN, RING, WK, EPI_IDENTITY>
+                      : conv2d_bn_silu_igemm_dma<BM, BN, WM, WN, RING, WK, EPI_FUSED>;
     static bool attr_set[2] = {false, false};
     if (!attr_set[identity ? 1 : 0]) {
         hipError_t e = hipFuncSetAttribute((const void*)k,
@@ -266,7 +311,8 @@ static hipError_t dma_launch_one(const ConvGeom& g, bool identity, const void* x
         if (e != hipSuccess) return e;
         attr_set[identity ? 1 : 0] = true;
     }
-    hipLaunchKernelGGL(k, dim3(tiles_m * tiles_n), dim3(256), lds, s, (const f16*)x, (const f16*)w,
+    hipLaunchKernelGGL(k, dim3(tiles_m * tiles_n), dim3(64 * S::NW), lds, s, (const f16*)x,
+                       (const f16*)w,
                        scale, bias, (f16*)y, g, tiles_m, tiles_n);
     return hipGetLastError();
 }
@@ -275,9 +321,9 @@ hipError_t launch_igemm_dma(const ConvGeom& g, int cfg, bool identity, const voi
                             const void* w, const float* scale, const float* bias, void* y,
                             hipStream_t s) {
     int i = 0;
-#define X(bm, bn, wm, wn, ring)                                                         \
-    if (cfg == i) return dma_launch_one<bm, bn, wm, wn, ring>(g, identity, x, w, scale, \
-                                                              bias, y, s);              \
+#define X(bm, bn, wm, wn, ring, wk)                                                         \
+    if (cfg == i) return dma_launch_one<bm, bn, wm, wn, ring, wk>(g, identity, x, w, scale, \
+                                                                  bias, y, s);              \
     ++i;
     TG_DMA_CFGS(X)
 #undef X

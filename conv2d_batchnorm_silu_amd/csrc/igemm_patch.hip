@@ -1,0 +1,498 @@
+// igemm_patch.hip -- conv2d_bn_silu_igemm for stride-1 convolutions with
+// C_in % 64 == 0 (the 3x3 and 7x7 layers): the input patch of a tile is
+// staged in LDS once and serves every filter tap.
+//
+// Same operation as igemm.hip ("Fusing an Epilogue", teenygrad docs, "The
+// shape of it": the K-loop on the matrix cores leaves the output tile in
+// registers, BatchNorm scale/shift and SiLU are applied there, then one
+// store). The implicit-GEMM formulation reads an input pixel once per filter
+// tap (9 or 49 times); here a workgroup's tile is BM consecutive output
+// pixels of one image, and the input rows they touch -- all C_in channels,
+// zero-padded at the image border -- are copied into LDS once:
+//   * patch pixel stride is C_in*2 + 32 bytes (2 mod 4 16-byte units), which
+//     measured conflict-free on gfx950 for 16 consecutive pixels read at one
+//     channel piece -- no swizzle that would depend on the tap's shift (the
+//     denser C_in*2 + 16 costs 2-way conflicts and is the fallback when LDS
+//     is short). When LDS allows, patch rows are padded to Q + 16 pixels: a
+//     fragment whose 16 pixels wrap to the next output row then jumps by 16
+//     pixels, which keeps the same bank groups;
+//   * for tap (r, s) a lane's fragment address is its tap-(0,0) address plus
+//     a wave-uniform (r*PW + s)*stride: one add per fragment and tap;
+//   * only the filter chunks stream (64 channels of one tap). Each wave
+//     fetches the rows and the half (or whole) 128-byte chunk row its own
+//     fragments need into a wave-private 4-stage ring with direct-to-LDS
+//     loads (rows XOR-swizzled), so the main loop has no workgroup barrier:
+//     a wave waits only for its own loads, with an exact vmcnt; per-lane
+//     offsets are precomputed so that a chunk costs one add per load;
+//   * WK = 2 runs two groups of four waves on the two 32-deep halves of every
+//     chunk (two waves per SIMD: one's fragment reads overlap the other's
+//     MFMAs); their partial tiles are summed through LDS before the epilogue,
+//     so the epilogue sees the complete K sum.
+#include "tg_device.hpp"
+#include "tg_internal.hpp"
+
+namespace tg {
+namespace {
+
+__device__ __forceinline__ void pt_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void pt_wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ u32x4_t pt_rsrc(const void* base, unsigned bytes) {
+    const unsigned long long a = (unsigned long long)base;
+    u32x4_t r;
+    r[0] = (unsigned)a;
+    r[1] = (unsigned)(a >> 32) & 0xffffu;
+    r[2] = bytes;
+    r[3] = 0x00020000u;
+    return r;
+}
+
+// 16-byte direct-to-LDS load (lane l -> lds + 16*l; offsets past num_records
+// read zeros); ordered by the caller's explicit vmcnt waits.
+__device__ __forceinline__ void pt_dma16(u32x4_t rsrc, unsigned voff, unsigned lds) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(lds)
+                 : "memory");
+}
+
+constexpr int kPatchRing = 4;
+
+template <int BM, int BN, int WM, int WN, int WK>
+struct PatchShape {
+    static constexpr int WPG = WM * WN;                // waves per K-group
+    static_assert(WPG == 2 || WPG == 4, "two or four waves per K-group");
+    static_assert(WK == 1 || WK == 2, "one or two K-groups");
+    static_assert(BM % (16 * WM) == 0 && BN % (16 * WN) == 0, "wave tiles of 16x16 blocks");
+    static constexpr int NW = WPG * WK;
+    static constexpr int FM = BM / WM / 16, FN = BN / WN / 16;
+    static constexpr int PPR = 8 / WK;                 // 16-byte pieces of a wave's chunk row
+    static constexpr int LI = FN * 16 * PPR / 64;      // filter loads per chunk per wave
+    static_assert(FN * 16 * PPR % 64 == 0, "whole load instructions");
+    static constexpr int WSTAGE = FN * 16 * PPR * 16;  // bytes per stage of a wave's ring
+    static constexpr int RING_BYTES = NW * kPatchRing * WSTAGE;
+    static constexpr int OROW = BN + 8;                // output tile row (halves)
+    static constexpr int RED_BYTES = WK == 2 ? WPG * FN * FM * 64 * 16 : 0;
+    static constexpr int EPI_BYTES = RED_BYTES + BM * OROW * 2;
+    static_assert(LI * kPatchRing <= 63, "vmcnt range");
+};
+
+// Slot of piece p in row r of a wave's filter stage is p ^ pt_wswz<WK>(r):
+// (r/2)%4 for 64-byte rows (WK = 2) and (r/2)%8 for 128-byte rows; both
+// measured conflict-free on gfx950 for 16 rows x one piece per lane group.
+template <int WK>
+__device__ __forceinline__ int pt_wswz(int r) {
+    return WK == 2 ? (r >> 1) & 3 : (r >> 1) & 7;
+}
+
+template <int BM, int BN, int WM, int WN, int WK, int EPI>
+__global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_patch(
+    const f16* __restrict__ x, const f16* __restrict__ w, const float* __restrict__ scale,
+    const float* __restrict__ bias, f16* __restrict__ y, ConvGeom g, int tiles_per_img,
+    int tiles_n, int PW, int pstride) {
+    using S = PatchShape<BM, BN, WM, WN, WK>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char pt_smem[];
+
+    const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
+    const int tn = tile % tiles_n, tmi = tile / tiles_n;
+    const int n = tmi / tiles_per_img, t = tmi - n * tiles_per_img;
+    const int PQ = g.P * g.Q;
+    const int r0 = t * BM;                              // first output pixel in the image
+    const int r1 = r0 + BM < PQ ? r0 + BM : PQ;         // one past the last valid one
+    const int p_first = r0 / g.Q, p_last = (r1 - 1) / g.Q;
+    const int PR = p_last - p_first + g.kh;             // patch rows
+    // PW: patch columns, Q + kw - 1 or (padded) Q + 16; columns past
+    // Q + kw - 2 are never read. pstride: bytes per patch pixel, C_in*2 + 32
+    // (conflict-free) or, when that does not fit, C_in*2 + 16.
+    const int n0 = tn * BN;
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int kg = wave / S::WPG, w4 = wave - kg * S::WPG;  // K-group, wave within it
+    const int wm = w4 / WN, wn = w4 - (w4 / WN) * WN;
+    const int lr = lane & 15, lg = lane >> 4;
+    const int cchunks = g.C_in / 64;
+    const int nk = g.kh * g.kw * cchunks;
+
+    unsigned char* ring = pt_smem + wave * kPatchRing * S::WSTAGE;  // this wave's ring
+    unsigned char* patch = pt_smem + S::RING_BYTES;
+    const unsigned ring_lds = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)ring));
+
+    // Filter chunk loads: this wave needs rows wn*FN*16 .. +FN*16 of the
+    // BN-row tile and pieces kg*PPR .. +PPR of each 128-byte chunk row.
+    // Instruction i moves 64/PPR rows; lane l takes row i*64/PPR + l/PPR,
+    // piece (l%PPR) ^ pt_wswz(row) -> slot l%PPR.
+    const u32x4_t wrs = pt_rsrc(w, (unsigned)g.C_out * (unsigned)g.K * 2u);
+    unsigned woff[S::LI];
+#pragma unroll
+    for (int i = 0; i < S::LI; ++i) {
+        const int row = i * (64 / S::PPR) + lane / S::PPR;
+        const int piece = (lane % S::PPR) ^ pt_wswz<WK>(row);
+        const int o = n0 + wn * S::FN * 16 + row;
+        const int kp = (WK == 2 ? kg * S::PPR : 0) + piece;
+        woff[i] = o < g.C_out ? (unsigned)((o * g.K + kp * 8) * 2) : 0x80000000u;
+    }
+    auto issue = [&](int kc) {
+        const int tap = kc / cchunks, cc = kc - tap * cchunks;
+        const unsigned koff = (unsigned)((tap * g.C_in + cc * 64) * 2);
+        const unsigned dst = ring_lds + (unsigned)(kc % kPatchRing) * S::WSTAGE;
+#pragma unroll
+        for (int i = 0; i < S::LI; ++i) pt_dma16(wrs, woff[i] + koff, dst + i * 1024);
+    };
+    int issued = 0;
+    for (; issued < kPatchRing - 1 && issued < nk; ++issued) issue(issued);
+
+    // Input patch: PR x PW pixels x C_in channels, zeros outside the image.
+    // Thread u copies 16-byte piece (u % upp) of pixels u/upp, u/upp + step,
+    // ... (64*NW is a multiple of upp = C_in/8, so the piece is fixed).
+    {
+        const int upp = g.C_in / 8;
+        const int npx = PR * PW;
+        const int step = 64 * S::NW / upp;
+        const int piece = threadIdx.x % upp;
+        int px = threadIdx.x / upp;
+        int pr = px / PW, pc = px - (px / PW) * PW;
+        const int step_r = step / PW, step_c = step - step_r * PW;
+        const f16* xn = x + (size_t)n * g.H * g.W * g.C_in + piece * 8;
+        const half8_t zero8 = {0, 0, 0, 0, 0, 0, 0, 0};
+        constexpr int B = 8;  // loads in flight per thread
+        while (px < npx) {
+            half8_t v[B];
+            int dst[B];
+#pragma unroll
+            for (int b = 0; b < B; ++b) {
+                const int ih = p_first - g.pad + pr, iw = pc - g.pad;
+                const bool ok = px < npx && (unsigned)ih < (unsigned)g.H &&
+                                (unsigned)iw < (unsigned)g.W;
+                v[b] = ok ? *(const half8_t*)(xn + (ih * g.W + iw) * g.C_in) : zero8;
+                dst[b] = px < npx ? px * pstride + piece * 16 : -1;
+                px += step;
+                pr += step_r;
+                pc += step_c;
+                if (pc >= PW) { pc -= PW; ++pr; }
+            }
+#pragma unroll
+            for (int b = 0; b < B; ++b)
+                if (dst[b] >= 0) *(half8_t*)(patch + dst[b]) = v[b];
+        }
+    }
+
+    // Fragment addresses for tap (0, 0), channel piece lg: x operand (pixels)
+    // from the patch, weight operand from the ring stage (ks = 1 is ks = 0
+    // with slot bit 2 flipped, i.e. byte offset ^ 64).
+    int abase[S::FM];
+#pragma unroll
+    for (int f = 0; f < S::FM; ++f) {
+        int r = r0 + (wm * S::FM + f) * 16 + lr;
+        if (r > r1 - 1) r = r1 - 1;  // beyond the tile: any valid pixel, result unused
+        const int p = r / g.Q, q = r - (r / g.Q) * g.Q;
+        abase[f] = ((p - p_first) * PW + q) * pstride + lg * 16;
+    }
+    int bbase[S::FN];  // piece lg (ks = 0) of row f*16 + lr; ks = 1 (WK = 1): ^ 64
+#pragma unroll
+    for (int f = 0; f < S::FN; ++f) {
+        const int row = f * 16 + lr;
+        bbase[f] = row * S::PPR * 16 + ((lg ^ pt_wswz<WK>(row)) * 16);
+    }
+    pt_barrier();  // the patch is complete
+
+    float4_t acc[S::FN][S::FM];
+#pragma unroll
+    for (int a = 0; a < S::FN; ++a)
+#pragma unroll
+        for (int b = 0; b < S::FM; ++b) acc[a][b] = (float4_t){0.f, 0.f, 0.f, 0.f};
+
+    // Fragments of chunk kc for this wave's 32-deep step(s): registers are
+    // double-buffered so that chunk kc+1's fragment reads overlap chunk kc's
+    // MFMAs (software pipelining across chunks).
+    constexpr int KSW = 2 / WK;  // 32-deep steps per chunk for this wave
+    struct Frags {
+        half8_t a[KSW][S::FN], b[KSW][S::FM];
+    };
+    // Chunk kc's filter data: this wave's loads are done when at most the
+    // (issued - kc - 1) later chunks' loads are pending.
+    auto wait_chunk = [&](int kc) {
+        switch (issued - kc - 1) {
+            case 0: pt_wait_vmcnt<0>(); break;
+            case 1: pt_wait_vmcnt<S::LI>(); break;
+            case 2: pt_wait_vmcnt<2 * S::LI>(); break;
+            default: pt_wait_vmcnt<3 * S::LI>(); break;
+        }
+    };
+    auto load = [&](int kc, int tr, int ts, int c, Frags& F) {
+        const unsigned char* st = ring + (kc % kPatchRing) * S::WSTAGE;
+        const int delta = (tr * PW + ts) * pstride + c * 128;
+#pragma unroll
+        for (int kk = 0; kk < KSW; ++kk) {
+            const int ks = WK == 2 ? kg : kk;
+#pragma unroll
+            for (int f = 0; f < S::FN; ++f)
+                F.a[kk][f] = *(const half8_t*)(st + (bbase[f] ^ (WK == 2 ? 0 : ks * 64)));
+#pragma unroll
+            for (int f = 0; f < S::FM; ++f)
+                F.b[kk][f] = *(const half8_t*)(patch + abase[f] + delta + ks * 64);
+        }
+    };
+    auto mma = [&](const Frags& F) {
+#pragma unroll
+        for (int kk = 0; kk < KSW; ++kk)
+#pragma unroll
+            for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+                for (int j = 0; j < S::FM; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(F.a[kk][i], F.b[kk][j],
+                                                                       acc[i][j], 0, 0, 0);
+    };
+    // (tap_r, tap_s, cc) of the chunk whose fragments are loaded next.
+    int tap_r = 0, tap_s = 0, cc = 0;
+    auto advance = [&]() {
+        if (++cc == cchunks) {
+            cc = 0;
+            if (++tap_s == g.kw) { tap_s = 0; ++tap_r; }
+        }
+    };
+    Frags F0, F1;
+    wait_chunk(0);
+    load(0, tap_r, tap_s, cc, F0);
+    advance();
+    // One step: refill the ring, fetch chunk kc+1's fragments into `nxt`,
+    // then run chunk kc's MFMAs from `cur`. Stage (kc + 3) % 4 was last read
+    // for chunk kc - 1, whose fragments are in registers by now.
+    auto step = [&](int kc, const Frags& cur, Frags& nxt) {
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (issued < nk) issue(issued++);
+        if (kc + 1 < nk) {
+            wait_chunk(kc + 1);
+            load(kc + 1, tap_r, tap_s, cc, nxt);
+            advance();
+        }
+        mma(cur);
+    };
+    for (int kc = 0; kc < nk; kc += 2) {
+        step(kc, F0, F1);
+        if (kc + 1 < nk) step(kc + 1, F1, F0);
+    }
+    pt_barrier();  // every wave is done with its ring and the patch: reuse LDS
+
+    if (WK == 2) {
+        float4_t* red = (float4_t*)pt_smem + w4 * S::FN * S::FM * 64 + lane;
+        if (kg == 1) {
+#pragma unroll
+            for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+                for (int j = 0; j < S::FM; ++j) red[(i * S::FM + j) * 64] = acc[i][j];
+        }
+        pt_barrier();
+        if (kg == 1) goto store_phase;
+#pragma unroll
+        for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+            for (int j = 0; j < S::FM; ++j) acc[i][j] += red[(i * S::FM + j) * 64];
+    }
+
+    {
+        // Lane holds channels cb..cb+3 of tile pixel pr for each block.
+        f16* out = (f16*)(pt_smem + S::RED_BYTES);
+#pragma unroll
+        for (int i = 0; i < S::FN; ++i) {
+            const int cb = wn * S::FN * 16 + i * 16 + lg * 4;
+            float sc[4], bi[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) epi_consts<EPI>(scale, bias, n0 + cb + e, g.C_out, sc[e], bi[e]);
+#pragma unroll
+            for (int j = 0; j < S::FM; ++j) {
+                const int pr = wm * S::FM * 16 + j * 16 + lr;
+                half4_t h;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h[e] = (f16)epilogue<EPI>(acc[i][j][e], sc[e], bi[e]);
+                *(half4_t*)(out + pr * S::OROW + cb) = h;
+            }
+        }
+    }
+
+store_phase:
+    pt_barrier();
+    {
+        const f16* out = (const f16*)(pt_smem + S::RED_BYTES);
+        const int rows = r1 - r0;
+        f16* yt = y + ((size_t)n * PQ + r0) * g.C_out;
+        constexpr int CV = BN / 8;
+        if ((g.C_out & 7) == 0) {
+            for (int v = threadIdx.x; v < BM * CV; v += 64 * S::NW) {
+                const int row = v / CV, cv = v - (v / CV) * CV;
+                const int o = n0 + cv * 8;
+                if (row < rows && o < g.C_out)
+                    *(half8_t*)(yt + row * g.C_out + o) = *(const half8_t*)(out + row * S::OROW + cv * 8);
+            }
+        } else {
+            for (int v = threadIdx.x; v < BM * BN; v += 64 * S::NW) {
+                const int row = v / BN, c = v - (v / BN) * BN;
+                const int o = n0 + c;
+                if (row < rows && o < g.C_out) yt[row * g.C_out + o] = out[row * S::OROW + c];
+            }
+        }
+    }
+}
+
+#define TG_PATCH_CFGS(X)        \
+    X(112, 128, 1, 2, 2)        \
+    X(224, 64, 2, 1, 2)         \
+    X(112, 128, 1, 4, 2)        \
+    X(224, 64, 2, 2, 2)         \
+    X(128, 64, 2, 2, 2)         \
+    X(64, 64, 2, 2, 2)          \
+    X(112, 128, 1, 4, 1)        \
+    X(224, 64, 2, 2, 1)
+
+struct PatchCfg {
+    int BM, BN, WM, WN, WK;
+};
+const PatchCfg kPatchCfgs[] = {
+#define X(bm, bn, wm, wn, wk) {bm, bn, wm, wn, wk},
+    TG_PATCH_CFGS(X)
+#undef X
+};
+constexpr int kNumPatchCfgs = (int)(sizeof(kPatchCfgs) / sizeof(kPatchCfgs[0]));
+
+// Rows of output pixels a BM-pixel tile can touch (tiles start at multiples
+// of BM within an image).
+int patch_rows_max(const ConvGeom& g, int BM) {
+    const int PQ = g.P * g.Q;
+    int worst = 0;
+    for (int r0 = 0; r0 < PQ; r0 += BM) {  // exact over the tiles of one image
+        const int r1 = r0 + BM < PQ ? r0 + BM : PQ;
+        const int rows = (r1 - 1) / g.Q - r0 / g.Q + 1;
+        if (rows > worst) worst = rows;
+    }
+    return worst;
+}
+
+size_t patch_lds_bytes_w(const ConvGeom& g, const PatchCfg& c, int pw, int pstride) {
+    // Wave-private rings: WM*WN*WK waves x 4 stages x (BN/WN rows x 128/WK bytes).
+    const size_t ring = (size_t)c.WM * c.WN * c.WK * kPatchRing * (c.BN / c.WN) * (128 / c.WK);
+    const size_t pr = (size_t)patch_rows_max(g, c.BM) + g.kh - 1;
+    const size_t patch = pr * (size_t)pw * (size_t)pstride;
+    const size_t red =
+        c.WK == 2 ? (size_t)c.WM * c.WN * (c.BN / c.WN / 16) * (c.BM / c.WM / 16) * 64 * 16 : 0;
+    const size_t epi = red + (size_t)c.BM * (c.BN + 8) * 2;
+    return ring + patch > epi ? ring + patch : epi;
+}
+
+// Patch layout, best first: padded rows with the conflict-free stride, plain
+// rows with it, plain rows with the dense stride.
+struct PatchLayout {
+    int pw, pstride;
+};
+PatchLayout patch_layout(const ConvGeom& g, const PatchCfg& c) {
+    const int plain = g.Q + g.kw - 1, padded = g.Q + 16;
+    const int wide = g.C_in * 2 + 32, dense = g.C_in * 2 + 16;
+    if (g.kw <= 17 && padded > plain && patch_lds_bytes_w(g, c, padded, wide) <= 160 * 1024)
+        return {padded, wide};
+    if (patch_lds_bytes_w(g, c, plain, wide) <= 160 * 1024) return {plain, wide};
+    return {plain, dense};
+}
+
+size_t patch_lds_bytes(const ConvGeom& g, const PatchCfg& c) {
+    const PatchLayout L = patch_layout(g, c);
+    return patch_lds_bytes_w(g, c, L.pw, L.pstride);
+}
+
+template <int BM, int BN, int WM, int WN, int WK>
+hipError_t patch_launch_one(const ConvGeom& g, bool identity, const void* x, const void* w,
+                            const float* scale, const float* bias, void* y, hipStream_t s) {
+    using S = PatchShape<BM, BN, WM, WN, WK>;
+    const PatchCfg c = {BM, BN, WM, WN, WK};
+    const size_t lds = patch_lds_bytes(g, c);
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    const int tiles_per_img = (g.P * g.Q + BM - 1) / BM, tiles_n = (g.C_out + BN - 1) / BN;
+    auto k = identity ? conv2d_bn_silu_igemm_patch<BM, BN, WM, WN, WK, EPI_IDENTITY>
+                      : conv2d_bn_silu_igemm_patch<BM, BN, WM, WN, WK, EPI_FUSED>;
+    static size_t attr_bytes[2] = {0, 0};
+    size_t& ab = attr_bytes[identity ? 1 : 0];
+    if (lds > ab) {
+        hipError_t e = hipFuncSetAttribute((const void*)k,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        ab = lds;
+    }
+    hipLaunchKernelGGL(k, dim3(g.N * tiles_per_img * tiles_n), dim3(64 * S::NW), lds, s,
+                       (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, tiles_per_img,
+                       tiles_n, patch_layout(g, c).pw, patch_layout(g, c).pstride);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int igemm_patch_num_cfgs() { return kNumPatchCfgs; }
+
+bool igemm_patch_fits(const ConvGeom& g, int cfg) {
+    if (cfg < 0 || cfg >= kNumPatchCfgs) return false;
+    const PatchCfg& c = kPatchCfgs[cfg];
+    // The patch copy gives each thread one fixed 16-byte channel piece.
+    if ((64 * c.WM * c.WN * c.WK) % (g.C_in / 8) != 0) return false;
+    return patch_lds_bytes(g, c) <= 160 * 1024;
+}
+
+bool igemm_patch_serves(const ConvGeom& g) {
+    const long long xbytes = 2LL * g.N * g.H * g.W * g.C_in, wbytes = 2LL * g.C_out * g.K;
+    if (g.stride != 1 || g.C_in % 64 != 0 || g.C_in > 512 || xbytes >= (1LL << 31) ||
+        wbytes >= (1LL << 31))
+        return false;
+    for (int i = 0; i < kNumPatchCfgs; ++i)
+        if (igemm_patch_fits(g, i)) return true;
+    return false;
+}
+
+// Busiest CU's tile count times the tile's MFMA work, with one K-group
+// penalised for its serialised fragment reads; ties go to the lower index.
+int igemm_patch_choose(const ConvGeom& g) {
+    int best = -1;
+    double best_cost = 1e300;
+    for (int i = 0; i < kNumPatchCfgs; ++i) {
+        if (!igemm_patch_fits(g, i)) continue;
+        const PatchCfg& c = kPatchCfgs[i];
+        const long long tiles = (long long)g.N * ((g.P * g.Q + c.BM - 1) / c.BM) *
+                                ((g.C_out + c.BN - 1) / c.BN);
+        const long long per_cu = (tiles + 255) / 256;
+        // LDS bytes per MFMA of a wave tile: (FM + FN) / (FM * FN).
+        const int fm = c.BM / c.WM / 16, fn = c.BN / c.WN / 16;
+        const double lds = (double)(fm + fn) / (fm * fn);
+        // Two waves per K-group (one per SIMD) expose LDS latency: slower on
+        // MI355X despite the lighter LDS traffic.
+        const double occ = c.WK == 2 && c.WM * c.WN == 4 ? 1.0 : 1.3;
+        double cost = (double)per_cu * c.BM * c.BN * occ * (0.7 + lds);
+        if (cost < best_cost * 0.999) { best = i; best_cost = cost; }
+    }
+    return best;
+}
+
+void igemm_patch_describe(int cfg, int* BM, int* BN, int* WM, int* WN, int* WK) {
+    const PatchCfg& c = kPatchCfgs[cfg];
+    *BM = c.BM; *BN = c.BN; *WM = c.WM; *WN = c.WN; *WK = c.WK;
+}
+
+hipError_t launch_igemm_patch(const ConvGeom& g, int cfg, bool identity, const void* x,
+                              const void* w, const float* scale, const float* bias, void* y,
+                              hipStream_t s) {
+    if (!igemm_patch_fits(g, cfg)) return hipErrorInvalidValue;
+    int i = 0;
+#define X(bm, bn, wm, wn, wk)                                                                  \
+    if (cfg == i) return patch_launch_one<bm, bn, wm, wn, wk>(g, identity, x, w, scale, bias, \
+                                                              y, s);                          \
+    ++i;
+    TG_PATCH_CFGS(X)
+#undef X
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tg

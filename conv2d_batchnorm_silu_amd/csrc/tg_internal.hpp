@@ -21,6 +21,7 @@ struct ConvGeom {
 // WM x WN); the reduction is staged through LDS BK halves at a time.
 struct IgemmCfg {
     int BM, BN, BK, WM, WN;
+    int WK = 1;  // K-groups of 4 waves splitting each chunk (direct-to-LDS variant)
 };
 int igemm_num_cfgs();
 const IgemmCfg& igemm_cfg(int i);
@@ -68,6 +69,16 @@ const IgemmCfg& igemm_dma_cfg(int i);
 hipError_t launch_igemm_dma(const ConvGeom& g, int cfg, bool identity, const void* x,
                             const void* w, const float* scale, const float* bias, void* y,
                             hipStream_t s);
+// Patch-staged implicit GEMM (igemm_patch.hip): stride 1, C_in % 64 == 0,
+// the tile's input patch (all channels) fits LDS next to the filter ring.
+bool igemm_patch_serves(const ConvGeom& g);
+int igemm_patch_num_cfgs();
+bool igemm_patch_fits(const ConvGeom& g, int cfg);
+int igemm_patch_choose(const ConvGeom& g);
+void igemm_patch_describe(int cfg, int* BM, int* BN, int* WM, int* WN, int* WK);
+hipError_t launch_igemm_patch(const ConvGeom& g, int cfg, bool identity, const void* x,
+                              const void* w, const float* scale, const float* bias, void* y,
+                              hipStream_t s);
 // Tiled direct conv on MFMA (tiled_mfma.hip): K <= 32, C_out <= 32.
 bool tiled_mfma_serves(const ConvGeom& g);
 int tiled_mfma_rows(const ConvGeom& g);

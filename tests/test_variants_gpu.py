@@ -10,8 +10,11 @@ when a plan is created) and checked against the fp64 oracle:
   * the register-weights kernel's non-default splits and plain stores;
   * the band-staged MFMA kernel without its persistent pipeline
     (TG_TM_PIPE=0), and the VALU tiled kernel (TG_TILED_MFMA=0);
-  * the classic implicit GEMM (TG_IGEMM_RW=0, TG_IGEMM_DMA=0) and the
-    direct-to-LDS one (TG_IGEMM_RW=0).
+  * the patch-staged implicit GEMM for stride-1 layers with C_in % 64 == 0
+    in every tile configuration (TG_PATCH_CFG), including partial channel
+    tiles, ragged pixel tails and channel counts it declines;
+  * the direct-to-LDS implicit GEMM in every tile configuration
+    (TG_IGEMM_PATCH=0, TG_DMA_CFG) and the classic one (TG_IGEMM_DMA=0).
 """
 import pytest
 
@@ -142,7 +145,45 @@ def test_tiled_variants(monkeypatch, env):
         check_workload(wl, "tiled")
 
 
-@pytest.mark.parametrize("env", [{"TG_IGEMM_RW": "0"}, {"TG_IGEMM_RW": "0", "TG_IGEMM_DMA": "0"}],
+PATCH_SHAPES = [
+    WORKLOADS["conv3x3_c128_k128"].scaled(N=1, H=17, W=15),
+    WORKLOADS["conv7x7_c64_k64"].scaled(N=1, H=13, W=11),
+    Workload("p3x3_c64_k33", 54, 2, 12, 12, 64, 33, 3, 3, 1, 1, "f16"),
+    Workload("p5x5_c256_k96", 55, 1, 9, 10, 256, 96, 5, 5, 1, 2, "f16"),
+    Workload("p3x3_c64_k128_wide", 56, 1, 6, 70, 64, 128, 3, 3, 1, 1, "f16"),
+    Workload("p1x1_pad_c64_k64", 57, 2, 9, 9, 64, 64, 1, 1, 1, 0, "f16"),
+    Workload("p3x3_c192_k64", 58, 1, 8, 8, 192, 64, 3, 3, 1, 1, "f16"),
+]
+
+
+@pytest.mark.parametrize("cfg", [str(i) for i in range(8)])
+def test_patch_kernel(monkeypatch, cfg):
+    monkeypatch.setenv("TG_CU", "0")
+    monkeypatch.setenv("TG_IGEMM_RW", "0")
+    monkeypatch.setenv("TG_PATCH_CFG", cfg)
+    ran = 0
+    for wl in PATCH_SHAPES:
+        d = _plan(wl).describe()
+        note("%s -> %s" % (wl.name, d))
+        ran += "igemm_patch" in d
+        check_workload(wl, "igemm")
+        check_workload(wl, "unfused")
+    assert ran >= 5
+
+
+@pytest.mark.parametrize("cfg", [str(i) for i in range(11)])
+def test_dma_kernel(monkeypatch, cfg):
+    monkeypatch.setenv("TG_CU", "0")
+    monkeypatch.setenv("TG_IGEMM_RW", "0")
+    monkeypatch.setenv("TG_IGEMM_PATCH", "0")
+    monkeypatch.setenv("TG_DMA_CFG", cfg)
+    for wl in PATCH_SHAPES[:4] + [Workload("s2_c64", 59, 1, 15, 13, 64, 80, 3, 3, 2, 1, "f16")]:
+        assert "igemm_dma" in _plan(wl).describe()
+        check_workload(wl, "igemm")
+
+
+@pytest.mark.parametrize("env", [{"TG_IGEMM_RW": "0", "TG_IGEMM_PATCH": "0"},
+                                 {"TG_IGEMM_RW": "0", "TG_IGEMM_PATCH": "0", "TG_IGEMM_DMA": "0"}],
                          ids=["dma", "classic"])
 def test_igemm_variants(monkeypatch, env):
     monkeypatch.setenv("TG_CU", "0")
