@@ -33,6 +33,8 @@ struct tg_conv_bn_silu_plan {
     int cu_waves;    // > 0: one-workgroup-per-CU variant with this many wavefronts
     int cu_pd;       // ... and this input prefetch depth
     int patch_cfg;   // >= 0: patch-staged implicit GEMM with this tile
+    int stem_wpc;    // > 0: stem kernel with this many workgroups per CU
+    int stem_rows;   // ... and bands of this many output rows
     TiledCfg tiled;
     size_t ws_bytes;  // unfused only
 };
@@ -246,6 +248,13 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
         }
     } else if (p.kernel == TG_KERNEL_TILED) {
         if (!tiled_serves(g, dtype, &p.tiled)) return TG_ERR_UNSUPPORTED;
+        // TG_STEM: workgroups per CU of the stem kernel (0 disables it);
+        // TG_STEM_ROWS: output rows per band.
+        if (stem_serves(g) && env_int("TG_STEM", 3) > 0) {
+            p.stem_wpc = env_int("TG_STEM", 3);
+            p.stem_rows = env_int("TG_STEM_ROWS", stem_rows(g));
+            if (!stem_rows_ok(g, p.stem_rows)) p.stem_rows = stem_rows(g);
+        }
         if (tiled_mfma_serves(g) && env_int("TG_TILED_MFMA", 1) != 0) {
             p.tm_rows = env_int("TG_TM_ROWS", tiled_mfma_rows(g));
             if (tiled_mfma_pipe_serves(g) && env_int("TG_TM_PIPE", 1) != 0) {
@@ -339,7 +348,10 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, c
                                  s);
             break;
         case TG_KERNEL_TILED:
-            if (plan->tm_pipe_grid > 0)
+            if (plan->stem_wpc > 0)
+                e = launch_stem(g, plan->stem_wpc, plan->stem_rows, identity, x, w, bn_scale, bn_bias,
+                                conv_out, s);
+            else if (plan->tm_pipe_grid > 0)
                 e = launch_tiled_mfma_pipe(g, plan->tm_rows, plan->tm_pipe_grid, identity, x, w,
                                            bn_scale, bn_bias, conv_out, s);
             else if (plan->tm_rows > 0)
@@ -413,6 +425,9 @@ tg_status tg_conv_bn_silu_describe(const tg_conv_bn_silu_plan* plan, char* buf, 
         int tm = (g.M + c.BM - 1) / c.BM, tn = (g.C_out + c.BN - 1) / c.BN;
         snprintf(k, sizeof(k), "igemm cfg=%d BM=%d BN=%d BK=%d waves=%dx%d grid=%d", plan->igemm_cfg,
                  c.BM, c.BN, c.BK, c.WM, c.WN, tm * tn);
+    } else if (plan->kernel == TG_KERNEL_TILED && plan->stem_wpc > 0) {
+        snprintf(k, sizeof(k), "stem (row bands in LDS, 3 MFMA per 32px x 32ch) wg/CU=%d rows=%d",
+                 plan->stem_wpc, plan->stem_rows);
     } else if (plan->kernel == TG_KERNEL_TILED && plan->tm_pipe_grid > 0) {
         snprintf(k, sizeof(k), "tiled_mfma_pipe R=%d grid=%d", plan->tm_rows,
                  plan->tm_pipe_grid);

@@ -1,0 +1,365 @@
+// stem.hip -- conv2d_bn_silu for the network stem: 3x3 filter, stride 2,
+// padding 1, three input channels (RGB), up to 64 output channels, even
+// image width. HBM-bound (x read once, y written once).
+//
+// Same operation as the other fused kernels ("Fusing an Epilogue", teenygrad
+// docs, "The shape of it": reduction on the matrix cores, BatchNorm + SiLU on
+// the accumulators, one store).
+//
+// K layout. With three channels the three input pixels of one filter row
+// (2q-1, 2q, 2q+1) are nine contiguous halves of an NHWC row. A window that
+// starts one pixel earlier (pixel 2q-2, 12(q-1) bytes into the row) is
+// 4-byte aligned and holds those nine values at halves 3..11 of a 16-half
+// K-slot; the slot's other halves meet zero filter weights. One filter row
+// is one slot, the K of one 32x32x16 MFMA: three MFMAs per 32 pixels and 32
+// output channels (MFMA rows = filter channels, columns = pixels; lane
+// (lc, hl) supplies window half hl of pixel lc).
+//
+// Data flow. A workgroup is one loader wave plus four compute waves and
+// walks bands of R output rows of one image. The loader copies the band's
+// 2R+1 input rows (those inside the image: a contiguous byte range of x) into
+// LDS with direct-to-LDS loads of whole aligned 16-byte pieces, starting at
+// the range's first byte rounded down to 16 (an earlier design that loaded
+// each window straight from memory stalled the texture-data path on the L1
+// with its overlapping misaligned 16-byte accesses). Rows outside the image
+// are the zero padding: the compute waves skip them. Three band buffers keep
+// up to two bands in flight; one workgroup barrier per band hands a buffer
+// over. The loader only loads, so its waits are exact and the compute waves'
+// stores are never waited for. Compute waves take 32-pixel groups of the
+// band, read each window half as dwords from LDS, run the MFMAs and the
+// epilogue, and store the group's 32 x C_out halves (contiguous in y)
+// through a small LDS tile as whole 16-byte pieces. A lane keeps its pixel's
+// row and column from one group to the next by adding (no division in the
+// loop): the loop is VALU-bound, and per-group index arithmetic was most of
+// it. Every half of the window that meets a zero weight (pixel 2q-2, and
+// halves 12-15) is masked to zero, as are the padding pixel -1 (q = 0) and
+// padding rows: the result never depends on an input outside the receptive
+// field, Inf and NaN included. The second window half never reads past its
+// row's end: its last 8 bytes are masked, not read from the next row.
+#include <stdlib.h>
+
+#include <type_traits>
+
+#include "tg_device.hpp"
+#include "tg_internal.hpp"
+
+namespace tg {
+namespace {
+
+constexpr int kStemBands = 3;  // band buffers in LDS
+
+template <int N>
+__device__ __forceinline__ void stem_wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ void stem_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// 16-byte direct-to-LDS buffer load (lane l -> lds + 16*l; offsets at or past
+// num_records read as zeros); ordered by explicit vmcnt waits.
+__device__ __forceinline__ void stem_dma16(u32x4_t rsrc, unsigned voff, unsigned lds) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds"
+                 :
+                 : "v"(voff), "s"(rsrc), "{m0}"(lds)
+                 : "memory");
+}
+
+// Band buffer bytes: 2R+1 input rows, the up to 12 bytes that the
+// rounded-down start adds and 20 bytes that the last window may read past
+// its row (masked), rounded up to whole 1 KB load instructions.
+__host__ __device__ inline int stem_band_bytes(int W, int R) {
+    const int b = (2 * R + 1) * W * 6 + 32;
+    return (b + 1023) / 1024 * 1024;
+}
+
+template <int NB, int EPI, int LI>
+__global__ __launch_bounds__(320) void conv2d_bn_silu_stem(
+    const f16* __restrict__ x, const f16* __restrict__ w, const float* __restrict__ scale,
+    const float* __restrict__ bias, f16* __restrict__ y, ConvGeom g, int R, int nbands) {
+    static_assert(LI <= 31, "vmcnt range for two bands in flight");
+    constexpr int kMaxC = 32 * NB;
+    // Band buffers are LI KB each: every band load issues exactly LI 1 KB
+    // instructions (the ones past the band's rows read zeros) so that the
+    // loader's wait counts are exact, and they all land inside the buffer.
+    constexpr int band_bytes = LI * 1024;
+    extern __shared__ __attribute__((aligned(16))) unsigned char stem_smem[];
+    // [16-byte margin][band buffers][4 x 32 x kMaxC output tiles]. The
+    // margin keeps the first window of a row (12 bytes before the row)
+    // inside the allocation; what it reads there is masked.
+    f16* tiles = (f16*)(stem_smem + 16 + kStemBands * band_bytes);
+
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int bands_per_img = (g.P + R - 1) / R;
+    const int rowb = g.W * 6;  // bytes per input row
+    // Bands of this workgroup: blockIdx.x, + gridDim.x, ...
+    const int nmine = (int)blockIdx.x < nbands ? (nbands - 1 - (int)blockIdx.x) / (int)gridDim.x + 1 : 0;
+
+    if (wave == 4) {
+        // ---------------- loader wave ----------------
+        const unsigned long long a = (unsigned long long)x;
+        u32x4_t rs;
+        rs[0] = (unsigned)a;
+        rs[1] = (unsigned)(a >> 32) & 0xffffu;
+        rs[2] = (unsigned)g.N * (unsigned)g.H * (unsigned)rowb;
+        rs[3] = 0x00020000u;
+        const unsigned base = __builtin_amdgcn_readfirstlane(
+            (unsigned)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)stem_smem) + 16u);
+        // Band k of this workgroup into buffer k % kStemBands: byte c of the
+        // buffer is byte a0 + c of x, a0 the band's first in-image row start
+        // rounded down to 16. Every call for one of the workgroup's bands
+        // issues exactly LI loads (past the band's rows: zeros); past its
+        // last band, none.
+        auto issue = [&](int k) {
+            if (k >= nmine) return;
+            const int band = (int)blockIdx.x + k * (int)gridDim.x;
+            const int n = band / bands_per_img, p0 = (band - n * bands_per_img) * R;
+            const int ih0 = 2 * p0 - 1 < 0 ? 0 : 2 * p0 - 1;
+            const int ih1 = 2 * p0 + 2 * R < g.H ? 2 * p0 + 2 * R : g.H;  // exclusive
+            const unsigned a0 = (unsigned)((n * g.H + ih0) * rowb) & ~15u;
+            const unsigned a1 = (unsigned)((n * g.H + ih1) * rowb);
+            const unsigned dst = base + (unsigned)((k % kStemBands) * band_bytes);
+#pragma unroll
+            for (int i = 0; i < LI; ++i) {
+                const unsigned c = (unsigned)((i * 64 + lane) * 16);
+                const bool ok = a0 + c < a1;
+                stem_dma16(rs, ok ? a0 + c : 0x80000000u, dst + (unsigned)(i * 1024));
+            }
+        };
+        // Band 0 alone first: at launch every workgroup's first band would
+        // otherwise share HBM with its second, and compute would start later.
+        issue(0);
+        stem_wait_vmcnt<0>();
+        stem_barrier();  // band 0 ready
+        issue(1);
+        issue(2);
+        for (int k = 0; k < nmine; ++k) {
+            if (k + 2 < nmine)
+                stem_wait_vmcnt<LI>();  // band k+1 landed (band k+2 may be pending)
+            else
+                stem_wait_vmcnt<0>();
+            stem_barrier();  // band k done by every compute wave
+            issue(k + 3);  // into the buffer band k has just released
+        }
+        stem_wait_vmcnt<0>();
+        return;
+    }
+
+    // ---------------- compute waves ----------------
+    // 32x32x16 MFMA: lane (lc, hl) supplies K halves 8hl..8hl+7 of column lc
+    // (pixel) and row lc (channel); accumulator i of a lane is channel
+    // 8(i/4) + 4hl + i%4 of pixel lc.
+    const int lc = lane & 31, hl = lane >> 5;
+    // Filter slots: A[f][r] holds, for channel 32f + lc, K-slot halves
+    // 8hl..8hl+7 of filter row r: slot half j carries w[o][r][s][c] at
+    // j = 3 + 3s + c, else 0.
+    half8_t A[NB][3];
+#pragma unroll
+    for (int f = 0; f < NB; ++f)
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            const int o = 32 * f + lc;
+            const bool ook = o < g.C_out;
+            const int wb = ((ook ? o : 0) * 3 + r) * 9;
+            half8_t v;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int j = 8 * hl + e - 3;  // 0..8 inside the window: (s, c) = (j/3, j%3)
+                const bool ok = ook && j >= 0 && j < 9;
+                const f16 wv = w[wb + (j < 0 ? 0 : (j > 8 ? 8 : j))];
+                v[e] = ok ? wv : (f16)0.0f;
+            }
+            A[f][r] = v;
+        }
+    float sc[NB][16], bi[NB][16];
+#pragma unroll
+    for (int f = 0; f < NB; ++f)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            epi_consts<EPI>(scale, bias, 32 * f + 8 * (i / 4) + 4 * hl + (i % 4), g.C_out, sc[f][i],
+                            bi[f][i]);
+
+    f16* tl = tiles + wave * 32 * kMaxC;
+    // Window dwords that always meet zero weights: half 0 holds pixel 2q-2
+    // (halves 0-2) before 2q-1 and 2q; half 1 holds 2q, 2q+1 (halves 8-11)
+    // and nothing of use in halves 12-15.
+    const unsigned hm = hl ? ~0u : 0u;
+    const int hoff = 16 * hl - 12;  // window bytes from 12q in its row
+    stem_barrier();  // band 0 ready
+    for (int k = 0; k < nmine; ++k) {
+        const int band = (int)blockIdx.x + k * (int)gridDim.x;
+        const int n = band / bands_per_img, p0 = (band - n * bands_per_img) * R;
+        const int rows = g.P - p0 < R ? g.P - p0 : R;
+        // Input row ih sits at byte (ih - ih0) * rowb + shift of the buffer.
+        const int ih0 = 2 * p0 - 1 < 0 ? 0 : 2 * p0 - 1;
+        const int shift = ((n * g.H + ih0) * rowb) & 15;
+        const unsigned char* bb = stem_smem + 16 + (k % kStemBands) * band_bytes + shift;
+        const int npx = rows * g.Q;
+        const int ngroups = (npx + 31) / 32;
+        const long long m_base = ((long long)n * g.P + p0) * g.Q;  // first pixel of the band
+        int pix = wave * 32 + lc;
+        int pl = pix / g.Q;
+        int q = pix - pl * g.Q;
+        int ihr = 2 * (p0 + pl) - 1;    // input row of filter row 0
+        int roff = (ihr - ih0) * rowb;  // its byte offset in the buffer (-rowb: row -1)
+        int colb = 12 * q;
+        // Bands touching a padding row (top of the image, or the bottom when
+        // H is odd) check rows per lane; the others skip that code.
+        auto walk = [&](auto edge_tag) {
+            constexpr bool EDGE = decltype(edge_tag)::value;
+            for (int grp = wave; grp < ngroups; grp += 4) {
+                const bool pok = pix < npx;
+                // Lanes past the band read a harmless in-buffer address.
+                const int a = pok ? roff + colb + hoff : 16;
+                const unsigned lm = q == 0 ? 0u : ~0u;  // q = 0: pixel -1 is padding
+                const u32x4_t m = {hm, hm | (lm & 0xffff0000u), ~hm & lm, ~hm};
+                half8_t b[3];
+#pragma unroll
+                for (int r = 0; r < 3; ++r) {
+                    int at = a + r * rowb;
+                    bool rok = true;
+                    if (EDGE) {  // padding rows are not in the buffer (row -1 lies before it)
+                        rok = (unsigned)(ihr + r) < (unsigned)g.H;
+                        if (!rok) at = 16;
+                    }
+                    const unsigned* p32 = (const unsigned*)(bb + at);
+                    u32x4_t u = {p32[0], p32[1], p32[2], p32[3]};
+                    u &= m;
+                    if (EDGE && !rok) u = (u32x4_t){0u, 0u, 0u, 0u};
+                    b[r] = __builtin_bit_cast(half8_t, u);
+                }
+                float16_t acc[NB];
+#pragma unroll
+                for (int f = 0; f < NB; ++f) {
+                    acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[f][0], b[0], (float16_t){}, 0, 0, 0);
+                    acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[f][1], b[1], acc[f], 0, 0, 0);
+                    acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[f][2], b[2], acc[f], 0, 0, 0);
+                }
+#pragma unroll
+                for (int f = 0; f < NB; ++f)
+#pragma unroll
+                    for (int blk = 0; blk < 4; ++blk) {
+                        const int c0 = 32 * f + 8 * blk;  // C_out % 8 == 0: whole blocks
+                        if (c0 < g.C_out) {
+                            half4_t h;
+#pragma unroll
+                            for (int e = 0; e < 4; ++e)
+                                h[e] = (f16)epilogue<EPI>(acc[f][4 * blk + e], sc[f][4 * blk + e],
+                                                          bi[f][4 * blk + e]);
+                            *(half4_t*)(tl + lc * g.C_out + c0 + 4 * hl) = h;
+                        }
+                    }
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_wave_barrier();
+                asm volatile("" ::: "memory");
+                // The group's 32 x C_out halves are contiguous in y.
+                const int valid = npx - grp * 32 < 32 ? npx - grp * 32 : 32;
+                const int pieces = valid * g.C_out / 8;
+                f16* yg = y + (m_base + grp * 32) * g.C_out;
+#pragma unroll
+                for (int i = 0; i < (4 * kMaxC + 63) / 64; ++i) {
+                    const int v = lane + 64 * i;
+                    if (v < pieces)
+                        __builtin_nontemporal_store(*(const half8_t*)(tl + v * 8), (half8_t*)(yg + v * 8));
+                }
+                asm volatile("" ::: "memory");
+                __builtin_amdgcn_wave_barrier();
+                asm volatile("" ::: "memory");
+                // Next group of this wave: 128 pixels on.
+                pix += 128;
+                q += 128;
+                colb += 12 * 128;
+                while (q >= g.Q) {
+                    q -= g.Q;
+                    colb -= 12 * g.Q;
+                    ihr += 2;
+                    roff += 2 * rowb;
+                }
+            }
+        };
+        if (p0 == 0 || 2 * (p0 + rows) > g.H)
+            walk(std::true_type{});
+        else
+            walk(std::false_type{});
+        stem_barrier();  // band k consumed; band k+1 ready
+    }
+}
+
+}  // namespace
+
+int stem_rows(const ConvGeom& g) {
+    // Enough rows that a band holds a few 32-pixel groups per compute wave.
+    int R = (384 + g.Q - 1) / g.Q;
+    if (R < 2) R = 2;
+    if (R > 8) R = 8;
+    if (R > g.P) R = g.P;
+    while (R > 1 && stem_band_bytes(g.W, R) > 31 * 1024) --R;
+    return R;
+}
+
+bool stem_rows_ok(const ConvGeom& g, int R) {
+    return R >= 1 && R <= g.P && stem_band_bytes(g.W, R) <= 31 * 1024;
+}
+
+bool stem_serves(const ConvGeom& g) {
+    return g.C_in == 3 && g.kh == 3 && g.kw == 3 && g.stride == 2 && g.pad == 1 &&
+           g.W % 2 == 0 && g.C_out % 8 == 0 && g.C_out <= 64 && stem_rows_ok(g, 1) &&
+           6LL * g.N * g.H * g.W < (1LL << 31);
+}
+
+hipError_t launch_stem(const ConvGeom& g, int wg_per_cu, int R, bool identity, const void* x,
+                       const void* w, const float* scale, const float* bias, void* y,
+                       hipStream_t s) {
+    if (!stem_serves(g) || !stem_rows_ok(g, R)) return hipErrorInvalidValue;
+    const int bands = g.N * ((g.P + R - 1) / R);
+    long long grid = 256LL * (wg_per_cu < 1 ? 1 : wg_per_cu);
+    if (grid > bands) grid = bands;
+    const int nb = (g.C_out + 31) / 32;
+    const int li = stem_band_bytes(g.W, R) / 1024;
+#define TG_STEM_K(NBV, EPI, LIV)                                                              \
+    do {                                                                                      \
+        auto k = conv2d_bn_silu_stem<NBV, EPI, LIV>;                                          \
+        const size_t lds = 16 + (size_t)kStemBands * (LIV)*1024 + 4 * 32 * 32 * (NBV) * 2;     \
+        static size_t attr = 0;                                                               \
+        if (lds > attr) {                                                                     \
+            hipError_t e = hipFuncSetAttribute((const void*)k,                                \
+                                               hipFuncAttributeMaxDynamicSharedMemorySize,    \
+                                               (int)lds);                                     \
+            if (e != hipSuccess) return e;                                                    \
+            attr = lds;                                                                       \
+        }                                                                                     \
+        hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(320), lds, s, (const f16*)x,         \
+                           (const f16*)w, scale, bias, (f16*)y, g, R, bands);                  \
+        return hipGetLastError();                                                             \
+    } while (0)
+#define TG_STEM_LI(NBV, EPI)                   \
+    do {                                       \
+        if (li <= 4) TG_STEM_K(NBV, EPI, 4);   \
+        if (li <= 6) TG_STEM_K(NBV, EPI, 6);   \
+        if (li <= 8) TG_STEM_K(NBV, EPI, 8);   \
+        if (li <= 10) TG_STEM_K(NBV, EPI, 10); \
+        if (li <= 12) TG_STEM_K(NBV, EPI, 12); \
+        if (li <= 14) TG_STEM_K(NBV, EPI, 14); \
+        if (li <= 16) TG_STEM_K(NBV, EPI, 16); \
+        if (li <= 20) TG_STEM_K(NBV, EPI, 20); \
+        if (li <= 24) TG_STEM_K(NBV, EPI, 24); \
+        TG_STEM_K(NBV, EPI, 31);               \
+    } while (0)
+#define TG_STEM(NBV)                                 \
+    do {                                             \
+        if (identity) TG_STEM_LI(NBV, EPI_IDENTITY); \
+        else TG_STEM_LI(NBV, EPI_FUSED);             \
+    } while (0)
+    if (nb == 1) TG_STEM(1);
+    TG_STEM(2);
+#undef TG_STEM
+#undef TG_STEM_LI
+#undef TG_STEM_K
+}
+
+}  // namespace tg

@@ -79,6 +79,14 @@ void igemm_patch_describe(int cfg, int* BM, int* BN, int* WM, int* WN, int* WK);
 hipError_t launch_igemm_patch(const ConvGeom& g, int cfg, bool identity, const void* x,
                               const void* w, const float* scale, const float* bias, void* y,
                               hipStream_t s);
+// Stem kernel (stem.hip): C_in = 3, 3x3, stride 2, pad 1, even W, C_out % 8 == 0
+// and <= 64; one workgroup per CU walks bands of R output rows.
+bool stem_serves(const ConvGeom& g);
+int stem_rows(const ConvGeom& g);
+bool stem_rows_ok(const ConvGeom& g, int R);
+hipError_t launch_stem(const ConvGeom& g, int wg_per_cu, int R, bool identity, const void* x,
+                       const void* w, const float* scale, const float* bias, void* y,
+                       hipStream_t s);
 // Tiled direct conv on MFMA (tiled_mfma.hip): K <= 32, C_out <= 32.
 bool tiled_mfma_serves(const ConvGeom& g);
 int tiled_mfma_rows(const ConvGeom& g);

@@ -8,8 +8,10 @@ when a plan is created) and checked against the fp64 oracle:
   * the streaming 1x1 kernel with and without full-line input staging
     (TG_STREAM, TG_XDMA = prefetch depth);
   * the register-weights kernel's non-default splits and plain stores;
-  * the band-staged MFMA kernel without its persistent pipeline
-    (TG_TM_PIPE=0), and the VALU tiled kernel (TG_TILED_MFMA=0);
+  * the stem kernel (3-channel 3x3 stride-2 layers) over channel counts,
+    image sizes, pixel tails and wave counts (TG_STEM), and with it switched
+    off the band-staged MFMA kernel with and without its persistent
+    pipeline (TG_TM_PIPE) and the VALU tiled kernel (TG_TILED_MFMA=0);
   * the patch-staged implicit GEMM for stride-1 layers with C_in % 64 == 0
     in every tile configuration (TG_PATCH_CFG), including partial channel
     tiles, ragged pixel tails and channel counts it declines;
@@ -138,11 +140,45 @@ def test_cu_kernel_falls_back_for_unaligned_batchnorm_vectors():
                                  {"TG_TM_ROWS": "4"}, {"TG_TILED_MFMA": "0"}],
                          ids=["nopipe", "nopipe_r4", "pipe_r4", "valu"])
 def test_tiled_variants(monkeypatch, env):
+    monkeypatch.setenv("TG_STEM", "0")
     for k, v in env.items():
         monkeypatch.setenv(k, v)
     for wl in (WORKLOADS["stem3x3s2_k16"].scaled(N=2), WORKLOADS["stem3x3s2_k24"].scaled(N=1),
                Workload("stem_odd", 53, 1, 37, 29, 3, 24, 3, 3, 2, 1, "f16")):
         check_workload(wl, "tiled")
+
+
+STEM_SHAPES = [
+    Workload("stem_k16_small", 60, 2, 40, 36, 3, 16, 3, 3, 2, 1, "f16"),
+    Workload("stem_k24_odd_h", 61, 1, 37, 34, 3, 24, 3, 3, 2, 1, "f16"),
+    Workload("stem_k8_q16", 62, 3, 32, 32, 3, 8, 3, 3, 2, 1, "f16"),
+    Workload("stem_k32", 63, 1, 50, 48, 3, 32, 3, 3, 2, 1, "f16", ("uniform", -2.0, 2.0)),
+    Workload("stem_k48_h2", 64, 2, 2, 64, 3, 48, 3, 3, 2, 1, "f16"),
+    Workload("stem_k64", 65, 1, 34, 40, 3, 64, 3, 3, 2, 1, "f16"),
+    Workload("stem_k16_tail", 66, 1, 33, 38, 3, 16, 3, 3, 2, 1, "f16"),
+    # Many short bands per workgroup.
+    Workload("stem_ring", 67, 96, 130, 16, 3, 16, 3, 3, 2, 1, "f16"),
+]
+
+
+@pytest.mark.parametrize("wpc,rows", [("3", ""), ("4", "1"), ("2", "2"), ("1", "")])
+def test_stem_kernel(monkeypatch, wpc, rows):
+    """Workgroups per CU and band heights: with one-row bands the full-size
+    workloads give each workgroup many bands, so its three band buffers are
+    refilled while its compute waves work."""
+    monkeypatch.setenv("TG_STEM", wpc)
+    monkeypatch.setenv("TG_STEM_ROWS", rows)
+    for wl in STEM_SHAPES:
+        d = _plan(wl, "tiled").describe()
+        note("%s -> %s" % (wl.name, d))
+        assert d.startswith("stem")
+        check_workload(wl, "tiled")
+        check_workload(wl, "unfused")
+    for name in ("stem3x3s2_k16", "stem3x3s2_k24"):
+        d = _plan(WORKLOADS[name], "auto").describe()
+        note("%s -> %s" % (name, d))
+        assert d.startswith("stem")
+        check_workload(WORKLOADS[name], "auto")
 
 
 PATCH_SHAPES = [
