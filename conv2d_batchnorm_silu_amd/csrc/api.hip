@@ -411,10 +411,11 @@ tg_status tg_conv_bn_silu_describe(const tg_conv_bn_silu_plan* plan, char* buf, 
                  plan->rw_nf, plan->rw_cs, plan->rw_ncw, plan->rw_grid, plan->rw_nt ? " nt" : "");
     } else if (plan->kernel == TG_KERNEL_IGEMM && plan->patch_cfg >= 0) {
         int BM, BN, WM, WN, WK;
-        igemm_patch_describe(plan->patch_cfg, &BM, &BN, &WM, &WN, &WK);
+        int ring;
+        igemm_patch_describe(plan->patch_cfg, &BM, &BN, &WM, &WN, &WK, &ring);
         int tiles = g.N * ((g.P * g.Q + BM - 1) / BM) * ((g.C_out + BN - 1) / BN);
-        snprintf(k, sizeof(k), "igemm_patch cfg=%d BM=%d BN=%d waves=%dx%dx%d grid=%d",
-                 plan->patch_cfg, BM, BN, WK, WM, WN, tiles);
+        snprintf(k, sizeof(k), "igemm_patch cfg=%d BM=%d BN=%d waves=%dx%dx%d ring=%d grid=%d",
+                 plan->patch_cfg, BM, BN, WK, WM, WN, ring, tiles);
     } else if (plan->kernel == TG_KERNEL_IGEMM && plan->dma_cfg >= 0) {
         const IgemmCfg& c = igemm_dma_cfg(plan->dma_cfg);
         int tm = (g.M + c.BM - 1) / c.BM, tn = (g.C_out + c.BN - 1) / c.BN;

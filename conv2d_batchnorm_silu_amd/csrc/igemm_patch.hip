@@ -65,10 +65,20 @@ __device__ __forceinline__ void pt_dma16(u32x4_t rsrc, unsigned voff, unsigned l
                  : "memory");
 }
 
-constexpr int kPatchRing = 4;
+// 16-byte LDS read issued as inline asm: the compiler does not track it, so
+// its completion is the caller's explicit lgkmcnt wait (pt_frag_wait). The
+// compiler's own tracking turned conservative in this kernel's K loop and
+// waited for the next chunk's fragment reads before the current chunk's
+// MFMAs, which serialised LDS and the matrix cores.
+__device__ __forceinline__ half8_t pt_lds16(unsigned addr) {
+    half8_t r;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(addr) : "memory");
+    return r;
+}
 
-template <int BM, int BN, int WM, int WN, int WK>
+template <int BM, int BN, int WM, int WN, int WK, int RING>
 struct PatchShape {
+    static_assert(RING == 3 || RING == 4, "filter ring of three or four stages");
     static constexpr int WPG = WM * WN;                // waves per K-group
     static_assert(WPG == 2 || WPG == 4, "two or four waves per K-group");
     static_assert(WK == 1 || WK == 2, "one or two K-groups");
@@ -79,11 +89,11 @@ struct PatchShape {
     static constexpr int LI = FN * 16 * PPR / 64;      // filter loads per chunk per wave
     static_assert(FN * 16 * PPR % 64 == 0, "whole load instructions");
     static constexpr int WSTAGE = FN * 16 * PPR * 16;  // bytes per stage of a wave's ring
-    static constexpr int RING_BYTES = NW * kPatchRing * WSTAGE;
+    static constexpr int RING_BYTES = NW * RING * WSTAGE;
     static constexpr int OROW = BN + 8;                // output tile row (halves)
     static constexpr int RED_BYTES = WK == 2 ? WPG * FN * FM * 64 * 16 : 0;
     static constexpr int EPI_BYTES = RED_BYTES + BM * OROW * 2;
-    static_assert(LI * kPatchRing <= 63, "vmcnt range");
+    static_assert(LI * RING <= 63, "vmcnt range");
 };
 
 // Slot of piece p in row r of a wave's filter stage is p ^ pt_wswz<WK>(r):
@@ -94,12 +104,12 @@ __device__ __forceinline__ int pt_wswz(int r) {
     return WK == 2 ? (r >> 1) & 3 : (r >> 1) & 7;
 }
 
-template <int BM, int BN, int WM, int WN, int WK, int EPI>
+template <int BM, int BN, int WM, int WN, int WK, int RING, int EPI>
 __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_patch(
     const f16* __restrict__ x, const f16* __restrict__ w, const float* __restrict__ scale,
     const float* __restrict__ bias, f16* __restrict__ y, ConvGeom g, int tiles_per_img,
     int tiles_n, int PW, int pstride) {
-    using S = PatchShape<BM, BN, WM, WN, WK>;
+    using S = PatchShape<BM, BN, WM, WN, WK, RING>;
     extern __shared__ __attribute__((aligned(16))) unsigned char pt_smem[];
 
     const int tile = xcd_contiguous_tile(blockIdx.x, gridDim.x);
@@ -123,7 +133,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
     const int cchunks = g.C_in / 64;
     const int nk = g.kh * g.kw * cchunks;
 
-    unsigned char* ring = pt_smem + wave * kPatchRing * S::WSTAGE;  // this wave's ring
+    unsigned char* ring = pt_smem + wave * RING * S::WSTAGE;  // this wave's ring
     unsigned char* patch = pt_smem + S::RING_BYTES;
     const unsigned ring_lds = __builtin_amdgcn_readfirstlane(
         (unsigned)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)ring));
@@ -142,15 +152,16 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
         const int kp = (WK == 2 ? kg * S::PPR : 0) + piece;
         woff[i] = o < g.C_out ? (unsigned)((o * g.K + kp * 8) * 2) : 0x80000000u;
     }
+    // Chunk kc's filter loads; past the last chunk they read zeros (out of
+    // the buffer's range) so that every step issues the same loads.
     auto issue = [&](int kc) {
         const int tap = kc / cchunks, cc = kc - tap * cchunks;
-        const unsigned koff = (unsigned)((tap * g.C_in + cc * 64) * 2);
-        const unsigned dst = ring_lds + (unsigned)(kc % kPatchRing) * S::WSTAGE;
+        const unsigned koff = kc < nk ? (unsigned)((tap * g.C_in + cc * 64) * 2) : 0x80000000u;
+        const unsigned dst = ring_lds + (unsigned)(kc % RING) * S::WSTAGE;
 #pragma unroll
         for (int i = 0; i < S::LI; ++i) pt_dma16(wrs, woff[i] + koff, dst + i * 1024);
     };
-    int issued = 0;
-    for (; issued < kPatchRing - 1 && issued < nk; ++issued) issue(issued);
+    for (int kc = 0; kc < RING - 1; ++kc) issue(kc);
 
     // Input patch: PR x PW pixels x C_in channels, zeros outside the image.
     // Thread u copies 16-byte piece (u % upp) of pixels u/upp, u/upp + step,
@@ -219,28 +230,37 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
     struct Frags {
         half8_t a[KSW][S::FN], b[KSW][S::FM];
     };
-    // Chunk kc's filter data: this wave's loads are done when at most the
-    // (issued - kc - 1) later chunks' loads are pending.
-    auto wait_chunk = [&](int kc) {
-        switch (issued - kc - 1) {
-            case 0: pt_wait_vmcnt<0>(); break;
-            case 1: pt_wait_vmcnt<S::LI>(); break;
-            case 2: pt_wait_vmcnt<2 * S::LI>(); break;
-            default: pt_wait_vmcnt<3 * S::LI>(); break;
+    // Wait for every outstanding fragment read, after the MFMAs that read
+    // F: F's registers pass through (empty) volatile asm statements placed
+    // before the wait, which orders those MFMAs ahead of it, so the wait
+    // overlaps their execution.
+    auto frag_wait = [&](Frags& F) {
+#pragma unroll
+        for (int kk = 0; kk < KSW; ++kk) {
+#pragma unroll
+            for (int f = 0; f < S::FN; ++f) asm volatile("" : "+v"(F.a[kk][f]));
+#pragma unroll
+            for (int f = 0; f < S::FM; ++f) asm volatile("" : "+v"(F.b[kk][f]));
         }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     };
+    // Chunk kc's filter data has landed once only the loads of the RING - 2
+    // chunks issued after it are pending (chunks run RING - 1 ahead).
+    auto wait_chunk = [&]() { pt_wait_vmcnt<(RING - 2) * S::LI>(); };
+    const unsigned patch_lds = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)patch));
     auto load = [&](int kc, int tr, int ts, int c, Frags& F) {
-        const unsigned char* st = ring + (kc % kPatchRing) * S::WSTAGE;
-        const int delta = (tr * PW + ts) * pstride + c * 128;
+        const unsigned st = ring_lds + (unsigned)((kc % RING) * S::WSTAGE);
+        const unsigned delta = (unsigned)((tr * PW + ts) * pstride + c * 128);
 #pragma unroll
         for (int kk = 0; kk < KSW; ++kk) {
             const int ks = WK == 2 ? kg : kk;
 #pragma unroll
             for (int f = 0; f < S::FN; ++f)
-                F.a[kk][f] = *(const half8_t*)(st + (bbase[f] ^ (WK == 2 ? 0 : ks * 64)));
+                F.a[kk][f] = pt_lds16(st + (unsigned)(bbase[f] ^ (WK == 2 ? 0 : ks * 64)));
 #pragma unroll
             for (int f = 0; f < S::FM; ++f)
-                F.b[kk][f] = *(const half8_t*)(patch + abase[f] + delta + ks * 64);
+                F.b[kk][f] = pt_lds16(patch_lds + (unsigned)(abase[f] + ks * 64) + delta);
         }
     };
     auto mma = [&](const Frags& F) {
@@ -253,51 +273,64 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
                     acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(F.a[kk][i], F.b[kk][j],
                                                                        acc[i][j], 0, 0, 0);
     };
-    // (tap_r, tap_s, cc) of the chunk whose fragments are loaded next.
+    // (tap_r, tap_s, cc) of the chunk whose fragments are loaded next;
+    // advanced with selects, not branches.
     int tap_r = 0, tap_s = 0, cc = 0;
     auto advance = [&]() {
-        if (++cc == cchunks) {
-            cc = 0;
-            if (++tap_s == g.kw) { tap_s = 0; ++tap_r; }
-        }
+        const bool wc = cc + 1 == cchunks;
+        cc = wc ? 0 : cc + 1;
+        const bool ws = wc && tap_s + 1 == g.kw;
+        tap_s = ws ? 0 : (wc ? tap_s + 1 : tap_s);
+        tap_r = ws ? tap_r + 1 : tap_r;
     };
     Frags F0, F1;
-    wait_chunk(0);
+    wait_chunk();
     load(0, tap_r, tap_s, cc, F0);
     advance();
+    frag_wait(F0);
     // One step: refill the ring, fetch chunk kc+1's fragments into `nxt`,
-    // then run chunk kc's MFMAs from `cur`. Stage (kc + 3) % 4 was last read
-    // for chunk kc - 1, whose fragments are in registers by now.
-    auto step = [&](int kc, const Frags& cur, Frags& nxt) {
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        if (issued < nk) issue(issued++);
-        if (kc + 1 < nk) {
-            wait_chunk(kc + 1);
-            load(kc + 1, tap_r, tap_s, cc, nxt);
-            advance();
-        }
+    // run chunk kc's MFMAs from `cur`, then wait for the fetch (it overlaps
+    // the MFMAs). Stage (kc + 3) % 4 was last read for chunk kc - 1, whose
+    // fragment reads completed at the end of step kc - 2. The last step
+    // re-reads chunk kc (unused) so that every step has the same shape.
+    auto step = [&](int kc, Frags& cur, Frags& nxt) {
+        issue(kc + RING - 1);
+        const bool more = kc + 1 < nk;
+        const int tr = more ? tap_r : 0, ts = more ? tap_s : 0, c = more ? cc : 0;
+        advance();
+        wait_chunk();
+        load(more ? kc + 1 : kc, tr, ts, c, nxt);
         mma(cur);
+        frag_wait(cur);
     };
-    for (int kc = 0; kc < nk; kc += 2) {
+    // Pairs of steps in straight-line code (the compiler's wait counts stay
+    // exact across the back edge), then an odd last step.
+    int kc = 0;
+    for (; kc + 1 < nk; kc += 2) {
         step(kc, F0, F1);
-        if (kc + 1 < nk) step(kc + 1, F1, F0);
+        step(kc + 1, F1, F0);
     }
+    if (kc < nk) step(kc, F0, F1);
     pt_barrier();  // every wave is done with its ring and the patch: reuse LDS
 
+    // WK = 2: the two K-groups share the epilogue. Group 0 owns fragment
+    // columns j < JH, group 1 the rest; each hands its partial sums of the
+    // other group's fragments over through LDS and adds the ones it gets.
+    constexpr int JH = (S::FM + 1) / 2;
+    auto owned = [&](int j) { return WK == 1 || (j < JH) == (kg == 0); };
     if (WK == 2) {
         float4_t* red = (float4_t*)pt_smem + w4 * S::FN * S::FM * 64 + lane;
-        if (kg == 1) {
-#pragma unroll
-            for (int i = 0; i < S::FN; ++i)
-#pragma unroll
-                for (int j = 0; j < S::FM; ++j) red[(i * S::FM + j) * 64] = acc[i][j];
-        }
-        pt_barrier();
-        if (kg == 1) goto store_phase;
 #pragma unroll
         for (int i = 0; i < S::FN; ++i)
 #pragma unroll
-            for (int j = 0; j < S::FM; ++j) acc[i][j] += red[(i * S::FM + j) * 64];
+            for (int j = 0; j < S::FM; ++j)
+                if (!owned(j)) red[(i * S::FM + j) * 64] = acc[i][j];
+        pt_barrier();
+#pragma unroll
+        for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+            for (int j = 0; j < S::FM; ++j)
+                if (owned(j)) acc[i][j] += red[(i * S::FM + j) * 64];
     }
 
     {
@@ -311,6 +344,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
             for (int e = 0; e < 4; ++e) epi_consts<EPI>(scale, bias, n0 + cb + e, g.C_out, sc[e], bi[e]);
 #pragma unroll
             for (int j = 0; j < S::FM; ++j) {
+                if (!owned(j)) continue;
                 const int pr = wm * S::FM * 16 + j * 16 + lr;
                 half4_t h;
 #pragma unroll
@@ -320,7 +354,6 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
         }
     }
 
-store_phase:
     pt_barrier();
     {
         const f16* out = (const f16*)(pt_smem + S::RED_BYTES);
@@ -344,21 +377,25 @@ store_phase:
     }
 }
 
+// BM, BN, WM, WN, WK, filter ring stages. The three-stage ring leaves room
+// for the conflict-free patch stride where four stages would not.
 #define TG_PATCH_CFGS(X)        \
-    X(112, 128, 1, 2, 2)        \
-    X(224, 64, 2, 1, 2)         \
-    X(112, 128, 1, 4, 2)        \
-    X(224, 64, 2, 2, 2)         \
-    X(128, 64, 2, 2, 2)         \
-    X(64, 64, 2, 2, 2)          \
-    X(112, 128, 1, 4, 1)        \
-    X(224, 64, 2, 2, 1)
+    X(112, 128, 1, 2, 2, 4)     \
+    X(224, 64, 2, 1, 2, 4)      \
+    X(112, 128, 1, 4, 2, 4)     \
+    X(224, 64, 2, 2, 2, 4)      \
+    X(128, 64, 2, 2, 2, 4)      \
+    X(64, 64, 2, 2, 2, 4)       \
+    X(112, 128, 1, 4, 1, 4)     \
+    X(224, 64, 2, 2, 1, 4)      \
+    X(224, 64, 2, 2, 2, 3)      \
+    X(112, 128, 1, 4, 2, 3)
 
 struct PatchCfg {
-    int BM, BN, WM, WN, WK;
+    int BM, BN, WM, WN, WK, RING;
 };
 const PatchCfg kPatchCfgs[] = {
-#define X(bm, bn, wm, wn, wk) {bm, bn, wm, wn, wk},
+#define X(bm, bn, wm, wn, wk, ring) {bm, bn, wm, wn, wk, ring},
     TG_PATCH_CFGS(X)
 #undef X
 };
@@ -378,8 +415,8 @@ int patch_rows_max(const ConvGeom& g, int BM) {
 }
 
 size_t patch_lds_bytes_w(const ConvGeom& g, const PatchCfg& c, int pw, int pstride) {
-    // Wave-private rings: WM*WN*WK waves x 4 stages x (BN/WN rows x 128/WK bytes).
-    const size_t ring = (size_t)c.WM * c.WN * c.WK * kPatchRing * (c.BN / c.WN) * (128 / c.WK);
+    // Wave-private rings: WM*WN*WK waves x RING stages x (BN/WN rows x 128/WK bytes).
+    const size_t ring = (size_t)c.WM * c.WN * c.WK * c.RING * (c.BN / c.WN) * (128 / c.WK);
     const size_t pr = (size_t)patch_rows_max(g, c.BM) + g.kh - 1;
     const size_t patch = pr * (size_t)pw * (size_t)pstride;
     const size_t red =
@@ -407,16 +444,16 @@ size_t patch_lds_bytes(const ConvGeom& g, const PatchCfg& c) {
     return patch_lds_bytes_w(g, c, L.pw, L.pstride);
 }
 
-template <int BM, int BN, int WM, int WN, int WK>
+template <int BM, int BN, int WM, int WN, int WK, int RING>
 hipError_t patch_launch_one(const ConvGeom& g, bool identity, const void* x, const void* w,
                             const float* scale, const float* bias, void* y, hipStream_t s) {
-    using S = PatchShape<BM, BN, WM, WN, WK>;
-    const PatchCfg c = {BM, BN, WM, WN, WK};
+    using S = PatchShape<BM, BN, WM, WN, WK, RING>;
+    const PatchCfg c = {BM, BN, WM, WN, WK, RING};
     const size_t lds = patch_lds_bytes(g, c);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     const int tiles_per_img = (g.P * g.Q + BM - 1) / BM, tiles_n = (g.C_out + BN - 1) / BN;
-    auto k = identity ? conv2d_bn_silu_igemm_patch<BM, BN, WM, WN, WK, EPI_IDENTITY>
-                      : conv2d_bn_silu_igemm_patch<BM, BN, WM, WN, WK, EPI_FUSED>;
+    auto k = identity ? conv2d_bn_silu_igemm_patch<BM, BN, WM, WN, WK, RING, EPI_IDENTITY>
+                      : conv2d_bn_silu_igemm_patch<BM, BN, WM, WN, WK, RING, EPI_FUSED>;
     static size_t attr_bytes[2] = {0, 0};
     size_t& ab = attr_bytes[identity ? 1 : 0];
     if (lds > ab) {
@@ -470,15 +507,19 @@ int igemm_patch_choose(const ConvGeom& g) {
         // Two waves per K-group (one per SIMD) expose LDS latency: slower on
         // MI355X despite the lighter LDS traffic.
         const double occ = c.WK == 2 && c.WM * c.WN == 4 ? 1.0 : 1.3;
-        double cost = (double)per_cu * c.BM * c.BN * occ * (0.7 + lds);
+        // The dense patch stride costs 2-way bank conflicts on every pixel
+        // fragment read; a three-stage ring hides less filter latency.
+        const double conflicts = patch_layout(g, c).pstride == g.C_in * 2 + 16 ? 1.25 : 1.0;
+        const double ring = c.RING == 3 ? 1.05 : 1.0;
+        double cost = (double)per_cu * c.BM * c.BN * occ * conflicts * ring * (0.7 + lds);
         if (cost < best_cost * 0.999) { best = i; best_cost = cost; }
     }
     return best;
 }
 
-void igemm_patch_describe(int cfg, int* BM, int* BN, int* WM, int* WN, int* WK) {
+void igemm_patch_describe(int cfg, int* BM, int* BN, int* WM, int* WN, int* WK, int* ring) {
     const PatchCfg& c = kPatchCfgs[cfg];
-    *BM = c.BM; *BN = c.BN; *WM = c.WM; *WN = c.WN; *WK = c.WK;
+    *BM = c.BM; *BN = c.BN; *WM = c.WM; *WN = c.WN; *WK = c.WK; *ring = c.RING;
 }
 
 hipError_t launch_igemm_patch(const ConvGeom& g, int cfg, bool identity, const void* x,
@@ -486,9 +527,9 @@ hipError_t launch_igemm_patch(const ConvGeom& g, int cfg, bool identity, const v
                               hipStream_t s) {
     if (!igemm_patch_fits(g, cfg)) return hipErrorInvalidValue;
     int i = 0;
-#define X(bm, bn, wm, wn, wk)                                                                  \
-    if (cfg == i) return patch_launch_one<bm, bn, wm, wn, wk>(g, identity, x, w, scale, bias, \
-                                                              y, s);                          \
+#define X(bm, bn, wm, wn, wk, ring)                                                   \
+    if (cfg == i)                                                                       \
+        return patch_launch_one<bm, bn, wm, wn, wk, ring>(g, identity, x, w, scale, bias, y, s); \
     ++i;
     TG_PATCH_CFGS(X)
 #undef X

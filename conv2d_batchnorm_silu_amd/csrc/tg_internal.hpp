@@ -75,7 +75,7 @@ bool igemm_patch_serves(const ConvGeom& g);
 int igemm_patch_num_cfgs();
 bool igemm_patch_fits(const ConvGeom& g, int cfg);
 int igemm_patch_choose(const ConvGeom& g);
-void igemm_patch_describe(int cfg, int* BM, int* BN, int* WM, int* WN, int* WK);
+void igemm_patch_describe(int cfg, int* BM, int* BN, int* WM, int* WN, int* WK, int* ring);
 hipError_t launch_igemm_patch(const ConvGeom& g, int cfg, bool identity, const void* x,
                               const void* w, const float* scale, const float* bias, void* y,
                               hipStream_t s);

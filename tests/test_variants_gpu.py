@@ -192,7 +192,7 @@ PATCH_SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", [str(i) for i in range(8)])
+@pytest.mark.parametrize("cfg", [str(i) for i in range(10)])
 def test_patch_kernel(monkeypatch, cfg):
     monkeypatch.setenv("TG_CU", "0")
     monkeypatch.setenv("TG_IGEMM_RW", "0")
