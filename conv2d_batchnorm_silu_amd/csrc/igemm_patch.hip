@@ -155,12 +155,25 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
     // Chunk kc's filter loads; past the last chunk they read zeros (out of
     // the buffer's range) so that every step issues the same loads.
     auto issue = [&](int kc) {
-        const int tap = kc / cchunks, cc = kc - tap * cchunks;
-        const unsigned koff = kc < nk ? (unsigned)((tap * g.C_in + cc * 64) * 2) : 0x80000000u;
+        // Chunk kc is K range [64 kc, 64 kc + 64) (tap kc / cchunks, channel
+        // chunk kc % cchunks, since C_in = 64 cchunks): 128 bytes per chunk.
+        const unsigned koff = kc < nk ? (unsigned)kc * 128u : 0x80000000u;
         const unsigned dst = ring_lds + (unsigned)(kc % RING) * S::WSTAGE;
 #pragma unroll
         for (int i = 0; i < S::LI; ++i) pt_dma16(wrs, woff[i] + koff, dst + i * 1024);
     };
+    // BatchNorm constants of this wave's channels, fetched before the first
+    // filter load (so that the loader's exact vmcnt waits still hold: these
+    // older loads complete first) and kept in registers: read at the
+    // epilogue, their memory latency was most of its time.
+    float esc[S::FN][4], ebi[S::FN][4];
+#pragma unroll
+    for (int i = 0; i < S::FN; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            epi_consts<EPI>(scale, bias, n0 + wn * S::FN * 16 + i * 16 + lg * 4 + e, g.C_out,
+                            esc[i][e], ebi[i][e]);
+    asm volatile("" ::: "memory");
     for (int kc = 0; kc < RING - 1; ++kc) issue(kc);
 
     // Input patch: PR x PW pixels x C_in channels, zeros outside the image.
@@ -290,16 +303,16 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
     frag_wait(F0);
     // One step: refill the ring, fetch chunk kc+1's fragments into `nxt`,
     // run chunk kc's MFMAs from `cur`, then wait for the fetch (it overlaps
-    // the MFMAs). Stage (kc + 3) % 4 was last read for chunk kc - 1, whose
-    // fragment reads completed at the end of step kc - 2. The last step
-    // re-reads chunk kc (unused) so that every step has the same shape.
+    // the MFMAs). Stage (kc + RING - 1) % RING was last read for chunk
+    // kc - 1, whose fragment reads completed at the end of step kc - 2.
     auto step = [&](int kc, Frags& cur, Frags& nxt) {
         issue(kc + RING - 1);
-        const bool more = kc + 1 < nk;
-        const int tr = more ? tap_r : 0, ts = more ? tap_s : 0, c = more ? cc : 0;
-        advance();
         wait_chunk();
-        load(more ? kc + 1 : kc, tr, ts, c, nxt);
+        // Never issue reads whose results are dead: the compiler would hand
+        // their registers to other values, which the late LDS data would
+        // then overwrite.
+        if (kc + 1 < nk) load(kc + 1, tap_r, tap_s, cc, nxt);
+        advance();
         mma(cur);
         frag_wait(cur);
     };
@@ -310,7 +323,13 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
         step(kc, F0, F1);
         step(kc + 1, F1, F0);
     }
-    if (kc < nk) step(kc, F0, F1);
+    if (kc < nk) {  // odd last step: nothing left to fetch
+        issue(kc + RING - 1);
+        mma(F0);
+    }
+    // The last steps' filter loads (past the last chunk, zero-filling) land
+    // in the ring asynchronously: drain them before the ring's LDS is reused.
+    pt_wait_vmcnt<0>();
     pt_barrier();  // every wave is done with its ring and the patch: reuse LDS
 
     // WK = 2: the two K-groups share the epilogue. Group 0 owns fragment
@@ -339,16 +358,14 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
 #pragma unroll
         for (int i = 0; i < S::FN; ++i) {
             const int cb = wn * S::FN * 16 + i * 16 + lg * 4;
-            float sc[4], bi[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) epi_consts<EPI>(scale, bias, n0 + cb + e, g.C_out, sc[e], bi[e]);
 #pragma unroll
             for (int j = 0; j < S::FM; ++j) {
                 if (!owned(j)) continue;
                 const int pr = wm * S::FM * 16 + j * 16 + lr;
                 half4_t h;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) h[e] = (f16)epilogue<EPI>(acc[i][j][e], sc[e], bi[e]);
+                for (int e = 0; e < 4; ++e)
+                    h[e] = (f16)epilogue<EPI>(acc[i][j][e], esc[i][e], ebi[i][e]);
                 *(half4_t*)(out + pr * S::OROW + cb) = h;
             }
         }
