@@ -105,7 +105,7 @@ __device__ __forceinline__ int pt_wswz(int r) {
 }
 
 template <int BM, int BN, int WM, int WN, int WK, int RING, int EPI>
-__global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_patch(
+__global__ __launch_bounds__(64 * (WM * WN * WK + 1), 1) void conv2d_bn_silu_igemm_patch(
     const f16* __restrict__ x, const f16* __restrict__ w, const float* __restrict__ scale,
     const float* __restrict__ bias, f16* __restrict__ y, ConvGeom g, int tiles_per_img,
     int tiles_n, int PW, int pstride) {
@@ -133,8 +133,20 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
     const int cchunks = g.C_in / 64;
     const int nk = g.kh * g.kw * cchunks;
 
-    unsigned char* ring = pt_smem + wave * RING * S::WSTAGE;  // this wave's ring
-    unsigned char* patch = pt_smem + S::RING_BYTES;
+    // LDS: [patch-progress flag (16 B)][rings][patch]; the epilogue reuses
+    // all of it once the K loop is done.
+    int* pflag = (int*)pt_smem;  // filter rows whose patch rows have landed
+    unsigned char* ring = pt_smem + 16 + wave * RING * S::WSTAGE;  // this wave's ring
+    unsigned char* patch = pt_smem + 16 + S::RING_BYTES;
+    const unsigned patch_lds = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)patch));
+    // Compute waves: patch rows of filter row r are in LDS once the flag
+    // exceeds r.
+    auto wait_rows = [&](int r) {
+        while (__hip_atomic_load(pflag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) <= r)
+            __builtin_amdgcn_s_sleep(1);
+        asm volatile("" ::: "memory");
+    };
     const unsigned ring_lds = __builtin_amdgcn_readfirstlane(
         (unsigned)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)ring));
 
@@ -162,26 +174,19 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
 #pragma unroll
         for (int i = 0; i < S::LI; ++i) pt_dma16(wrs, woff[i] + koff, dst + i * 1024);
     };
-    // BatchNorm constants of this wave's channels, fetched before the first
-    // filter load (so that the loader's exact vmcnt waits still hold: these
-    // older loads complete first) and kept in registers: read at the
-    // epilogue, their memory latency was most of its time.
-    float esc[S::FN][4], ebi[S::FN][4];
-#pragma unroll
-    for (int i = 0; i < S::FN; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            epi_consts<EPI>(scale, bias, n0 + wn * S::FN * 16 + i * 16 + lg * 4 + e, g.C_out,
-                            esc[i][e], ebi[i][e]);
-    asm volatile("" ::: "memory");
-    for (int kc = 0; kc < RING - 1; ++kc) issue(kc);
+    if (wave < S::NW)
+        for (int kc = 0; kc < RING - 1; ++kc) issue(kc);
 
-    // Input patch: PR x PW pixels x C_in channels, zeros outside the image.
-    // Thread u copies 16-byte piece (u % upp) of pixels u/upp, u/upp + step,
-    // ... (64*NW is a multiple of upp = C_in/8, so the piece is fixed).
-    {
+    const int orows = p_last - p_first + 1;  // output rows of the tile
+
+    // Patch rows [0, orows) -- all that filter row 0 needs -- copied by the
+    // compute waves together: PR x PW pixels x C_in channels, zeros outside
+    // the image. Thread u copies 16-byte piece (u % upp) of pixels u/upp,
+    // u/upp + step, ... (64*NW is a multiple of upp = C_in/8, so the piece
+    // is fixed).
+    if (wave < S::NW) {
         const int upp = g.C_in / 8;
-        const int npx = PR * PW;
+        const int npx = orows * PW;
         const int step = 64 * S::NW / upp;
         const int piece = threadIdx.x % upp;
         int px = threadIdx.x / upp;
@@ -210,6 +215,44 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
                 if (dst[b] >= 0) *(half8_t*)(patch + dst[b]) = v[b];
         }
     }
+    if (threadIdx.x == 0) __hip_atomic_store(pflag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    __syncthreads();  // filter row 0's patch rows are in LDS
+
+    if (wave == S::NW) {
+        // ---------------- patch loader wave ----------------
+        // Filter row r (r >= 1) needs patch row orows + r - 1 as well: the
+        // remaining rows stream in that order while the K loop runs, one
+        // phase per filter row, each published once its loads have landed.
+        // A load instruction fills PPI whole patch pixels: lane l takes
+        // 16-byte piece l % PP of pixel l / PP (pieces past the C_in*2 data
+        // bytes and pixels outside the image read zeros).
+        const int PP = pstride / 16, PPI = 64 / PP;
+        const int lp = lane / PP, piece = lane - lp * PP;
+        const bool lane_on = lane < PPI * PP;
+        const bool data = piece * 16 < g.C_in * 2;
+        const u32x4_t xrs = pt_rsrc(x, (unsigned)g.N * (unsigned)g.H * (unsigned)g.W * (unsigned)g.C_in * 2u);
+        int cur = orows * PW;  // first pixel of the next load instruction
+        int pix = cur + lp, pr = pix / PW, pc = pix - (pix / PW) * PW;
+        for (int r = 1; r < g.kh; ++r) {
+            const int pend = (orows + r) * PW;
+            for (; cur < pend; cur += PPI) {
+                const int ih = p_first - g.pad + pr, iw = pc - g.pad;
+                const bool ok = data && (unsigned)ih < (unsigned)g.H && (unsigned)iw < (unsigned)g.W;
+                const unsigned off =
+                    ok ? (unsigned)((((n * g.H + ih) * g.W + iw) * g.C_in + piece * 8) * 2) : 0x80000000u;
+                if (lane_on && pix < PR * PW) pt_dma16(xrs, off, patch_lds + (unsigned)(cur * pstride));
+                pix += PPI;
+                pc += PPI;
+                while (pc >= PW) {
+                    pc -= PW;
+                    ++pr;
+                }
+            }
+            pt_wait_vmcnt<0>();
+            __hip_atomic_store(pflag, r + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        return;
+    }
 
     // Fragment addresses for tap (0, 0), channel piece lg: x operand (pixels)
     // from the patch, weight operand from the ring stage (ks = 1 is ks = 0
@@ -228,7 +271,6 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
         const int row = f * 16 + lr;
         bbase[f] = row * S::PPR * 16 + ((lg ^ pt_wswz<WK>(row)) * 16);
     }
-    pt_barrier();  // the patch is complete
 
     float4_t acc[S::FN][S::FM];
 #pragma unroll
@@ -260,8 +302,6 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
     // Chunk kc's filter data has landed once only the loads of the RING - 2
     // chunks issued after it are pending (chunks run RING - 1 ahead).
     auto wait_chunk = [&]() { pt_wait_vmcnt<(RING - 2) * S::LI>(); };
-    const unsigned patch_lds = __builtin_amdgcn_readfirstlane(
-        (unsigned)(uintptr_t)((__attribute__((address_space(3))) unsigned char*)patch));
     auto load = [&](int kc, int tr, int ts, int c, Frags& F) {
         const unsigned st = ring_lds + (unsigned)((kc % RING) * S::WSTAGE);
         const unsigned delta = (unsigned)((tr * PW + ts) * pstride + c * 128);
@@ -298,6 +338,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
     };
     Frags F0, F1;
     wait_chunk();
+    wait_rows(0);
     load(0, tap_r, tap_s, cc, F0);
     advance();
     frag_wait(F0);
@@ -311,7 +352,10 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
         // Never issue reads whose results are dead: the compiler would hand
         // their registers to other values, which the late LDS data would
         // then overwrite.
-        if (kc + 1 < nk) load(kc + 1, tap_r, tap_s, cc, nxt);
+        if (kc + 1 < nk) {
+            if (tap_s == 0 && cc == 0) wait_rows(tap_r);  // first chunk of a filter row
+            load(kc + 1, tap_r, tap_s, cc, nxt);
+        }
         advance();
         mma(cur);
         frag_wait(cur);
@@ -358,6 +402,9 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
 #pragma unroll
         for (int i = 0; i < S::FN; ++i) {
             const int cb = wn * S::FN * 16 + i * 16 + lg * 4;
+            float sc[4], bi[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) epi_consts<EPI>(scale, bias, n0 + cb + e, g.C_out, sc[e], bi[e]);
 #pragma unroll
             for (int j = 0; j < S::FM; ++j) {
                 if (!owned(j)) continue;
@@ -365,7 +412,7 @@ __global__ __launch_bounds__(64 * WM * WN * WK, 1) void conv2d_bn_silu_igemm_pat
                 half4_t h;
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    h[e] = (f16)epilogue<EPI>(acc[i][j][e], esc[i][e], ebi[i][e]);
+                    h[e] = (f16)epilogue<EPI>(acc[i][j][e], sc[e], bi[e]);
                 *(half4_t*)(out + pr * S::OROW + cb) = h;
             }
         }
@@ -435,7 +482,7 @@ size_t patch_lds_bytes_w(const ConvGeom& g, const PatchCfg& c, int pw, int pstri
     // Wave-private rings: WM*WN*WK waves x RING stages x (BN/WN rows x 128/WK bytes).
     const size_t ring = (size_t)c.WM * c.WN * c.WK * c.RING * (c.BN / c.WN) * (128 / c.WK);
     const size_t pr = (size_t)patch_rows_max(g, c.BM) + g.kh - 1;
-    const size_t patch = pr * (size_t)pw * (size_t)pstride;
+    const size_t patch = pr * (size_t)pw * (size_t)pstride + 16;  // + progress flag
     const size_t red =
         c.WK == 2 ? (size_t)c.WM * c.WN * (c.BN / c.WN / 16) * (c.BM / c.WM / 16) * 64 * 16 : 0;
     const size_t epi = red + (size_t)c.BM * (c.BN + 8) * 2;
@@ -479,7 +526,7 @@ hipError_t patch_launch_one(const ConvGeom& g, bool identity, const void* x, con
         if (e != hipSuccess) return e;
         ab = lds;
     }
-    hipLaunchKernelGGL(k, dim3(g.N * tiles_per_img * tiles_n), dim3(64 * S::NW), lds, s,
+    hipLaunchKernelGGL(k, dim3(g.N * tiles_per_img * tiles_n), dim3(64 * (S::NW + 1)), lds, s,
                        (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, tiles_per_img,
                        tiles_n, patch_layout(g, c).pw, patch_layout(g, c).pstride);
     return hipGetLastError();
@@ -492,14 +539,16 @@ int igemm_patch_num_cfgs() { return kNumPatchCfgs; }
 bool igemm_patch_fits(const ConvGeom& g, int cfg) {
     if (cfg < 0 || cfg >= kNumPatchCfgs) return false;
     const PatchCfg& c = kPatchCfgs[cfg];
-    // The patch copy gives each thread one fixed 16-byte channel piece.
+    // The cooperative patch copy gives each thread one fixed 16-byte piece.
     if ((64 * c.WM * c.WN * c.WK) % (g.C_in / 8) != 0) return false;
     return patch_lds_bytes(g, c) <= 160 * 1024;
 }
 
 bool igemm_patch_serves(const ConvGeom& g) {
     const long long xbytes = 2LL * g.N * g.H * g.W * g.C_in, wbytes = 2LL * g.C_out * g.K;
-    if (g.stride != 1 || g.C_in % 64 != 0 || g.C_in > 512 || xbytes >= (1LL << 31) ||
+    // C_in <= 448: a patch pixel (C_in*2 + 16 or + 32 bytes) fits one
+    // 1 KB load instruction of the loader wave.
+    if (g.stride != 1 || g.C_in % 64 != 0 || g.C_in > 448 || xbytes >= (1LL << 31) ||
         wbytes >= (1LL << 31))
         return false;
     for (int i = 0; i < kNumPatchCfgs; ++i)
