@@ -9,6 +9,12 @@
 // tap (9 or 49 times); here a workgroup's tile is BM consecutive output
 // pixels of one image, and the input rows they touch -- all C_in channels,
 // zero-padded at the image border -- are copied into LDS once:
+//   * the rows filter row 0 needs are copied by all compute waves before
+//     the K loop; each later filter row needs one more patch row, which a
+//     loader wave streams in with direct-to-LDS loads while the K loop runs
+//     and publishes through an LDS flag (at kernel start every workgroup
+//     wants its whole patch at once, so the copy was HBM-bound time with the
+//     matrix cores idle);
 //   * patch pixel stride is C_in*2 + 32 bytes (2 mod 4 16-byte units), which
 //     measured conflict-free on gfx950 for 16 consecutive pixels read at one
 //     channel piece -- no swizzle that would depend on the tap's shift (the
@@ -20,7 +26,7 @@
 //     a wave-uniform (r*PW + s)*stride: one add per fragment and tap;
 //   * only the filter chunks stream (64 channels of one tap). Each wave
 //     fetches the rows and the half (or whole) 128-byte chunk row its own
-//     fragments need into a wave-private 4-stage ring with direct-to-LDS
+//     fragments need into a wave-private 3- or 4-stage ring with direct-to-LDS
 //     loads (rows XOR-swizzled), so the main loop has no workgroup barrier:
 //     a wave waits only for its own loads, with an exact vmcnt; per-lane
 //     offsets are precomputed so that a chunk costs one add per load;
