@@ -175,11 +175,25 @@ tg_kernel dispatch(const ConvGeom& g, tg_dtype dt, tg_dispatch table) {
         if (g.C_out > 16 && tiled_serves(g, dt, nullptr)) return TG_KERNEL_TILED;
         return TG_KERNEL_SCALAR;
     }
-    // MI355X table: thresholds measured on MI355X (gfx950, ROCm 7.2) by timing
-    // every kernel that serves a shape and keeping the fastest.
+    // MI355X table, from timing every kernel that serves a shape over k in
+    // {1,3,5,7}, stride {1,2}, C_in {3,16,64,128}, C_out {8..256} at 10^5
+    // output pixels (sweep_dispatch.py; MI355X, gfx950, ROCm 7.2):
+    //  * C_in % 8 == 0: the implicit GEMM wins at every C_out (2.7-78x over
+    //    the tiled and scalar kernels from C_out 8 on), except 1x1 layers
+    //    with K < 32 and C_out <= 32, where the MFMA tiled kernel is 5-15%
+    //    faster;
+    //  * otherwise (RGB input): tiled wherever it fits, except 1x1 layers
+    //    beyond the MFMA tiled kernel's C_out <= 32, where the VALU tiled
+    //    kernel loses to the scalar one (1.3-1.75x); scalar past C_out 64.
     if (dt == TG_F32) return TG_KERNEL_SCALAR;
-    if (igemm_serves(g, dt) && g.C_out >= 16 && g.K >= 32) return TG_KERNEL_IGEMM;
-    if (tiled_serves(g, dt, nullptr)) return TG_KERNEL_TILED;
+    if (igemm_serves(g, dt)) {
+        if (g.K < 32 && tiled_mfma_serves(g) && tiled_serves(g, dt, nullptr)) return TG_KERNEL_TILED;
+        return TG_KERNEL_IGEMM;
+    }
+    if (tiled_serves(g, dt, nullptr)) {
+        if (g.kh * g.kw == 1 && !tiled_mfma_serves(g)) return TG_KERNEL_SCALAR;
+        return TG_KERNEL_TILED;
+    }
     return TG_KERNEL_SCALAR;
 }
 

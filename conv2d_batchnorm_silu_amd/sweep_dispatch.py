@@ -1,0 +1,142 @@
+"""Re-measure the shape -> kernel dispatch table on the GPU this runs on.
+
+Times every kernel that serves a shape (scalar, tiled, igemm, each forced)
+and the default dispatch over a grid of layer shapes, and writes one JSON
+line per shape plus a markdown summary: the fastest kernel, what the
+default table picks, and how far it is from the fastest. This is the
+measurement behind the default (MI355X) table in csrc/api.hip; the page's
+own thresholds ("Fusing an Epilogue", teenygrad docs, "Three kernels for one
+operation") were set on other hardware.
+
+Grid: k in {1, 3, 5, 7} (pad k//2), stride in {1, 2}, C_in in {3, 16, 64,
+128}, C_out in {8, 12, 16, 20, 24, 32, 48, 64, 128, 256}; N = 8 and H = W =
+112 (stride 1) or 224 (stride 2), i.e. 100,352 output pixels per channel.
+Inputs are device-side random fp16 tensors (correctness is the tests' job).
+
+    python -m conv2d_batchnorm_silu_amd.sweep_dispatch --out profiles/dispatch_sweep
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+KERNELS = ("scalar", "tiled", "igemm")
+SCALAR_MAX_GFLOP = 40.0  # the scalar kernel is not timed beyond this (seconds per shape)
+
+
+def shapes():
+    for k in (1, 3, 5, 7):
+        for s in (1, 2):
+            for cin in (3, 16, 64, 128):
+                for cout in (8, 12, 16, 20, 24, 32, 48, 64, 128, 256):
+                    hw = 112 if s == 1 else 224
+                    yield dict(N=8, H=hw, W=hw, C_in=cin, C_out=cout, k=k, stride=s, pad=k // 2)
+
+
+def time_plan(torch, plan, x, w, sc, bi, y, reps):
+    for _ in range(2):
+        plan.run(x, w, sc, bi, out=y)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        plan.run(x, w, sc, bi, out=y)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps  # us
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--out", default="dispatch_sweep", help="output path prefix (.jsonl, .md)")
+    ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--limit", type=int, default=0, help="only the first N shapes (0: all)")
+    args = ap.parse_args(argv)
+
+    import torch
+    from conv2d_batchnorm_silu_amd import binding as B
+
+    dev = torch.device("cuda")
+    rows = []
+    t_start = time.time()
+    for i, sh in enumerate(shapes()):
+        if args.limit and i >= args.limit:
+            break
+        N, H, W, cin, cout, k, s, p = (sh[a] for a in ("N", "H", "W", "C_in", "C_out", "k",
+                                                     "stride", "pad"))
+        P = (H + 2 * p - k) // s + 1
+        Q = (W + 2 * p - k) // s + 1
+        gflop = 2.0 * N * P * Q * cout * k * k * cin / 1e9
+        x = torch.randn(N, H, W, cin, device=dev, dtype=torch.float16)
+        w = (torch.randn(cout, k, k, cin, device=dev) / math.sqrt(k * k * cin)).half()
+        sc = torch.ones(cout, device=dev)
+        bi = torch.zeros(cout, device=dev)
+        y = torch.empty(N, P, Q, cout, device=dev, dtype=torch.float16)
+        row = dict(sh, gflop=round(gflop, 3), us={})
+        for kern in KERNELS + ("auto",):
+            if kern == "scalar" and gflop > SCALAR_MAX_GFLOP:
+                row["us"][kern] = None
+                continue
+            try:
+                plan = B.ConvBnSilu(N, H, W, cin, cout, k, k, s, p, "f16", kern)
+            except Exception:
+                row["us"][kern] = None  # the kernel does not serve this shape
+                continue
+            reps = args.reps if kern != "scalar" or gflop < 4 else 2
+            try:
+                row["us"][kern] = round(time_plan(torch, plan, x, w, sc, bi, y, reps), 2)
+            except Exception as e:  # a launch-time refusal (e.g. alignment): not served
+                print("[sweep] %s refused: %s" % (kern, e), flush=True)
+                row["us"][kern] = None
+                continue
+            if kern == "auto":
+                row["auto"] = B.kernel_name(plan.kernel)
+                row["auto_describe"] = plan.describe()
+        timed = {kk: v for kk, v in row["us"].items() if kk != "auto" and v is not None}
+        row["best"] = min(timed, key=timed.get)
+        row["auto_over_best"] = round(row["us"]["auto"] / timed[row["best"]], 3)
+        rows.append(row)
+        print("[sweep] %3d k=%d s=%d C_in=%3d C_out=%3d  %s  best=%s auto=%s (%.2fx)  %.0fs" % (
+            i, k, s, cin, cout, " ".join("%s=%s" % (kk, v) for kk, v in row["us"].items()),
+            row["best"], row["auto"], row["auto_over_best"], time.time() - t_start), flush=True)
+        del x, w, y
+        torch.cuda.empty_cache()
+
+    with open(args.out + ".jsonl", "w") as f:
+        for r in rows:
+            f.write(json.dumps(r) + "\n")
+    write_summary(rows, args.out + ".md")
+
+
+def write_summary(rows, path):
+    import torch
+    gpu = torch.cuda.get_device_name(0) if torch.cuda.is_available() else "?"
+    L = ["# Dispatch sweep: every kernel that serves a shape, timed on %s" % gpu,
+         "# command: python -m conv2d_batchnorm_silu_amd.sweep_dispatch --out profiles/dispatch_sweep",
+         "# times: us per launch (HIP events, back to back, same input); '-' = kernel does not serve "
+         "the shape or the scalar kernel was not timed (> %.0f GFLOP)" % SCALAR_MAX_GFLOP,
+         "",
+         "k | s | C_in | C_out | GFLOP | scalar | tiled | igemm | default picks | default / fastest"]
+    L.append("|".join(["---"] * 10))
+    for r in rows:
+        u = r["us"]
+        f = lambda v: "-" if v is None else "%.1f" % v
+        L.append("%d | %d | %d | %d | %.2f | %s | %s | %s | %s | %.2f" % (
+            r["k"], r["stride"], r["C_in"], r["C_out"], r["gflop"], f(u.get("scalar")),
+            f(u.get("tiled")), f(u.get("igemm")), r["auto"], r["auto_over_best"]))
+    within = sum(1 for r in rows if r["auto_over_best"] <= 1.10)
+    worst = sorted(rows, key=lambda r: -r["auto_over_best"])[:10]
+    L += ["", "default within 10%% of the fastest kernel on %d of %d shapes; worst:" % (
+        within, len(rows))]
+    for r in worst:
+        L.append("  k=%d s=%d C_in=%d C_out=%d: default %s %.2fx the fastest (%s)" % (
+            r["k"], r["stride"], r["C_in"], r["C_out"], r["auto"], r["auto_over_best"], r["best"]))
+    with open(path, "w") as f:
+        f.write("\n".join(L) + "\n")
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -110,6 +110,31 @@ def test_pages_dispatch_table():
     assert ch(32, k=3) == B.Kernel.TILED
 
 
+def test_mi355x_dispatch_table_regions():
+    """The MI355X table's measured regions (sweep over k, stride, C_in,
+    C_out at 10^5 output pixels): implicit GEMM for C_in % 8 == 0 except
+    1x1 layers with K < 32 and C_out <= 32 (MFMA tiled kernel); for RGB
+    input tiled, except 1x1 layers past C_out 32 (scalar)."""
+    ch = lambda ci, co, k=1, s=1: B.dispatch_choose(8, 112 * s, 112 * s, ci, co, k, k, s, k // 2,
+                                                    B.Dtype.F16, B.Table.MI355X)
+    for co in (8, 12, 16, 20, 24, 32):
+        assert ch(16, co) == B.Kernel.TILED, co      # K = 16 < 32
+    for co in (48, 64, 128, 256):
+        assert ch(16, co) == B.Kernel.IGEMM, co
+    for ci in (16, 64, 128):
+        for co in (8, 12):
+            for k in (3, 5, 7):
+                assert ch(ci, co, k) == B.Kernel.IGEMM, (ci, co, k)
+        assert ch(ci, 8, 1, 2) == (B.Kernel.TILED if ci == 16 else B.Kernel.IGEMM), ci
+    for co in (8, 16, 32):
+        assert ch(3, co) == B.Kernel.TILED, co
+    for co in (48, 64):
+        assert ch(3, co) == B.Kernel.SCALAR and ch(3, co, 1, 2) == B.Kernel.SCALAR, co
+        assert ch(3, co, 3) == B.Kernel.TILED and ch(3, co, 7, 2) == B.Kernel.TILED, co
+    for co in (128, 256):
+        assert ch(3, co, 3) == B.Kernel.SCALAR, co
+
+
 def test_mi355x_dispatch_table():
     for name, wl in WORKLOADS.items():
         dt = B.Dtype.F16 if wl.dtype == "f16" else B.Dtype.F32
