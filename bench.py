@@ -158,6 +158,12 @@ def bench_workload(torch, wl, steps, warmup, with_unfused=True):
         ums = time_plan(torch, up, sets, steps, warmup)
         row.update({"unfused_us": round(ums * 1e3, 2), "speedup_vs_unfused": round(ums / ms, 3),
                     "unfused_gbs_effective": round(traffic.unfused_bytes(wl) / ums / 1e6, 1)})
+        # Split form: the same conv kernel writing t1, then one bn+silu kernel.
+        sp = B.ConvBnSilu(wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride, wl.pad,
+                          wl.dtype, "split")
+        sms = time_plan(torch, sp, sets, steps, warmup)
+        row.update({"split_us": round(sms * 1e3, 2), "speedup_vs_split": round(sms / ms, 3),
+                    "split_gbs_effective": round(traffic.split_bytes(wl) / sms / 1e6, 1)})
     del sets
     torch.cuda.empty_cache()
     return row, d

@@ -33,6 +33,7 @@ class Kernel(enum.IntEnum):
     TILED = 2
     IGEMM = 3
     UNFUSED = 0x100
+    SPLIT = 0x200
 
 
 class Table(enum.IntEnum):
@@ -152,9 +153,10 @@ def _as_kernel(k) -> int:
         return int(k)
     names = {"auto": 0, "scalar": 1, "tiled": 2, "igemm": 3}
     s = str(k)
-    if s.startswith("unfused"):
-        inner = s[len("unfused"):].strip("_:()") or "auto"
-        return names[inner] | Kernel.UNFUSED
+    for prefix, flag in (("unfused", Kernel.UNFUSED), ("split", Kernel.SPLIT)):
+        if s.startswith(prefix):
+            inner = s[len(prefix):].strip("_:()") or "auto"
+            return names[inner] | flag
     return names[s]
 
 

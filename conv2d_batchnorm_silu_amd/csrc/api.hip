@@ -22,6 +22,7 @@ struct tg_conv_bn_silu_plan {
     tg_dtype dtype;
     int kernel;      // TG_KERNEL_SCALAR / TILED / IGEMM (resolved)
     bool unfused;
+    bool split;      // conv (identity epilogue) -> t1, then one bn+silu kernel
     bool forced;     // kernel was requested explicitly (alignment errors instead of fallback)
     int igemm_cfg;   // index into the igemm variant table (-1: register-weights variant)
     int dma_cfg;     // >= 0: direct-to-LDS pipelined variant with this tile
@@ -36,7 +37,7 @@ struct tg_conv_bn_silu_plan {
     int stem_wpc;    // > 0: stem kernel with this many workgroups per CU
     int stem_rows;   // ... and bands of this many output rows
     TiledCfg tiled;
-    size_t ws_bytes;  // unfused only
+    size_t ws_bytes;  // unfused and split only
 };
 
 namespace {
@@ -213,7 +214,9 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
     if (table != TG_DISPATCH_MI355X && table != TG_DISPATCH_PAGES) return TG_ERR_UNSUPPORTED;
     int kv = (int)kernel;
     bool unfused = (kv & TG_UNFUSED) != 0;
-    int base = kv & ~TG_UNFUSED;
+    bool split = (kv & TG_SPLIT) != 0;
+    if (unfused && split) return TG_ERR_UNSUPPORTED;
+    int base = kv & ~(TG_UNFUSED | TG_SPLIT);
     if (base < TG_KERNEL_AUTO || base > TG_KERNEL_IGEMM) return TG_ERR_UNSUPPORTED;
 
     tg_conv_bn_silu_plan p;
@@ -221,6 +224,7 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
     p.g = g;
     p.dtype = dtype;
     p.unfused = unfused;
+    p.split = split;
     p.forced = base != TG_KERNEL_AUTO;
     p.dma_cfg = -1;
     p.patch_cfg = -1;
@@ -278,7 +282,7 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
         }
     }
     size_t ysz = (size_t)g.M * g.C_out * (dtype == TG_F16 ? 2 : 4);
-    p.ws_bytes = unfused ? 2 * round256(ysz) : 0;
+    p.ws_bytes = unfused ? 2 * round256(ysz) : (split ? round256(ysz) : 0);
 
     tg_conv_bn_silu_plan* h = new (std::nothrow) tg_conv_bn_silu_plan(p);
     if (!h) return TG_ERR_UNSUPPORTED;
@@ -328,17 +332,17 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, c
     }
     void* conv_out = y;
     void* t2 = nullptr;
-    if (plan->unfused) {
+    if (plan->unfused || plan->split) {
         if (!workspace || workspace_bytes < plan->ws_bytes) return TG_ERR_WORKSPACE;
         size_t ysz = (size_t)g.M * g.C_out * (f32 ? 4 : 2);
         conv_out = workspace;
-        t2 = (char*)workspace + round256(ysz);
+        if (plan->unfused) t2 = (char*)workspace + round256(ysz);
         if (kernel != TG_KERNEL_SCALAR && !aligned16(workspace)) {
             if (plan->forced) return TG_ERR_ALIGNMENT;
             kernel = TG_KERNEL_SCALAR;
         }
     }
-    bool identity = plan->unfused;
+    bool identity = plan->unfused || plan->split;
     hipError_t e;
     switch (kernel) {
         case TG_KERNEL_IGEMM:
@@ -388,6 +392,10 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, c
         if (e != hipSuccess) return TG_ERR_HIP;
         e = launch_silu_apply(f32, t2, y, total, s);
         if (e != hipSuccess) return TG_ERR_HIP;
+    } else if (plan->split) {
+        long long total = (long long)g.M * g.C_out;
+        e = launch_bn_silu_apply(f32, conv_out, bn_scale, bn_bias, y, total, g.C_out, s);
+        if (e != hipSuccess) return TG_ERR_HIP;
     }
     return TG_OK;
 }
@@ -406,7 +414,9 @@ tg_status tg_conv_bn_silu_query(const tg_conv_bn_silu_plan* plan, int* P, int* Q
     if (!plan) return TG_ERR_INVALID_ARGUMENT;
     if (P) *P = plan->g.P;
     if (Q) *Q = plan->g.Q;
-    if (chosen) *chosen = (tg_kernel)(plan->kernel | (plan->unfused ? TG_UNFUSED : 0));
+    if (chosen)
+        *chosen = (tg_kernel)(plan->kernel | (plan->unfused ? TG_UNFUSED : 0) |
+                              (plan->split ? TG_SPLIT : 0));
     if (workspace_bytes) *workspace_bytes = plan->ws_bytes;
     return TG_OK;
 }
@@ -457,7 +467,7 @@ tg_status tg_conv_bn_silu_describe(const tg_conv_bn_silu_plan* plan, char* buf, 
         snprintf(k, sizeof(k), "scalar grid=%d", (g.M * g.C_out + 255) / 256);
     }
     snprintf(buf, len, "%s%s %s N=%d H=%d W=%d C_in=%d C_out=%d k=%dx%d s=%d p=%d -> %dx%d",
-             plan->unfused ? "unfused:" : "", k, plan->dtype == TG_F16 ? "f16" : "f32", g.N, g.H,
+             plan->unfused ? "unfused:" : (plan->split ? "split:" : ""), k, plan->dtype == TG_F16 ? "f16" : "f32", g.N, g.H,
              g.W, g.C_in, g.C_out, g.kh, g.kw, g.stride, g.pad, g.P, g.Q);
     return TG_OK;
 }
@@ -488,12 +498,16 @@ const char* tg_status_string(tg_status s) {
 
 const char* tg_kernel_name(tg_kernel k) {
     int kv = (int)k;
-    bool unf = (kv & TG_UNFUSED) != 0;
-    switch (kv & ~TG_UNFUSED) {
-        case TG_KERNEL_AUTO: return unf ? "unfused(auto)" : "auto";
-        case TG_KERNEL_SCALAR: return unf ? "unfused(scalar)" : "conv2d_bn_silu_scalar";
-        case TG_KERNEL_TILED: return unf ? "unfused(tiled)" : "conv2d_bn_silu_tiled";
-        case TG_KERNEL_IGEMM: return unf ? "unfused(igemm)" : "conv2d_bn_silu_igemm";
+    bool unf = (kv & TG_UNFUSED) != 0, spl = (kv & TG_SPLIT) != 0;
+    if (unf && spl) return "unknown kernel";
+    switch (kv & ~(TG_UNFUSED | TG_SPLIT)) {
+        case TG_KERNEL_AUTO: return unf ? "unfused(auto)" : (spl ? "split(auto)" : "auto");
+        case TG_KERNEL_SCALAR:
+            return unf ? "unfused(scalar)" : (spl ? "split(scalar)" : "conv2d_bn_silu_scalar");
+        case TG_KERNEL_TILED:
+            return unf ? "unfused(tiled)" : (spl ? "split(tiled)" : "conv2d_bn_silu_tiled");
+        case TG_KERNEL_IGEMM:
+            return unf ? "unfused(igemm)" : (spl ? "split(igemm)" : "conv2d_bn_silu_igemm");
     }
     return "unknown kernel";
 }

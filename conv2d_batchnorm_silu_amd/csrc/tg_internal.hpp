@@ -100,6 +100,9 @@ hipError_t launch_tiled_mfma_pipe(const ConvGeom& g, int R, int grid, bool ident
 hipError_t launch_bn_apply(bool f32, const void* t1, const float* scale, const float* bias, void* t2,
                            long long total, int C, hipStream_t s);
 hipError_t launch_silu_apply(bool f32, const void* t2, void* y, long long total, hipStream_t s);
+// Split form: y = silu(t1 * scale[c] + bias[c]) in one streaming kernel.
+hipError_t launch_bn_silu_apply(bool f32, const void* t1, const float* scale, const float* bias,
+                                void* y, long long total, int C, hipStream_t s);
 hipError_t launch_bn_fold(const float* gamma, const float* beta, const float* mean,
                           const float* var, float eps, int C, float* scale, float* bias,
                           hipStream_t s);

@@ -56,6 +56,14 @@ def unfused_bytes(wl) -> int:
                                                    ELEM_BYTES[wl.dtype])
 
 
+def split_bytes(wl) -> int:
+    """conv writes t1, one bn+silu kernel reads t1 and writes y: one
+    intermediate of y's shape and dtype is added."""
+    b = workload_bytes(wl)
+    return fused_bytes(wl) + intermediate_bytes(b["y"] // ELEM_BYTES[wl.dtype],
+                                                ELEM_BYTES[wl.dtype])
+
+
 def conv_flops(wl) -> int:
     """2 * M * K * C_out with M = N*P*Q and K = kh*kw*C_in (unpadded K)."""
     return 2 * wl.N * wl.P * wl.Q * wl.kh * wl.kw * wl.C_in * wl.C_out

@@ -60,7 +60,11 @@ typedef enum { TG_F16 = 0, TG_F32 = 1 } tg_dtype;
  * by shape). A value may be OR-ed with TG_UNFUSED to run the three-kernel
  * baseline instead: that conv kernel with an identity epilogue writing t1,
  * then a BatchNorm kernel t1 -> t2, then a SiLU kernel t2 -> y ("The problem"
- * section of the same page). */
+ * section of the same page). Or it may be OR-ed with TG_SPLIT for the split
+ * form that "When not to fuse" (same page) and "Kernel Fusion: When to Fuse
+ * and When Not To" (section on when fusion does not pay) weigh against the
+ * fused one: the conv kernel with an identity epilogue writing t1, then one
+ * BatchNorm+SiLU kernel t1 -> y. TG_UNFUSED and TG_SPLIT exclude each other. */
 typedef enum {
     TG_KERNEL_AUTO = 0,   /* the dispatch table decides (see tg_dispatch_choose) */
     TG_KERNEL_SCALAR = 1, /* one output element per lane; any shape, fp16 and fp32 */
@@ -68,7 +72,8 @@ typedef enum {
                              C_out <= 64, padded input row band must fit in LDS */
     TG_KERNEL_IGEMM = 3,  /* implicit GEMM on fp16 MFMA with the epilogue in registers;
                              fp16, C_in % 8 == 0 */
-    TG_UNFUSED = 0x100    /* flag: run conv, bn and silu as three kernels */
+    TG_UNFUSED = 0x100,   /* flag: run conv, bn and silu as three kernels */
+    TG_SPLIT = 0x200      /* flag: run conv, then bn+silu, as two kernels */
 } tg_kernel;
 
 /* Dispatch tables. TG_DISPATCH_MI355X (default) holds thresholds measured on
@@ -99,12 +104,13 @@ tg_status tg_conv_bn_silu_create_with_table(tg_conv_bn_silu_plan **out, int N, i
 /* Run the planned operation on `stream`. x, w, y: device pointers in the
  * plan's dtype and the layouts above; bn_scale, bn_bias: device fp32
  * [C_out] (from tg_bn_fold). workspace/workspace_bytes: device scratch for the
- * unfused baseline only (two intermediates t1 and t2 of y's size; see
- * tg_conv_bn_silu_query), ignored and may be NULL/0 for fused kernels.
+ * unfused baseline (two intermediates t1 and t2 of y's size) and the split
+ * form (one intermediate t1); see tg_conv_bn_silu_query. Ignored and may be
+ * NULL/0 for fused kernels. The workspace must not alias x, w or y.
  * Errors: TG_ERR_INVALID_ARGUMENT for a NULL plan or data pointer;
  * TG_ERR_ALIGNMENT when a forced tiled/igemm plan gets x, w or y not 16-byte
  * aligned (an AUTO plan falls back to the scalar kernel instead);
- * TG_ERR_WORKSPACE when the unfused workspace is NULL or too small;
+ * TG_ERR_WORKSPACE when the unfused or split workspace is NULL or too small;
  * TG_ERR_HIP when a launch fails. Nothing is launched on error. */
 tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan *plan, const void *x, const void *w,
                               const float *bn_scale, const float *bn_bias, void *y,
@@ -125,7 +131,7 @@ tg_status tg_bn_fold(const float *gamma, const float *beta, const float *mean, c
                      float eps, int C_out, float *bn_scale, float *bn_bias, void *stream);
 
 /* Describe a plan: output extent, the kernel run() will launch (for aligned
- * pointers; may include TG_UNFUSED) and the workspace it needs. Any out
+ * pointers; may include TG_UNFUSED or TG_SPLIT) and the workspace it needs. Any out
  * pointer may be NULL. TG_ERR_INVALID_ARGUMENT for a NULL plan. */
 tg_status tg_conv_bn_silu_query(const tg_conv_bn_silu_plan *plan, int *P, int *Q,
                                 tg_kernel *chosen, size_t *workspace_bytes);

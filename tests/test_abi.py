@@ -176,10 +176,31 @@ def test_bn_fold_argument_errors(lib):
     assert f(a, a, a, a, float("nan"), 4, a, a, None) == INVAL
 
 
+def test_split_workspace_size(lib):
+    """Split form (conv -> t1, then one bn+silu kernel): one intermediate."""
+    wl = WORKLOADS["conv3x3_c128_k128"]
+    st, h = _create(lib, wl.N, wl.H, wl.W, wl.C_in, wl.C_out, 3, 3, 1, 1, kernel=0x200)
+    assert st == OK
+    k, ws = ctypes.c_int(), ctypes.c_size_t()
+    lib.tg_conv_bn_silu_query(h, None, None, ctypes.byref(k), ctypes.byref(ws))
+    ybytes = wl.N * wl.P * wl.Q * wl.C_out * 2
+    assert ws.value == (ybytes + 255) // 256 * 256
+    assert k.value == (3 | 0x200)
+    buf = ctypes.create_string_buffer(256)
+    assert lib.tg_conv_bn_silu_describe(h, buf, 256) == OK
+    assert buf.value.decode().startswith("split:")
+    lib.tg_conv_bn_silu_destroy(h)
+    # the two baselines exclude each other
+    st, h = _create(lib, wl.N, wl.H, wl.W, wl.C_in, wl.C_out, 3, 3, 1, 1, kernel=0x300)
+    assert st == 2 and not h
+
+
 def test_strings(lib):
     for s in range(6):
         assert B.status_string(s)
     assert B.status_string(99) == "unknown status"
     assert B.kernel_name(3) == "conv2d_bn_silu_igemm"
     assert B.kernel_name(3 | 0x100) == "unfused(igemm)"
+    assert B.kernel_name(1 | 0x200) == "split(scalar)"
+    assert B.kernel_name(3 | 0x300) == "unknown kernel"
     assert B.kernel_name(77) == "unknown kernel"

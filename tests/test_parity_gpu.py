@@ -53,7 +53,7 @@ def test_bn_fold_matches_definition():
     np.testing.assert_allclose(bi.cpu().numpy(), b64 - m64 * s_ref, rtol=0, atol=3e-7)
 
 
-KERNELS = ["auto", "scalar", "tiled", "igemm", "unfused"]
+KERNELS = ["auto", "scalar", "tiled", "igemm", "unfused", "split"]
 
 
 @pytest.mark.parametrize("kernel", KERNELS)
@@ -68,7 +68,7 @@ def test_workload(name, kernel):
 SMALL = random_small_workloads(40, seed=123)
 
 
-@pytest.mark.parametrize("kernel", ["scalar", "tiled", "igemm", "unfused"])
+@pytest.mark.parametrize("kernel", ["scalar", "tiled", "igemm", "unfused", "split"])
 def test_random_small_shapes(kernel):
     ran = 0
     for wl in SMALL:
@@ -113,16 +113,18 @@ def test_edge_shapes(wl, kernel):
 def test_fused_matches_gpu_unfused_and_scalar(name):
     """Full-size cross-check of every output: the dispatched fused kernel
     against the unfused three-kernel baseline (same conv mainloop; differs only
-    by fp16 rounding of t1 and t2) and against the scalar kernel."""
+    by fp16 rounding of t1 and t2), the split two-kernel form (rounding of t1)
+    and the scalar kernel."""
     wl = WORKLOADS[name]
     d = make_inputs(wl)
     t = to_device(d)
     sb = fold(t)
     _, y = run_plan(wl, t, "auto", scale_bias=sb)
     _, yu = run_plan(wl, t, "unfused", scale_bias=sb)
+    _, ysp = run_plan(wl, t, "split", scale_bias=sb)
     _, ys = run_plan(wl, t, "scalar", scale_bias=sb)
     yf = y.float()
-    for other, what in ((yu.float(), "unfused"), (ys.float(), "scalar")):
+    for other, what in ((yu.float(), "unfused"), (ysp.float(), "split"), (ys.float(), "scalar")):
         err = ((yf - other).abs() / other.abs().clamp(min=1.0)).max().item()
         note("%s fused vs %s: max scaled diff %.3g" % (name, what, err))
         assert err <= 1e-2
