@@ -137,13 +137,13 @@ def cpu_baseline(wl, d, budget_s=12.0):
                 n, wl.N, wl.name, reps, dt, threads, reps * traffic.conv_flops(sub) / dt / 1e9)}
 
 
-def bench_workload(torch, wl, steps, warmup, with_unfused=True):
+def bench_workload(torch, wl, steps, warmup, with_unfused=True, plan_kind="auto"):
     from conv2d_batchnorm_silu_amd import binding as B, traffic
     from conv2d_batchnorm_silu_amd.inputs import make_inputs
     d = make_inputs(wl)
     sets = Sets(torch, wl, d)
     plan = B.ConvBnSilu(wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride, wl.pad,
-                        wl.dtype, "auto")
+                        wl.dtype, plan_kind)
     ms = time_plan(torch, plan, sets, steps, warmup)
     fb, fl = traffic.fused_bytes(wl), traffic.conv_flops(wl)
     bound, ai = binding_roof(wl)
@@ -178,6 +178,8 @@ def main():
     ap.add_argument("--only", action="store_true",
                     help="time only the headline workload's fused kernel (for profiling)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--plan", default="auto",
+                    help="with --only: the plan to time (auto, split, unfused, scalar, ...)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -195,7 +197,8 @@ def main():
     log("device:", torch.cuda.get_device_name(0), "| torch", torch.__version__)
 
     if args.only:
-        row, d = bench_workload(torch, head, args.steps, args.warmup, with_unfused=False)
+        row, d = bench_workload(torch, head, args.steps, args.warmup, with_unfused=False,
+                                plan_kind=args.plan)
         log(json.dumps(row))
         print(json.dumps({"metric": METRIC, "workload": head.name, "row": row}))
         return

@@ -1,0 +1,316 @@
+"""Regenerate the rocprofv3 summaries committed under profiles/ (GPU host only).
+
+    python -m conv2d_batchnorm_silu_amd.make_profiles --raw gpurun_out/prof \
+        [--traces] [--split] [--counters] [--workloads W1,W2]
+
+* ``--traces``: one ``--kernel-trace --stats`` run of ``bench.py --only`` per
+  workload -> ``profiles/kernel_trace_<workload>.txt`` (average duration of
+  the fused kernel per launch, with its algorithmic GB/s and TFLOP/s).
+* ``--split``: the same for the fused, split (conv kernel, then one
+  BatchNorm+SiLU kernel) and unfused (conv, BatchNorm, SiLU) plans of every
+  fp16 workload, with each kernel's registers and LDS from the trace ->
+  ``profiles/fused_vs_split.md``.
+* ``--counters``: ``FETCH_SIZE`` and ``WRITE_SIZE`` (each in its own
+  ``--pmc`` run) of the headline's fused kernel and of a plain device copy of
+  known size (``copy_calibration.py``), which gives the scale of each counter
+  -> ``profiles/counters.json`` and ``profiles/hbm_traffic_<workload>.txt``.
+
+Raw rocprofv3 output stays under ``--raw``. Every profiled program is run as
+``rocprofv3 ... -- python3 <script>`` from /tmp with TMPDIR=/tmp; this
+process itself never touches the GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import glob
+import json
+import os
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+PROFILES = os.path.join(ROOT, "profiles")  # --dest overrides
+REUSE = False  # --reuse: summarise raw output already under --raw, run nothing
+sys.path.insert(0, ROOT)
+
+from conv2d_batchnorm_silu_amd import profiling, traffic  # noqa: E402
+from conv2d_batchnorm_silu_amd.inputs import HEADLINE, WORKLOADS  # noqa: E402
+
+BENCH = os.path.join(ROOT, "bench.py")
+COPY = os.path.join(PKG, "copy_calibration.py")
+
+
+def log(msg):
+    print("[make_profiles] " + msg, flush=True)
+
+
+def run_profiled(raw, name, prof_args, prog_args, limit):
+    """rocprofv3 <prof_args> -d raw/name -o run -- python3 <prog_args>; the
+    whole command under `timeout -s KILL limit`. Returns the output dir.
+    rocprofv3 may end with a signal after a complete run, so success is
+    judged by the CSV it leaves."""
+    out = os.path.join(raw, name)
+    if REUSE:
+        return out
+    cmd = (["timeout", "-s", "KILL", str(limit), "rocprofv3"] + prof_args +
+           ["-f", "csv", "-d", out, "-o", "run", "--", "python3"] + prog_args)
+    env = dict(os.environ, TMPDIR="/tmp")
+    log("run %s: %s" % (name, " ".join(cmd)))
+    with open(os.path.join(raw, name + ".log"), "w") as f:
+        rc = subprocess.run(cmd, cwd="/tmp", env=env, stdout=f, stderr=subprocess.STDOUT).returncode
+    log("%s finished, status %d" % (name, rc))
+    if rc in (124, 137) or rc == -9:
+        raise RuntimeError("%s hit its time limit" % name)
+    return out
+
+
+def find_csv(out, suffix):
+    hits = sorted(glob.glob(os.path.join(out, "**", "*" + suffix), recursive=True))
+    if not hits:
+        raise RuntimeError("no %s under %s" % (suffix, out))
+    return hits[-1]
+
+
+def cmd_text(prof_args, prog_args):
+    rel = [a.replace(ROOT, "<repo>") for a in prog_args]
+    return "cd /tmp && rocprofv3 %s -f csv -d <out> -o run -- python3 %s" % (
+        " ".join(prof_args), " ".join(rel))
+
+
+def fused_row(stats):
+    """The fused conv kernel of a bench --only run: the most-called kernel
+    whose name is one of this library's conv kernels."""
+    rows = [r for r in stats if "conv2d_bn_silu" in r["name"]]
+    return max(rows, key=lambda r: r["calls"])
+
+
+def write_trace(raw, wl):
+    prof = ["--kernel-trace", "--stats", "-T"]
+    prog = [BENCH, "--only", "--workload", wl.name, "--steps", "50", "--warmup", "5"]
+    out = run_profiled(raw, "trace_" + wl.name, prof, prog, 180)
+    stats = profiling.kernel_stats(find_csv(out, "_kernel_stats.csv"))
+    fb, fl = traffic.fused_bytes(wl), traffic.conv_flops(wl)
+    lines = ["# rocprofv3 kernel-trace summary: fused conv2d+BN+SiLU, workload %s" % wl.name,
+             "# shape: N=%d H=%d W=%d C_in=%d C_out=%d k=%dx%d s=%d p=%d (%s)" % (
+                 wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride, wl.pad, wl.dtype),
+             "# command: " + cmd_text(prof, prog),
+             "# algorithmic bytes per launch %d, conv FLOP per launch %d" % (fb, fl),
+             "# kernel | calls | avg us | min us | max us | % of GPU time | "
+             "GB/s (algorithmic, avg) | TFLOP/s (avg)"]
+    fr = fused_row(stats)
+    for r in stats:
+        cells = [r["name"][:110], str(r["calls"]), "%.2f" % (r["avg_ns"] / 1e3),
+                 "%.2f" % (r["min_ns"] / 1e3), "%.2f" % (r["max_ns"] / 1e3), "%.1f" % r["pct"]]
+        if r is fr:
+            cells += ["%.1f" % (fb / r["avg_ns"]), "%.2f" % (fl / r["avg_ns"] / 1e3)]
+        lines.append(" | ".join(cells))
+    path = os.path.join(PROFILES, "kernel_trace_%s.txt" % wl.name)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("wrote " + path)
+    return fr
+
+
+def compiler_resources():
+    """Kernel symbol -> dict of VGPRs, AGPRs, SGPRs, spills, static LDS and
+    scratch bytes, from the code-object metadata of each source compiled to
+    gfx950 assembly with the library's own flags (host-side: hipcc only)."""
+    import concurrent.futures as cf
+    import re
+    import tempfile
+    from conv2d_batchnorm_silu_amd import build as Bld
+
+    def one(src):
+        with tempfile.TemporaryDirectory(prefix="tg_res_") as d:
+            out = os.path.join(d, "k.s")
+            r = subprocess.run([Bld.hipcc()] + Bld.HIPCC_FLAGS +
+                               ["--cuda-device-only", "-S", src, "-o", out],
+                               capture_output=True, text=True)
+            if r.returncode != 0:
+                raise RuntimeError("hipcc failed for %s" % src)
+            return open(out).read()
+
+    res = {}
+    with cf.ThreadPoolExecutor(max_workers=8) as ex:
+        for asm in ex.map(one, Bld.sources()):
+            meta = asm[asm.find("amdhsa.kernels:"):]
+            for blk in re.split(r"\n  - ", meta)[1:]:
+                kv = dict(re.findall(r"\.([a-z_]+):\s+(\S+)", blk))
+                if "name" not in kv:
+                    continue
+                res[kv["name"]] = {k: kv.get(k, "n/a") for k in (
+                    "vgpr_count", "agpr_count", "sgpr_count", "vgpr_spill_count",
+                    "sgpr_spill_count", "group_segment_fixed_size",
+                    "private_segment_fixed_size")}
+    return res
+
+
+def lookup(res, name):
+    for sym, v in res.items():
+        if sym.startswith(name) or name.startswith(sym):
+            return v
+    return None
+
+
+def write_split(raw, names):
+    prof = ["--kernel-trace", "--stats", "-T"]
+    res = compiler_resources()
+    lines = ["# Fused vs split vs unfused, per workload (one MI355X)",
+             "",
+             "Split = the conv kernel with an identity epilogue writing t1 (fp16), then one "
+             "BatchNorm+SiLU streaming kernel; unfused = conv, BatchNorm, SiLU as three kernels. "
+             "Durations are rocprofv3 kernel-trace averages per launch (kernel time only, no "
+             "launch gaps); the sum over a plan's kernels is its GPU time per step. Registers, "
+             "spills, static LDS and scratch come from the code-object metadata of the "
+             "library's gfx950 build (dynamic LDS is requested per launch by the plan and is "
+             "not included); VGPR+AGPR sets the waves a SIMD can hold (512 registers per "
+             "lane: 2 waves at 256, 3 at 168, 4 at 128).",
+             "",
+             "command per workload W and plan K: " +
+             cmd_text(prof, [BENCH, "--only", "--workload", "W", "--plan", "K", "--steps", "50",
+                             "--warmup", "5"]),
+             ""]
+    for name in names:
+        wl = WORKLOADS[name]
+        lines += ["## %s (%s)" % (name, "N=%d %dx%d C_in=%d -> C_out=%d, %dx%d s%d p%d" % (
+            wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride, wl.pad)), "",
+                  "plan | kernel | calls | avg us | VGPR | AGPR | SGPR | spills (V/S) | "
+                  "static LDS B | scratch B",
+                  "---|---|---|---|---|---|---|---|---|---"]
+        totals = {}
+        for kind in ("auto", "split", "unfused"):
+            prog = [BENCH, "--only", "--workload", name, "--plan", kind, "--steps", "50",
+                    "--warmup", "5"]
+            out = run_profiled(raw, "split_%s_%s" % (name, kind), prof, prog, 180)
+            stats = profiling.kernel_stats(find_csv(out, "_kernel_stats.csv"))
+            calls = max(r["calls"] for r in stats if "conv2d_bn_silu" in r["name"])
+            tot = 0.0
+            for r in stats:
+                # the plan's own kernels: launched once per step
+                if r["calls"] != calls:
+                    continue
+                v = lookup(res, r["name"]) or {}
+                g = lambda k: v.get(k, "n/a")
+                lines.append("%s | %s | %d | %.2f | %s | %s | %s | %s/%s | %s | %s" % (
+                    "fused" if kind == "auto" else kind, r["name"][:90], r["calls"],
+                    r["avg_ns"] / 1e3, g("vgpr_count"), g("agpr_count"), g("sgpr_count"),
+                    g("vgpr_spill_count"), g("sgpr_spill_count"),
+                    g("group_segment_fixed_size"), g("private_segment_fixed_size")))
+                tot += r["avg_ns"] / 1e3
+            totals[kind] = tot
+        lines += ["", "GPU time per step: fused %.2f us, split %.2f us (%.2fx), unfused %.2f us "
+                  "(%.2fx)" % (totals["auto"], totals["split"], totals["split"] / totals["auto"],
+                               totals["unfused"], totals["unfused"] / totals["auto"]), ""]
+    path = os.path.join(PROFILES, "fused_vs_split.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("wrote " + path)
+
+
+def write_counters(raw, wl, source_hash):
+    prog = [BENCH, "--only", "--workload", wl.name, "--steps", "20", "--warmup", "2"]
+    val = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        out = run_profiled(raw, "pmc_%s_%s" % (counter.lower(), wl.name), ["--pmc", counter],
+                           prog, 60)
+        path = find_csv(out, "_counter_collection.csv")
+        with open(path) as f:
+            names = collections.Counter(r["Kernel_Name"] for r in csv.DictReader(f)
+                                        if "conv2d_bn_silu" in r["Kernel_Name"])
+        sym = names.most_common(1)[0][0]
+        v, n = profiling.counter_per_dispatch(path, sym, counter)
+        cout = run_profiled(raw, "pmc_%s_copy" % counter.lower(), ["--pmc", counter], [COPY], 60)
+        cpath = find_csv(cout, "_counter_collection.csv")
+        cv, cn = profiling.counter_per_dispatch(cpath, "copy", counter)
+        if cv is None:  # the copy kernel's name varies between torch builds
+            cv, cn = profiling.counter_per_dispatch(cpath, "", counter)
+        from conv2d_batchnorm_silu_amd.copy_calibration import COPY_BYTES
+        scale = COPY_BYTES / (cv * 1024.0)
+        val[counter] = dict(raw_kib=v, dispatches=n, copy_kib=cv, scale=scale, symbol=sym,
+                            bytes=v * 1024.0 * scale)
+    b = traffic.workload_bytes(wl)
+    alg = traffic.fused_bytes(wl)
+    hbm = val["FETCH_SIZE"]["bytes"] + val["WRITE_SIZE"]["bytes"]
+    sym = val["FETCH_SIZE"]["symbol"]
+    entry = {"source_hash": source_hash, "kernel_symbol": sym,
+             "fetch_kib_raw": val["FETCH_SIZE"]["raw_kib"],
+             "write_kib_raw": val["WRITE_SIZE"]["raw_kib"],
+             "fetch_scale": val["FETCH_SIZE"]["scale"], "write_scale": val["WRITE_SIZE"]["scale"],
+             "fetch_bytes": val["FETCH_SIZE"]["bytes"], "write_bytes": val["WRITE_SIZE"]["bytes"],
+             "hbm_bytes_per_launch": int(round(hbm)), "algorithmic_bytes": alg,
+             "excess_frac": hbm / alg - 1.0}
+    cpath = os.path.join(PROFILES, "counters.json")
+    try:
+        with open(cpath) as f:
+            allc = json.load(f)
+    except (OSError, ValueError):
+        allc = {}
+    allc[wl.name] = entry
+    with open(cpath, "w") as f:
+        json.dump(allc, f, indent=1)
+    lines = ["# HBM traffic of the fused kernel, workload %s (N=%d %dx%d C_in=%d -> C_out=%d, "
+             "%dx%d, %s)" % (wl.name, wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.dtype),
+             "# commands (cd /tmp; TMPDIR=/tmp), each counter in its own run:"]
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        lines.append("#   " + cmd_text(["--pmc", counter], prog))
+    lines += ["# calibration with a plain %d MiB device copy (reads and writes exactly %d bytes):"
+              % (COPY_BYTES_MIB(), COPY_BYTES_MIB() * 2**20),
+              "#   " + cmd_text(["--pmc", "FETCH_SIZE"], [COPY]) + "   (and WRITE_SIZE)",
+              "# copy: FETCH_SIZE %.1f KiB/dispatch (scale %.4f); WRITE_SIZE %.1f KiB/dispatch "
+              "(scale %.4f)" % (val["FETCH_SIZE"]["copy_kib"], val["FETCH_SIZE"]["scale"],
+                                val["WRITE_SIZE"]["copy_kib"], val["WRITE_SIZE"]["scale"]),
+              "kernel %s (source hash %s), %d dispatches averaged" % (
+                  sym[:80], source_hash, val["FETCH_SIZE"]["dispatches"]),
+              "FETCH_SIZE raw %.1f KiB -> %.3f MB   (algorithmic reads x+w+BN = %.3f MB)" % (
+                  val["FETCH_SIZE"]["raw_kib"], val["FETCH_SIZE"]["bytes"] / 1e6,
+                  (b["x"] + b["w"] + b["bn"]) / 1e6),
+              "WRITE_SIZE raw %.1f KiB -> %.3f MB   (algorithmic writes y = %.3f MB)" % (
+                  val["WRITE_SIZE"]["raw_kib"], val["WRITE_SIZE"]["bytes"] / 1e6, b["y"] / 1e6),
+              "total %.3f MB vs algorithmic %.3f MB -> excess %+.2f%%" % (
+                  hbm / 1e6, alg / 1e6, 100.0 * (hbm / alg - 1.0))]
+    path = os.path.join(PROFILES, "hbm_traffic_%s.txt" % wl.name)
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("wrote %s and %s" % (path, cpath))
+
+
+def COPY_BYTES_MIB():
+    from conv2d_batchnorm_silu_amd.copy_calibration import COPY_BYTES
+    return COPY_BYTES // 2**20
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--raw", required=True, help="directory for raw rocprofv3 output")
+    ap.add_argument("--traces", action="store_true")
+    ap.add_argument("--split", action="store_true")
+    ap.add_argument("--counters", action="store_true")
+    ap.add_argument("--workloads", default=None, help="comma-separated (default: all)")
+    ap.add_argument("--dest", default=None, help="where the summaries go (default: profiles/)")
+    ap.add_argument("--reuse", action="store_true",
+                    help="summarise the raw output already under --raw without profiling")
+    args = ap.parse_args()
+    global PROFILES, REUSE
+    if args.dest:
+        PROFILES = os.path.abspath(args.dest)
+        os.makedirs(PROFILES, exist_ok=True)
+    REUSE = args.reuse
+    raw = os.path.abspath(args.raw)
+    os.makedirs(raw, exist_ok=True)
+    names = args.workloads.split(",") if args.workloads else [
+        n for n, w in WORKLOADS.items() if w.dtype == "f16"]
+    import bench  # source_hash only; bench imports torch lazily
+    if args.traces:
+        for n in names:
+            write_trace(raw, WORKLOADS[n])
+    if args.split:
+        write_split(raw, names)
+    if args.counters:
+        write_counters(raw, WORKLOADS[HEADLINE], bench.source_hash())
+
+
+if __name__ == "__main__":
+    main()
