@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void silu_apply_f16x8(const half8_t* __restric
 }
 
 // Split form ("Fusing an Epilogue", section "When not to fuse"; "Kernel
-// Fusion: When to Fuse and When Not To"): the conv kernel writes t1, then
+// Fusion", the passage on when fusion does not pay): the conv kernel writes t1, then
 // this kernel applies the same fp32 epilogue as the fused kernels,
 // y = silu(t1 * scale[c] + bias[c]), reading t1 once and writing y once.
 template <typename T>

@@ -61,9 +61,9 @@ typedef enum { TG_F16 = 0, TG_F32 = 1 } tg_dtype;
  * baseline instead: that conv kernel with an identity epilogue writing t1,
  * then a BatchNorm kernel t1 -> t2, then a SiLU kernel t2 -> y ("The problem"
  * section of the same page). Or it may be OR-ed with TG_SPLIT for the split
- * form that "When not to fuse" (same page) and "Kernel Fusion: When to Fuse
- * and When Not To" (section on when fusion does not pay) weigh against the
- * fused one: the conv kernel with an identity epilogue writing t1, then one
+ * form that "When not to fuse" (same page) and "Kernel Fusion" (cheatsheet
+ * page, the passage on when fusion does not pay) weigh against the fused
+ * one: the conv kernel with an identity epilogue writing t1, then one
  * BatchNorm+SiLU kernel t1 -> y. TG_UNFUSED and TG_SPLIT exclude each other. */
 typedef enum {
     TG_KERNEL_AUTO = 0,   /* the dispatch table decides (see tg_dispatch_choose) */

@@ -20,6 +20,13 @@ What each function follows:
   * ``silu`` -- same section: v * sigmoid(v) with the logistic sigmoid.
   * ``conv_bn_silu`` / ``conv_bn_silu_at`` -- same page, section "The shape
     of it": the three applied in order to every output element.
+  * ``conv_bn_silu_train`` -- batch norm with batch statistics (training
+    mode), the reduction case that "Kernel Fusion" (cheatsheet page, the
+    passages on reductions and on synchronization boundaries) sets apart:
+    per output channel, the mean and the biased variance over all N*P*Q
+    conv outputs normalise the batch (the batch-normalising transform of
+    Ioffe and Szegedy, 2015); running estimates, if given, move by
+    ``momentum`` towards the batch mean and the unbiased batch variance.
 """
 from __future__ import annotations
 
@@ -166,4 +173,32 @@ def conv_bn_silu_at(x, w, gamma, beta, mean, var, eps: float, stride: int, pad: 
                                         idx.ctypes.data_as(_llp), idx.size, _ptr(out))
     if rc:
         raise ValueError("oracle_conv_bn_silu_at rejected the arguments (%d)" % rc)
+    return out
+
+
+def conv_bn_silu_train(x, w, gamma, beta, eps: float, stride: int, pad: int,
+                       running_mean=None, running_var=None, momentum: float = 0.1,
+                       threads: int | None = None) -> dict:
+    """Training-mode path: t = conv2d(x, w); per channel c, over the M =
+    N*P*Q outputs, mean_c = sum(t)/M and var_c = sum((t - mean_c)^2)/M
+    (two passes, fp64); y = silu(batchnorm(t, gamma, beta, mean, var, eps)).
+    With running estimates: running_mean <- (1-momentum)*running_mean +
+    momentum*mean and running_var <- (1-momentum)*running_var +
+    momentum*var*M/(M-1). Needs M >= 2. Returns y, mean, var and the new
+    running estimates (None when not given), all fp64."""
+    t = conv2d(x, w, stride, pad, threads)
+    C = t.shape[-1]
+    flat = t.reshape(-1, C)
+    M = flat.shape[0]
+    if M < 2:
+        raise ValueError("batch statistics need at least two values per channel")
+    mean = flat.sum(axis=0) / M
+    var = ((flat - mean) ** 2).sum(axis=0) / M
+    y = silu(batchnorm(t, gamma, beta, mean, var, eps))
+    out = {"y": y, "mean": mean, "var": var, "running_mean": None, "running_var": None}
+    m = float(momentum)
+    if running_mean is not None:
+        out["running_mean"] = (1.0 - m) * _f64(running_mean).reshape(C) + m * mean
+    if running_var is not None:
+        out["running_var"] = (1.0 - m) * _f64(running_var).reshape(C) + m * var * (M / (M - 1.0))
     return out

@@ -276,3 +276,83 @@ def test_rejects_bad_geometry():
         oracle.conv2d(np.zeros((1, 2, 2, 1)), np.zeros((1, 5, 5, 1)), 1, 0)
     with pytest.raises(ValueError):
         oracle.conv2d(np.zeros((1, 4, 4, 2)), np.zeros((1, 3, 3, 3)), 1, 0)
+
+
+# ---- training-mode batch norm (batch statistics) ----
+
+def _train_case(seed, shape=(3, 9, 7, 5), C_out=6, k=3, stride=1, pad=1, shift=0.0):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(size=shape) + shift
+    w = rng.normal(size=(C_out, k, k, shape[3])) / np.sqrt(k * k * shape[3])
+    gamma = rng.uniform(0.5, 1.5, C_out)
+    beta = rng.normal(0.0, 0.3, C_out)
+    rm = rng.normal(0.0, 0.3, C_out)
+    rv = rng.uniform(0.5, 2.0, C_out)
+    return x, w, gamma, beta, rm, rv, stride, pad
+
+
+def test_train_matches_torch_batch_norm():
+    """torch CPU fp64 conv2d + batch_norm(training=True) + silu, including the
+    running-estimate update (a library cross-check of every output)."""
+    import torch
+    import torch.nn.functional as F
+    for seed, (stride, pad, mom) in enumerate([(1, 1, 0.1), (2, 0, 0.3), (1, 2, 1.0)]):
+        x, w, g, b, rm, rv, _, _ = _train_case(40 + seed, stride=stride, pad=pad)
+        eps = 1e-5
+        got = oracle.conv_bn_silu_train(x, w, g, b, eps, stride, pad, rm, rv, mom)
+        xt = torch.from_numpy(x).permute(0, 3, 1, 2)
+        wt = torch.from_numpy(w).permute(0, 3, 1, 2)
+        t = F.conv2d(xt, wt, stride=stride, padding=pad)
+        rmt, rvt = torch.from_numpy(rm.copy()), torch.from_numpy(rv.copy())
+        bn = F.batch_norm(t, rmt, rvt, torch.from_numpy(g), torch.from_numpy(b), training=True,
+                          momentum=mom, eps=eps)
+        ref = F.silu(bn).permute(0, 2, 3, 1).numpy()
+        np.testing.assert_allclose(got["y"], ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(got["running_mean"], rmt.numpy(), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(got["running_var"], rvt.numpy(), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(got["mean"], t.mean(dim=(0, 2, 3)).numpy(), rtol=1e-12,
+                                   atol=1e-14)
+        np.testing.assert_allclose(got["var"], t.var(dim=(0, 2, 3), unbiased=False).numpy(),
+                                   rtol=1e-12, atol=1e-14)
+
+
+def test_train_normalises_each_channel():
+    """gamma = 1, beta = 0: before SiLU every channel has mean 0 and variance
+    var/(var + eps) over the batch (the defining property of the transform);
+    undoing SiLU is not needed -- the stage entries give the pre-SiLU values."""
+    x, w, _, _, _, _, s, p = _train_case(50, shift=3.0)
+    C = w.shape[0]
+    got = oracle.conv_bn_silu_train(x, w, np.ones(C), np.zeros(C), 1e-5, s, p)
+    t = oracle.conv2d(x, w, s, p)
+    z = oracle.batchnorm(t, np.ones(C), np.zeros(C), got["mean"], got["var"], 1e-5).reshape(-1, C)
+    np.testing.assert_allclose(z.mean(axis=0), 0.0, atol=1e-12)
+    np.testing.assert_allclose(z.var(axis=0), got["var"] / (got["var"] + 1e-5), rtol=1e-10)
+    np.testing.assert_array_equal(got["y"], oracle.silu(z.reshape(t.shape)))
+
+
+def test_train_constant_channel_gives_beta():
+    """A channel whose conv output is the same everywhere has variance 0, so
+    its normalised value is 0 and the output is silu(beta) exactly."""
+    x = np.ones((2, 4, 4, 3))
+    w = np.ones((2, 1, 1, 3))
+    w[1] *= -0.5
+    beta = np.array([0.25, -1.5])
+    got = oracle.conv_bn_silu_train(x, w, np.array([1.3, 0.7]), beta, 1e-5, 1, 0)
+    np.testing.assert_array_equal(got["var"], 0.0)
+    np.testing.assert_array_equal(got["y"][..., 0], oracle.silu(np.full((2, 4, 4), 0.25)))
+    np.testing.assert_array_equal(got["y"][..., 1], oracle.silu(np.full((2, 4, 4), -1.5)))
+
+
+def test_train_needs_two_values_per_channel():
+    with pytest.raises(ValueError):
+        oracle.conv_bn_silu_train(np.ones((1, 1, 1, 2)), np.ones((3, 1, 1, 2)), np.ones(3),
+                                  np.zeros(3), 1e-5, 1, 0)
+
+
+def test_train_with_batch_stats_equals_inference_path():
+    """Feeding the batch statistics to the inference path reproduces the
+    training output bit for bit (same stages, same order)."""
+    x, w, g, b, _, _, s, p = _train_case(51)
+    got = oracle.conv_bn_silu_train(x, w, g, b, 1e-5, s, p)
+    inf = oracle.conv_bn_silu(x, w, g, b, got["mean"], got["var"], 1e-5, s, p)
+    np.testing.assert_array_equal(got["y"], inf)
