@@ -89,20 +89,62 @@ class Sets:
         torch.cuda.synchronize()
 
 
-def time_plan(torch, plan, sets, steps, warmup):
-    """Average ms per call over `steps` calls (after `warmup`), rotating sets."""
-    n = sets.n
+def _timed(torch, call, n, steps, warmup):
+    """Average ms per call(i % n) over `steps` calls after `warmup`, with HIP
+    events on the current stream (the one the calls launch on). Every call
+    returns a tg_status, checked after the timed region."""
     for i in range(warmup):
-        plan.run(sets.x[i % n], sets.w, sets.scale, sets.bias, out=sets.y[i % n])
+        assert call(i % n) == 0
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    st = []
     e0.record()
     for i in range(steps):
-        plan.run(sets.x[i % n], sets.w, sets.scale, sets.bias, out=sets.y[i % n])
+        st.append(call(i % n))
     e1.record()
     torch.cuda.synchronize()
+    assert not any(st), "a timed call failed: status %s" % max(st)
     return e0.elapsed_time(e1) / steps
+
+
+def time_plan(torch, plan, sets, steps, warmup):
+    """Average ms per call over `steps` calls (after `warmup`), rotating sets.
+    Calls go straight to tg_conv_bn_silu_run with device addresses taken once
+    (shapes and dtypes are checked through the binding's run() first), so the
+    host's per-call work stays well below the kernels' time."""
+    n = sets.n
+    plan.run(sets.x[0], sets.w, sets.scale, sets.bias, out=sets.y[0])  # checked call
+    ws = None
+    if plan.workspace_bytes:
+        ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=sets.w.device)
+    lib = plan._lib
+    stream = torch.cuda.current_stream().cuda_stream
+    args = [(plan._h, sets.x[i].data_ptr(), sets.w.data_ptr(), sets.scale.data_ptr(),
+             sets.bias.data_ptr(), sets.y[i].data_ptr(), ws.data_ptr() if ws is not None else 0,
+             plan.workspace_bytes, stream) for i in range(n)]
+    return _timed(torch, lambda i: lib.tg_conv_bn_silu_run(*args[i]), n, steps, warmup)
+
+
+def time_train(torch, plan, sets, steps, warmup):
+    """Average ms per training-mode call (batch statistics), rotating sets;
+    the workspace, running estimates and batch-statistic outputs are
+    allocated once and the calls go straight to tg_conv_bn_silu_train_run."""
+    n, C, dev = sets.n, sets.scale.numel(), sets.w.device
+    ws = torch.empty(plan.train_workspace_bytes(), dtype=torch.uint8, device=dev)
+    gamma, beta = sets.scale.clone(), sets.bias.clone()
+    rm = torch.zeros(C, dtype=torch.float32, device=dev)
+    rv = torch.ones(C, dtype=torch.float32, device=dev)
+    bm, bv = torch.empty_like(rm), torch.empty_like(rv)
+    plan.run_train(sets.x[0], sets.w, gamma, beta, 1e-5, 0.1, rm, rv, out=sets.y[0],
+                   workspace=ws)  # checked call
+    lib = plan._lib
+    stream = torch.cuda.current_stream().cuda_stream
+    args = [(plan._h, sets.x[i].data_ptr(), sets.w.data_ptr(), gamma.data_ptr(),
+             beta.data_ptr(), 1e-5, 0.1, rm.data_ptr(), rv.data_ptr(), bm.data_ptr(),
+             bv.data_ptr(), sets.y[i].data_ptr(), ws.data_ptr(), ws.numel(), stream)
+            for i in range(n)]
+    return _timed(torch, lambda i: lib.tg_conv_bn_silu_train_run(*args[i]), n, steps, warmup)
 
 
 def binding_roof(wl):
@@ -164,6 +206,11 @@ def bench_workload(torch, wl, steps, warmup, with_unfused=True, plan_kind="auto"
         sms = time_plan(torch, sp, sets, steps, warmup)
         row.update({"split_us": round(sms * 1e3, 2), "speedup_vs_split": round(sms / ms, 3),
                     "split_gbs_effective": round(traffic.split_bytes(wl) / sms / 1e6, 1)})
+        # Training-mode BatchNorm (batch statistics): conv -> t1, statistics,
+        # fold, BatchNorm+SiLU; the same plan, timed the same way.
+        tms = time_train(torch, plan, sets, steps, warmup)
+        row.update({"train_us": round(tms * 1e3, 2),
+                    "train_gbs_effective": round(traffic.train_bytes(wl) / tms / 1e6, 1)})
     del sets
     torch.cuda.empty_cache()
     return row, d

@@ -94,6 +94,11 @@ def library():
         lib.tg_status_string.restype = ctypes.c_char_p
         lib.tg_kernel_name.argtypes = [i]
         lib.tg_kernel_name.restype = ctypes.c_char_p
+        f = ctypes.c_float
+        lib.tg_conv_bn_silu_train_run.argtypes = [vp] * 5 + [f, f] + [vp] * 5 + [vp, sz, vp]
+        lib.tg_conv_bn_silu_train_run.restype = i
+        lib.tg_conv_bn_silu_train_workspace.argtypes = [vp, ctypes.POINTER(sz)]
+        lib.tg_conv_bn_silu_train_workspace.restype = i
         _lib = lib
         return lib
 
@@ -241,6 +246,46 @@ class ConvBnSilu:
         return out
 
     __call__ = run
+
+    def train_workspace_bytes(self) -> int:
+        ws = ctypes.c_size_t()
+        _check(self._lib.tg_conv_bn_silu_train_workspace(self._h, ctypes.byref(ws)),
+               "tg_conv_bn_silu_train_workspace")
+        return ws.value
+
+    def run_train(self, x, w, gamma, beta, eps=1e-5, momentum=0.1, running_mean=None,
+                  running_var=None, out=None, workspace=None, stream=None):
+        """Training-mode BatchNorm (batch statistics): returns (y, batch_mean,
+        batch_var); running_mean/running_var (fp32 [C_out]) are updated in
+        place when given."""
+        import torch
+        N, H, W, C_in, C_out, kh, kw, _, _ = self.shape
+        td = _torch_dtype(self.dtype)
+        self._check_tensor(x, (N, H, W, C_in), td, "x")
+        self._check_tensor(w, (C_out, kh, kw, C_in), td, "w")
+        for t, name in ((gamma, "gamma"), (beta, "beta")):
+            self._check_tensor(t, (C_out,), torch.float32, name)
+        if (running_mean is None) != (running_var is None):
+            raise ValueError("give both running_mean and running_var, or neither")
+        for t, name in ((running_mean, "running_mean"), (running_var, "running_var")):
+            if t is not None:
+                self._check_tensor(t, (C_out,), torch.float32, name)
+        if out is None:
+            out = torch.empty(self.y_shape, dtype=td, device=x.device)
+        self._check_tensor(out, self.y_shape, td, "out")
+        bm = torch.empty(C_out, dtype=torch.float32, device=x.device)
+        bv = torch.empty(C_out, dtype=torch.float32, device=x.device)
+        need = self.train_workspace_bytes()
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+        ptr = lambda t: 0 if t is None else t.data_ptr()
+        st = self._lib.tg_conv_bn_silu_train_run(
+            self._h, x.data_ptr(), w.data_ptr(), gamma.data_ptr(), beta.data_ptr(), float(eps),
+            float(momentum), ptr(running_mean), ptr(running_var), bm.data_ptr(), bv.data_ptr(),
+            out.data_ptr(), workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+            _stream_handle(stream))
+        _check(st, "tg_conv_bn_silu_train_run")
+        return out, bm, bv
 
     def close(self):
         if getattr(self, "_h", None):

@@ -295,6 +295,73 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
     return TG_OK;
 }
 
+// Launch the plan's conv kernel (or `kernel`, after an alignment fallback)
+// writing `out`, with the fused or the identity epilogue.
+hipError_t launch_conv(const tg_conv_bn_silu_plan* plan, int kernel, bool identity, const void* x,
+                       const void* w, const float* bn_scale, const float* bn_bias, void* conv_out,
+                       hipStream_t s) {
+    const ConvGeom& g = plan->g;
+    const bool f32 = plan->dtype == TG_F32;
+    hipError_t e;
+    switch (kernel) {
+        case TG_KERNEL_IGEMM:
+            if (plan->cu_waves > 0 && aligned16(bn_scale) && aligned16(bn_bias))
+                e = launch_igemm_cu(g, plan->cu_waves, plan->cu_pd, plan->rw_nt, identity, x, w,
+                                    bn_scale, bn_bias, conv_out, s);
+            else if (plan->igemm_cfg < 0 && env_int("TG_STREAM", 0) > 0)
+                e = launch_igemm_stream(g, env_int("TG_STREAM", 16), plan->rw_nt, identity, x, w,
+                                        bn_scale, bn_bias, conv_out, s);
+            else if (plan->patch_cfg >= 0)
+                e = launch_igemm_patch(g, plan->patch_cfg, identity, x, w, bn_scale, bn_bias,
+                                       conv_out, s);
+            else if (plan->dma_cfg >= 0)
+                e = launch_igemm_dma(g, plan->dma_cfg, identity, x, w, bn_scale, bn_bias, conv_out,
+                                     s);
+            else if (plan->igemm_cfg < 0)
+                e = launch_igemm_rw(g, plan->rw_grid, plan->rw_nf, plan->rw_cs, plan->rw_ncw,
+                                    plan->rw_nt, identity, x, w, bn_scale, bn_bias, conv_out, s);
+            else
+                e = launch_igemm(g, plan->igemm_cfg, identity, x, w, bn_scale, bn_bias, conv_out,
+                                 s);
+            break;
+        case TG_KERNEL_TILED:
+            if (plan->stem_wpc > 0)
+                e = launch_stem(g, plan->stem_wpc, plan->stem_rows, identity, x, w, bn_scale, bn_bias,
+                                conv_out, s);
+            else if (plan->tm_pipe_grid > 0)
+                e = launch_tiled_mfma_pipe(g, plan->tm_rows, plan->tm_pipe_grid, identity, x, w,
+                                           bn_scale, bn_bias, conv_out, s);
+            else if (plan->tm_rows > 0)
+                e = launch_tiled_mfma(g, plan->tm_rows, identity, x, w, bn_scale, bn_bias,
+                                      conv_out, s);
+            else
+                e = launch_tiled(g, plan->tiled, identity, x, w, bn_scale, bn_bias, conv_out, s);
+            break;
+        default:
+            e = launch_scalar(g, f32, identity, x, w, bn_scale, bn_bias, conv_out, s);
+            break;
+    }
+    return e;
+}
+
+// Training-mode workspace: [t1, y-sized][scale fp32 [C]][bias fp32 [C]]
+// [row-block partials, fp64], each piece 256-byte aligned.
+struct TrainWs {
+    size_t t1, scale, bias, partial, total;
+};
+TrainWs train_ws(const tg_conv_bn_silu_plan* plan) {
+    const ConvGeom& g = plan->g;
+    const size_t ysz = (size_t)g.M * g.C_out * (plan->dtype == TG_F32 ? 4 : 2);
+    const size_t vec = round256((size_t)g.C_out * 4);
+    TrainWs t;
+    t.t1 = 0;
+    t.scale = round256(ysz);
+    t.bias = t.scale + vec;
+    t.partial = t.bias + vec;
+    t.total = t.partial + round256(bn_train_partial_bytes(g.M, g.C_out));
+    return t;
+}
+
 }  // namespace
 
 extern "C" {
@@ -343,45 +410,7 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, c
         }
     }
     bool identity = plan->unfused || plan->split;
-    hipError_t e;
-    switch (kernel) {
-        case TG_KERNEL_IGEMM:
-            if (plan->cu_waves > 0 && aligned16(bn_scale) && aligned16(bn_bias))
-                e = launch_igemm_cu(g, plan->cu_waves, plan->cu_pd, plan->rw_nt, identity, x, w,
-                                    bn_scale, bn_bias, conv_out, s);
-            else if (plan->igemm_cfg < 0 && env_int("TG_STREAM", 0) > 0)
-                e = launch_igemm_stream(g, env_int("TG_STREAM", 16), plan->rw_nt, identity, x, w,
-                                        bn_scale, bn_bias, conv_out, s);
-            else if (plan->patch_cfg >= 0)
-                e = launch_igemm_patch(g, plan->patch_cfg, identity, x, w, bn_scale, bn_bias,
-                                       conv_out, s);
-            else if (plan->dma_cfg >= 0)
-                e = launch_igemm_dma(g, plan->dma_cfg, identity, x, w, bn_scale, bn_bias, conv_out,
-                                     s);
-            else if (plan->igemm_cfg < 0)
-                e = launch_igemm_rw(g, plan->rw_grid, plan->rw_nf, plan->rw_cs, plan->rw_ncw,
-                                    plan->rw_nt, identity, x, w, bn_scale, bn_bias, conv_out, s);
-            else
-                e = launch_igemm(g, plan->igemm_cfg, identity, x, w, bn_scale, bn_bias, conv_out,
-                                 s);
-            break;
-        case TG_KERNEL_TILED:
-            if (plan->stem_wpc > 0)
-                e = launch_stem(g, plan->stem_wpc, plan->stem_rows, identity, x, w, bn_scale, bn_bias,
-                                conv_out, s);
-            else if (plan->tm_pipe_grid > 0)
-                e = launch_tiled_mfma_pipe(g, plan->tm_rows, plan->tm_pipe_grid, identity, x, w,
-                                           bn_scale, bn_bias, conv_out, s);
-            else if (plan->tm_rows > 0)
-                e = launch_tiled_mfma(g, plan->tm_rows, identity, x, w, bn_scale, bn_bias,
-                                      conv_out, s);
-            else
-                e = launch_tiled(g, plan->tiled, identity, x, w, bn_scale, bn_bias, conv_out, s);
-            break;
-        default:
-            e = launch_scalar(g, f32, identity, x, w, bn_scale, bn_bias, conv_out, s);
-            break;
-    }
+    hipError_t e = launch_conv(plan, kernel, identity, x, w, bn_scale, bn_bias, conv_out, s);
     if (e != hipSuccess) {
         if (env_flag("TG_LOG")) fprintf(stderr, "[tgconv] launch failed: %s\n", hipGetErrorString(e));
         return TG_ERR_HIP;
@@ -398,6 +427,49 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, c
         if (e != hipSuccess) return TG_ERR_HIP;
     }
     return TG_OK;
+}
+
+tg_status tg_conv_bn_silu_train_workspace(const tg_conv_bn_silu_plan* plan, size_t* bytes) {
+    if (!plan || !bytes) return TG_ERR_INVALID_ARGUMENT;
+    *bytes = train_ws(plan).total;
+    return TG_OK;
+}
+
+tg_status tg_conv_bn_silu_train_run(const tg_conv_bn_silu_plan* plan, const void* x, const void* w,
+                                    const float* gamma, const float* beta, float eps,
+                                    float momentum, float* running_mean, float* running_var,
+                                    float* batch_mean, float* batch_var, void* y, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
+    if (!plan || !x || !w || !gamma || !beta || !y) return TG_ERR_INVALID_ARGUMENT;
+    if ((running_mean == nullptr) != (running_var == nullptr)) return TG_ERR_INVALID_ARGUMENT;
+    if (!(eps >= 0.0f) || !(momentum >= 0.0f && momentum <= 1.0f)) return TG_ERR_INVALID_ARGUMENT;
+    const ConvGeom& g = plan->g;
+    if (g.M < 2) return TG_ERR_INVALID_ARGUMENT;  // batch statistics need two values per channel
+    const TrainWs L = train_ws(plan);
+    if (!workspace || workspace_bytes < L.total) return TG_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    const bool f32 = plan->dtype == TG_F32;
+    int kernel = plan->kernel;
+    if (kernel != TG_KERNEL_SCALAR &&
+        !(aligned16(x) && aligned16(w) && aligned16(y) && aligned16(workspace))) {
+        if (plan->forced) return TG_ERR_ALIGNMENT;
+        kernel = TG_KERNEL_SCALAR;
+    }
+    char* ws = (char*)workspace;
+    void* t1 = ws + L.t1;
+    float* scale = (float*)(ws + L.scale);
+    float* bias = (float*)(ws + L.bias);
+    double* partial = (double*)(ws + L.partial);
+    // 1. conv -> t1 (identity epilogue: scale/bias are not read)
+    hipError_t e = launch_conv(plan, kernel, true, x, w, scale, bias, t1, s);
+    if (e != hipSuccess) return TG_ERR_HIP;
+    // 2-3. batch statistics -> scale, bias, running estimates
+    e = launch_bn_train_stats(f32, t1, g.M, g.C_out, gamma, beta, eps, momentum, running_mean,
+                              running_var, batch_mean, batch_var, partial, scale, bias, s);
+    if (e != hipSuccess) return TG_ERR_HIP;
+    // 4. BatchNorm + SiLU: t1 -> y
+    e = launch_bn_silu_apply(f32, t1, scale, bias, y, (long long)g.M * g.C_out, g.C_out, s);
+    return e == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 
 tg_status tg_bn_fold(const float* gamma, const float* beta, const float* mean, const float* var,

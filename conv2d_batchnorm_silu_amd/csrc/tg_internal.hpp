@@ -100,6 +100,15 @@ hipError_t launch_tiled_mfma_pipe(const ConvGeom& g, int R, int grid, bool ident
 hipError_t launch_bn_apply(bool f32, const void* t1, const float* scale, const float* bias, void* t2,
                            long long total, int C, hipStream_t s);
 hipError_t launch_silu_apply(bool f32, const void* t2, void* y, long long total, hipStream_t s);
+// Training-mode BatchNorm (train_bn.hip): per-channel batch statistics of
+// t1 [M][C] into row-block partials, then scale/bias (and running estimates).
+void bn_train_grid(int M, int* R, int* GX);
+size_t bn_train_partial_bytes(int M, int C);
+hipError_t launch_bn_train_stats(bool f32, const void* t1, int M, int C, const float* gamma,
+                                 const float* beta, float eps, float momentum,
+                                 float* running_mean, float* running_var, float* batch_mean,
+                                 float* batch_var, double* partial, float* scale, float* bias,
+                                 hipStream_t s);
 // Split form: y = silu(t1 * scale[c] + bias[c]) in one streaming kernel.
 hipError_t launch_bn_silu_apply(bool f32, const void* t1, const float* scale, const float* bias,
                                 void* y, long long total, int C, hipStream_t s);

@@ -64,6 +64,14 @@ def split_bytes(wl) -> int:
                                                 ELEM_BYTES[wl.dtype])
 
 
+def train_bytes(wl) -> int:
+    """Training-mode BatchNorm as built: conv writes t1, the statistics pass
+    reads t1, the BatchNorm+SiLU pass reads t1 and writes y (gamma/beta in
+    place of the folded constants: the same 8*C_out bytes)."""
+    b = workload_bytes(wl)
+    return fused_bytes(wl) + 3 * b["y"]
+
+
 def conv_flops(wl) -> int:
     """2 * M * K * C_out with M = N*P*Q and K = kh*kw*C_in (unpadded K)."""
     return 2 * wl.N * wl.P * wl.Q * wl.kh * wl.kw * wl.C_in * wl.C_out

@@ -116,6 +116,39 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan *plan, const void *x, c
                               const float *bn_scale, const float *bn_bias, void *y,
                               void *workspace, size_t workspace_bytes, void *stream);
 
+/* Training-mode BatchNorm: the batch's own statistics instead of running
+ * ones. Per output channel k, over all M = N*P*Q conv outputs acc:
+ *   mean_k = sum(acc)/M, var_k = sum((acc - mean_k)^2)/M   (biased),
+ *   y = silu(gamma_k * (acc - mean_k) / sqrt(var_k + eps) + beta_k),
+ * the batch-normalising transform (Ioffe and Szegedy, 2015). The statistics
+ * are a reduction over every block's outputs, which "Kernel Fusion"
+ * (cheatsheet page, passages on reductions and on synchronization
+ * boundaries) says cannot be fused without a kernel boundary, so the call
+ * runs in passes on `stream`: the plan's conv kernel writes the conv output
+ * t1 into the workspace, a reduction forms per-channel sums in fp64 (in a
+ * fixed order: results are deterministic), a small kernel folds them into one
+ * scale and one bias, and a streaming kernel applies BatchNorm and SiLU
+ * (t1 -> y). gamma, beta: device fp32 [C_out]. running_mean/running_var:
+ * device fp32 [C_out] updated in place as r = (1-momentum)*r +
+ * momentum*batch_value, with the unbiased variance var_k*M/(M-1); both NULL
+ * for no update. batch_mean/batch_var: device fp32 [C_out] outputs (the
+ * biased variance), each may be NULL. workspace: at least the size from
+ * tg_conv_bn_silu_train_workspace, 16-byte aligned for the vector kernels,
+ * not aliasing any other argument. Errors: TG_ERR_INVALID_ARGUMENT for a
+ * NULL plan/x/w/gamma/beta/y, only one of running_mean/running_var given,
+ * eps < 0, momentum outside [0, 1], or M < 2; TG_ERR_WORKSPACE;
+ * TG_ERR_ALIGNMENT (forced kernels only, as for run); TG_ERR_HIP. */
+tg_status tg_conv_bn_silu_train_run(const tg_conv_bn_silu_plan *plan, const void *x,
+                                    const void *w, const float *gamma, const float *beta,
+                                    float eps, float momentum, float *running_mean,
+                                    float *running_var, float *batch_mean, float *batch_var,
+                                    void *y, void *workspace, size_t workspace_bytes,
+                                    void *stream);
+
+/* Workspace bytes tg_conv_bn_silu_train_run needs for this plan (host only).
+ * TG_ERR_INVALID_ARGUMENT for NULL arguments. */
+tg_status tg_conv_bn_silu_train_workspace(const tg_conv_bn_silu_plan *plan, size_t *bytes);
+
 /* Free a plan. NULL is a no-op. */
 tg_status tg_conv_bn_silu_destroy(tg_conv_bn_silu_plan *plan);
 

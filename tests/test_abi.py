@@ -167,6 +167,33 @@ def test_run_argument_errors_before_any_launch(lib):
     lib.tg_conv_bn_silu_destroy(h)
 
 
+def test_train_argument_errors_before_any_launch(lib):
+    """Training-mode entry: argument checks return before any launch."""
+    st, h = _create(lib, 2, 16, 16, 16, 32, 3, 3, 1, 1)
+    assert st == OK
+    ws = ctypes.c_size_t()
+    assert lib.tg_conv_bn_silu_train_workspace(h, ctypes.byref(ws)) == OK
+    ybytes = 2 * 16 * 16 * 32 * 2
+    assert ws.value >= ybytes + 2 * 256
+    assert lib.tg_conv_bn_silu_train_workspace(None, ctypes.byref(ws)) == INVAL
+    a = 1 << 20  # aligned fake addresses: never dereferenced on these paths
+    tr = lib.tg_conv_bn_silu_train_run
+    n = ws.value
+    assert tr(None, a, a, a, a, 1e-5, 0.1, a, a, a, a, a, a, n, None) == INVAL
+    assert tr(h, a, a, None, a, 1e-5, 0.1, a, a, a, a, a, a, n, None) == INVAL
+    assert tr(h, a, a, a, a, 1e-5, 0.1, a, None, a, a, a, a, n, None) == INVAL   # one running
+    assert tr(h, a, a, a, a, -1.0, 0.1, a, a, a, a, a, a, n, None) == INVAL
+    assert tr(h, a, a, a, a, 1e-5, 1.5, a, a, a, a, a, a, n, None) == INVAL
+    assert tr(h, a, a, a, a, 1e-5, 0.1, a, a, a, a, a, None, n, None) == WS
+    assert tr(h, a, a, a, a, 1e-5, 0.1, a, a, a, a, a, a, n - 1, None) == WS
+    lib.tg_conv_bn_silu_destroy(h)
+    st, h = _create(lib, 1, 1, 1, 8, 16, 1, 1, 1, 0)  # one output pixel: M = 1
+    assert st == OK
+    assert lib.tg_conv_bn_silu_train_workspace(h, ctypes.byref(ws)) == OK
+    assert tr(h, a, a, a, a, 1e-5, 0.1, None, None, a, a, a, a, ws.value, None) == INVAL
+    lib.tg_conv_bn_silu_destroy(h)
+
+
 def test_bn_fold_argument_errors(lib):
     a = 1 << 20
     f = lib.tg_bn_fold
