@@ -126,6 +126,34 @@ def time_plan(torch, plan, sets, steps, warmup):
     return _timed(torch, lambda i: lib.tg_conv_bn_silu_run(*args[i]), n, steps, warmup)
 
 
+def time_nchw_legs(torch, plan, wl, sets, steps, warmup):
+    """Average ms per step for a caller whose activations stay NCHW: x
+    NCHW -> NHWC, the fused kernel, y NHWC -> NCHW (three launches; the
+    filters are converted once, at load time, outside the step)."""
+    n, dev = sets.n, sets.w.device
+    dt = 0 if wl.dtype == "f16" else 1
+    xs = [torch.empty((wl.N, wl.C_in, wl.H, wl.W), dtype=sets.x[0].dtype, device=dev)
+          for _ in range(n)]
+    for i in range(n):
+        xs[i].copy_(sets.x[i].permute(0, 3, 1, 2))
+    ys = [torch.empty((wl.N, wl.C_out, wl.P, wl.Q), dtype=sets.y[0].dtype, device=dev)
+          for _ in range(n)]
+    lib = plan._lib
+    stream = torch.cuda.current_stream().cuda_stream
+    a = [(xs[i].data_ptr(), sets.x[i].data_ptr(), sets.y[i].data_ptr(), ys[i].data_ptr())
+         for i in range(n)]
+    w, sc, bi = sets.w.data_ptr(), sets.scale.data_ptr(), sets.bias.data_ptr()
+
+    def step(i):
+        xn, xh, yh, yn = a[i]
+        return (lib.tg_nchw_to_nhwc(xn, xh, wl.N, wl.C_in, wl.H, wl.W, dt, stream) or
+                lib.tg_conv_bn_silu_run(plan._h, xh, w, sc, bi, yh, 0, 0, stream) or
+                lib.tg_nhwc_to_nchw(yh, yn, wl.N, wl.C_out, wl.P, wl.Q, dt, stream))
+    ms = _timed(torch, step, n, steps, warmup)
+    del xs, ys
+    return ms
+
+
 def time_train(torch, plan, sets, steps, warmup):
     """Average ms per training-mode call (batch statistics), rotating sets;
     the workspace, running estimates and batch-statistic outputs are
@@ -206,6 +234,11 @@ def bench_workload(torch, wl, steps, warmup, with_unfused=True, plan_kind="auto"
         sms = time_plan(torch, sp, sets, steps, warmup)
         row.update({"split_us": round(sms * 1e3, 2), "speedup_vs_split": round(sms / ms, 3),
                     "split_gbs_effective": round(traffic.split_bytes(wl) / sms / 1e6, 1)})
+        # A caller whose activations stay NCHW (PyTorch's default layout):
+        # the two per-call conversion legs around the same fused kernel.
+        lms = time_nchw_legs(torch, plan, wl, sets, steps, warmup)
+        row.update({"nchw_legs_us": round(lms * 1e3, 2),
+                    "nchw_legs_share": round(1.0 - ms / lms, 3)})
         # Training-mode BatchNorm (batch statistics): conv -> t1, statistics,
         # fold, BatchNorm+SiLU; the same plan, timed the same way.
         tms = time_train(torch, plan, sets, steps, warmup)

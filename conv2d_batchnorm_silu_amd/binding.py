@@ -99,6 +99,9 @@ def library():
         lib.tg_conv_bn_silu_train_run.restype = i
         lib.tg_conv_bn_silu_train_workspace.argtypes = [vp, ctypes.POINTER(sz)]
         lib.tg_conv_bn_silu_train_workspace.restype = i
+        for name in ("tg_filter_oihw_to_ohwi", "tg_nchw_to_nhwc", "tg_nhwc_to_nchw"):
+            getattr(lib, name).argtypes = [vp, vp, i, i, i, i, i, vp]
+            getattr(lib, name).restype = i
         _lib = lib
         return lib
 
@@ -297,6 +300,33 @@ class ConvBnSilu:
             self.close()
         except Exception:
             pass
+
+
+def _layout(name, src, dst_shape, dims, stream):
+    import torch
+    if not src.is_cuda or not src.is_contiguous():
+        raise ValueError("src must be a contiguous device tensor")
+    dt = {torch.float16: Dtype.F16, torch.float32: Dtype.F32}[src.dtype]
+    dst = torch.empty(dst_shape, dtype=src.dtype, device=src.device)
+    _check(getattr(library(), name)(src.data_ptr(), dst.data_ptr(), *dims, int(dt),
+                                    _stream_handle(stream)), name)
+    return dst
+
+
+def filter_oihw_to_ohwi(w, stream=None):
+    """[C_out, C_in, kh, kw] (PyTorch) -> [C_out, kh, kw, C_in], on the device."""
+    O, I, kh, kw = w.shape
+    return _layout("tg_filter_oihw_to_ohwi", w, (O, kh, kw, I), (O, I, kh, kw), stream)
+
+
+def nchw_to_nhwc(x, stream=None):
+    N, C, H, W = x.shape
+    return _layout("tg_nchw_to_nhwc", x, (N, H, W, C), (N, C, H, W), stream)
+
+
+def nhwc_to_nchw(y, stream=None):
+    N, H, W, C = y.shape
+    return _layout("tg_nhwc_to_nchw", y, (N, C, H, W), (N, C, H, W), stream)
 
 
 def bn_fold(gamma, beta, mean, var, eps, scale=None, bias=None, stream=None):

@@ -472,6 +472,34 @@ tg_status tg_conv_bn_silu_train_run(const tg_conv_bn_silu_plan* plan, const void
     return e == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 
+static tg_status transpose_entry(const void* src, void* dst, long long B, long long R,
+                                 long long S, tg_dtype dtype, void* stream) {
+    if (!src || !dst || src == dst || B < 1 || R < 1 || S < 1) return TG_ERR_INVALID_ARGUMENT;
+    if (dtype != TG_F16 && dtype != TG_F32) return TG_ERR_UNSUPPORTED;
+    if (B * R * S >= (1LL << 31)) return TG_ERR_UNSUPPORTED;
+    hipError_t e = launch_transpose(dtype == TG_F32, src, dst, (int)B, (int)R, (int)S,
+                                    (hipStream_t)stream);
+    return e == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
+tg_status tg_nchw_to_nhwc(const void* src, void* dst, int N, int C, int H, int W,
+                          tg_dtype dtype, void* stream) {
+    if (N < 1 || C < 1 || H < 1 || W < 1) return TG_ERR_INVALID_ARGUMENT;
+    return transpose_entry(src, dst, N, C, (long long)H * W, dtype, stream);
+}
+
+tg_status tg_nhwc_to_nchw(const void* src, void* dst, int N, int C, int H, int W,
+                          tg_dtype dtype, void* stream) {
+    if (N < 1 || C < 1 || H < 1 || W < 1) return TG_ERR_INVALID_ARGUMENT;
+    return transpose_entry(src, dst, N, (long long)H * W, C, dtype, stream);
+}
+
+tg_status tg_filter_oihw_to_ohwi(const void* src, void* dst, int C_out, int C_in, int kh, int kw,
+                                 tg_dtype dtype, void* stream) {
+    if (C_out < 1 || C_in < 1 || kh < 1 || kw < 1) return TG_ERR_INVALID_ARGUMENT;
+    return transpose_entry(src, dst, C_out, C_in, (long long)kh * kw, dtype, stream);
+}
+
 tg_status tg_bn_fold(const float* gamma, const float* beta, const float* mean, const float* var,
                      float eps, int C_out, float* bn_scale, float* bn_bias, void* stream) {
     if (!gamma || !beta || !mean || !var || !bn_scale || !bn_bias || C_out < 1 || !(eps >= 0.0f))

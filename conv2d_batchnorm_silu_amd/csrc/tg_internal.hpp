@@ -109,6 +109,9 @@ hipError_t launch_bn_train_stats(bool f32, const void* t1, int M, int C, const f
                                  float* running_mean, float* running_var, float* batch_mean,
                                  float* batch_var, double* partial, float* scale, float* bias,
                                  hipStream_t s);
+// Batched transpose src [B][R][S] -> dst [B][S][R] (layout.hip).
+hipError_t launch_transpose(bool f32, const void* src, void* dst, int B, int R, int S,
+                            hipStream_t s);
 // Split form: y = silu(t1 * scale[c] + bias[c]) in one streaming kernel.
 hipError_t launch_bn_silu_apply(bool f32, const void* t1, const float* scale, const float* bias,
                                 void* y, long long total, int C, hipStream_t s);

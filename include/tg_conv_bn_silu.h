@@ -163,6 +163,26 @@ tg_status tg_conv_bn_silu_destroy(tg_conv_bn_silu_plan *plan);
 tg_status tg_bn_fold(const float *gamma, const float *beta, const float *mean, const float *var,
                      float eps, int C_out, float *bn_scale, float *bn_bias, void *stream);
 
+/* Layout conversions for callers holding PyTorch-layout tensors ("When the
+ * fusion you want is impossible, fuse into the producer", layout paragraph:
+ * store the filters channels-last once, at load time, and the per-call
+ * conversion kernels disappear, with bit-identical output). Each is a pure
+ * permutation on the device, bit-exact for fp16 and fp32, asynchronous on
+ * `stream`; src and dst are device buffers that must not overlap.
+ *   tg_filter_oihw_to_ohwi: w [C_out][C_in][kh][kw] -> [C_out][kh][kw][C_in],
+ *     once per weight load;
+ *   tg_nchw_to_nhwc: x [N][C][H][W] -> [N][H][W][C];
+ *   tg_nhwc_to_nchw: y [N][H][W][C] -> [N][C][H][W] (H, W: y's extent).
+ * Errors: TG_ERR_INVALID_ARGUMENT for NULL or identical pointers or a size
+ * < 1; TG_ERR_UNSUPPORTED for an unknown dtype or 2^31 or more elements;
+ * TG_ERR_HIP on launch failure. */
+tg_status tg_filter_oihw_to_ohwi(const void *src, void *dst, int C_out, int C_in, int kh, int kw,
+                                 tg_dtype dtype, void *stream);
+tg_status tg_nchw_to_nhwc(const void *src, void *dst, int N, int C, int H, int W,
+                          tg_dtype dtype, void *stream);
+tg_status tg_nhwc_to_nchw(const void *src, void *dst, int N, int C, int H, int W,
+                          tg_dtype dtype, void *stream);
+
 /* Describe a plan: output extent, the kernel run() will launch (for aligned
  * pointers; may include TG_UNFUSED or TG_SPLIT) and the workspace it needs. Any out
  * pointer may be NULL. TG_ERR_INVALID_ARGUMENT for a NULL plan. */

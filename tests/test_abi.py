@@ -194,6 +194,18 @@ def test_train_argument_errors_before_any_launch(lib):
     lib.tg_conv_bn_silu_destroy(h)
 
 
+def test_layout_argument_errors(lib):
+    a, b = 1 << 20, 1 << 21  # fake addresses: never dereferenced on these paths
+    for fn in (lib.tg_nchw_to_nhwc, lib.tg_nhwc_to_nchw, lib.tg_filter_oihw_to_ohwi):
+        assert fn(None, b, 1, 2, 3, 4, 0, None) == INVAL
+        assert fn(a, None, 1, 2, 3, 4, 0, None) == INVAL
+        assert fn(a, a, 1, 2, 3, 4, 0, None) == INVAL
+        assert fn(a, b, 0, 2, 3, 4, 0, None) == INVAL
+        assert fn(a, b, 1, 2, 3, -4, 0, None) == INVAL
+        assert fn(a, b, 1, 2, 3, 4, 7, None) == 2
+        assert fn(a, b, 1024, 1024, 64, 64, 0, None) == 2  # 2^32 elements
+
+
 def test_bn_fold_argument_errors(lib):
     a = 1 << 20
     f = lib.tg_bn_fold
