@@ -20,6 +20,10 @@ What each function follows:
   * ``silu`` -- same section: v * sigmoid(v) with the logistic sigmoid.
   * ``conv_bn_silu`` / ``conv_bn_silu_at`` -- same page, section "The shape
     of it": the three applied in order to every output element.
+  * ``relu``, ``gelu``, ``conv_bn_act`` -- the other activations "Fusing an
+    Epilogue" (section "What an epilogue is") counts as epilogue work:
+    max(v, 0) and the exact GELU v * Phi(v) = v/2 * (1 + erf(v / sqrt 2))
+    (Phi the standard normal CDF), or none, after the same batch norm.
   * ``conv_bn_silu_train`` -- batch norm with batch statistics (training
     mode), the reduction case that "Kernel Fusion" (cheatsheet page, the
     passages on reductions and on synchronization boundaries) sets apart:
@@ -202,3 +206,26 @@ def conv_bn_silu_train(x, w, gamma, beta, eps: float, stride: int, pad: int,
     if running_var is not None:
         out["running_var"] = (1.0 - m) * _f64(running_var).reshape(C) + m * var * (M / (M - 1.0))
     return out
+
+
+def relu(t) -> np.ndarray:
+    """max(v, 0), elementwise."""
+    return np.maximum(_f64(t), 0.0)
+
+
+def gelu(t) -> np.ndarray:
+    """v * Phi(v) with Phi(v) = (1 + erf(v / sqrt 2)) / 2, elementwise (libm
+    erf through scipy)."""
+    from scipy.special import erf
+    t = _f64(t)
+    return 0.5 * t * (1.0 + erf(t / np.sqrt(2.0)))
+
+
+ACTIVATIONS = {"silu": silu, "relu": relu, "gelu": gelu, "none": lambda t: _f64(t)}
+
+
+def conv_bn_act(x, w, gamma, beta, mean, var, eps: float, stride: int, pad: int, act: str,
+                threads: int | None = None) -> np.ndarray:
+    """act(batchnorm(conv2d(x, w))) for act in silu, relu, gelu, none."""
+    return ACTIVATIONS[act](batchnorm(conv2d(x, w, stride, pad, threads), gamma, beta, mean, var,
+                                      eps))

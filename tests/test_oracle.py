@@ -356,3 +356,53 @@ def test_train_with_batch_stats_equals_inference_path():
     got = oracle.conv_bn_silu_train(x, w, g, b, 1e-5, s, p)
     inf = oracle.conv_bn_silu(x, w, g, b, got["mean"], got["var"], 1e-5, s, p)
     np.testing.assert_array_equal(got["y"], inf)
+
+
+# ---- other epilogue activations ----
+
+def test_gelu_pins():
+    """GELU(v) = v * Phi(v): zero at zero, GELU(v) - GELU(-v) = v (since
+    Phi(v) + Phi(-v) = 1), Phi(1) and Phi(-3) from scipy's normal CDF, the
+    limits, and torch's exact GELU."""
+    import torch
+    from scipy.stats import norm
+    assert oracle.gelu(np.array([0.0]))[0] == 0.0
+    v = np.linspace(-8, 8, 1601)
+    np.testing.assert_allclose(oracle.gelu(v) - oracle.gelu(-v), v, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(oracle.gelu(np.array([1.0, -3.0])),
+                               [norm.cdf(1.0), -3.0 * norm.cdf(-3.0)], rtol=1e-14)
+    assert abs(oracle.gelu(np.array([12.0]))[0] - 12.0) < 1e-15
+    assert abs(oracle.gelu(np.array([-12.0]))[0]) < 1e-30
+    ref = torch.nn.functional.gelu(torch.from_numpy(v)).numpy()
+    np.testing.assert_allclose(oracle.gelu(v), ref, rtol=1e-14, atol=1e-15)
+
+
+def test_relu_pins():
+    import torch
+    v = np.random.default_rng(3).normal(size=1000) * 3
+    np.testing.assert_array_equal(oracle.relu(v) - oracle.relu(-v), v)
+    assert (oracle.relu(v)[v < 0] == 0).all()
+    np.testing.assert_array_equal(oracle.relu(v), torch.relu(torch.from_numpy(v)).numpy())
+
+
+def test_conv_bn_act_matches_torch_and_silu_path():
+    """conv_bn_act against torch CPU fp64 conv2d + batch_norm + relu / gelu /
+    nothing; with silu it is the fused oracle bit for bit."""
+    import torch
+    import torch.nn.functional as F
+    wl = WORKLOADS["tiny_f32_3x3"]
+    d = make_inputs(wl)
+    args = (d["gamma"], d["beta"], d["mean"], d["var"], float(d["eps"]), wl.stride, wl.pad)
+    xt = torch.from_numpy(d["x"].astype(np.float64)).permute(0, 3, 1, 2)
+    wt = torch.from_numpy(d["w"].astype(np.float64)).permute(0, 3, 1, 2)
+    bn = F.batch_norm(F.conv2d(xt, wt, stride=wl.stride, padding=wl.pad),
+                      *(torch.from_numpy(d[k].astype(np.float64)) for k in ("mean", "var")),
+                      torch.from_numpy(d["gamma"].astype(np.float64)),
+                      torch.from_numpy(d["beta"].astype(np.float64)), training=False,
+                      eps=float(d["eps"]))
+    for act, fn in (("relu", F.relu), ("gelu", F.gelu), ("none", lambda t: t)):
+        ref = fn(bn).permute(0, 2, 3, 1).numpy()
+        np.testing.assert_allclose(oracle.conv_bn_act(d["x"], d["w"], *args, act), ref,
+                                   rtol=1e-12, atol=1e-13)
+    np.testing.assert_array_equal(oracle.conv_bn_act(d["x"], d["w"], *args, "silu"),
+                                  oracle.conv_bn_silu(d["x"], d["w"], *args))
