@@ -229,3 +229,22 @@ def conv_bn_act(x, w, gamma, beta, mean, var, eps: float, stride: int, pad: int,
     """act(batchnorm(conv2d(x, w))) for act in silu, relu, gelu, none."""
     return ACTIVATIONS[act](batchnorm(conv2d(x, w, stride, pad, threads), gamma, beta, mean, var,
                                       eps))
+
+
+def conv_bn_act_at(x, w, gamma, beta, mean, var, eps: float, stride: int, pad: int, act: str,
+                   flat_idx) -> np.ndarray:
+    """conv_bn_act at selected flat indices into the [N,P,Q,C_out] output:
+    each conv value is the plain window sum over an explicitly zero-padded
+    copy of x, then the unfolded batch norm and the activation."""
+    x, w = _f64(x), _f64(w)
+    N, H, W, C_in, C_out, kh, kw, P, Q = _geom(x, w, stride, pad)
+    idx = np.asarray(flat_idx, dtype=np.int64)
+    n, rem = np.divmod(idx, P * Q * C_out)
+    p, rem = np.divmod(rem, Q * C_out)
+    q, k = np.divmod(rem, C_out)
+    xp = np.pad(x, ((0, 0), (pad, pad), (pad, pad), (0, 0)))
+    conv = np.array([np.sum(xp[n[i], p[i] * stride:p[i] * stride + kh,
+                               q[i] * stride:q[i] * stride + kw, :] * w[k[i]])
+                     for i in range(idx.size)])
+    g, b, m, v = (_f64(a).reshape(C_out)[k] for a in (gamma, beta, mean, var))
+    return ACTIVATIONS[act](g * (conv - m) / np.sqrt(v + eps) + b)

@@ -406,3 +406,15 @@ def test_conv_bn_act_matches_torch_and_silu_path():
                                    rtol=1e-12, atol=1e-13)
     np.testing.assert_array_equal(oracle.conv_bn_act(d["x"], d["w"], *args, "silu"),
                                   oracle.conv_bn_silu(d["x"], d["w"], *args))
+
+
+def test_conv_bn_act_at_matches_full():
+    for name in ("tiny_f32_3x3", "stem3x3s2_k16"):
+        wl = WORKLOADS[name].scaled(N=1, H=9, W=11) if name != "tiny_f32_3x3" else WORKLOADS[name]
+        d = make_inputs(wl)
+        args = (d["gamma"], d["beta"], d["mean"], d["var"], float(d["eps"]), wl.stride, wl.pad)
+        for act in ("relu", "gelu", "none", "silu"):
+            full = oracle.conv_bn_act(d["x"], d["w"], *args, act)
+            idx = np.random.default_rng(1).integers(0, full.size, 300)
+            np.testing.assert_allclose(oracle.conv_bn_act_at(d["x"], d["w"], *args, act, idx),
+                                       full.ravel()[idx], rtol=1e-13, atol=1e-14)
