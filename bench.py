@@ -234,6 +234,13 @@ def bench_workload(torch, wl, steps, warmup, with_unfused=True, plan_kind="auto"
         sms = time_plan(torch, sp, sets, steps, warmup)
         row.update({"split_us": round(sms * 1e3, 2), "speedup_vs_split": round(sms / ms, 3),
                     "split_gbs_effective": round(traffic.split_bytes(wl) / sms / 1e6, 1)})
+        # The same fused kernel with the other epilogue activations.
+        acts = {}
+        for act in ("relu", "gelu", "none"):
+            ap_ = B.ConvBnSilu(wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride,
+                               wl.pad, wl.dtype, "auto", act=act)
+            acts[act] = round(time_plan(torch, ap_, sets, steps, warmup) * 1e3, 2)
+        row["act_us"] = acts
         # A caller whose activations stay NCHW (PyTorch's default layout):
         # the two per-call conversion legs around the same fused kernel.
         lms = time_nchw_legs(torch, plan, wl, sets, steps, warmup)

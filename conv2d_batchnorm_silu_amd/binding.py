@@ -36,6 +36,13 @@ class Kernel(enum.IntEnum):
     SPLIT = 0x200
 
 
+class Activation(enum.IntEnum):
+    SILU = 0
+    RELU = 1
+    GELU = 2
+    NONE = 3
+
+
 class Table(enum.IntEnum):
     MI355X = 0
     PAGES = 1
@@ -77,6 +84,8 @@ def library():
         lib.tg_conv_bn_silu_create.restype = i
         lib.tg_conv_bn_silu_create_with_table.argtypes = [pp] + [i] * 9 + [i, i, i]
         lib.tg_conv_bn_silu_create_with_table.restype = i
+        lib.tg_conv_bn_act_create.argtypes = [pp] + [i] * 9 + [i, i, i]
+        lib.tg_conv_bn_act_create.restype = i
         lib.tg_conv_bn_silu_run.argtypes = [vp] * 6 + [vp, sz, vp]
         lib.tg_conv_bn_silu_run.restype = i
         lib.tg_conv_bn_silu_destroy.argtypes = [vp]
@@ -177,15 +186,23 @@ class ConvBnSilu:
     """
 
     def __init__(self, N, H, W, C_in, C_out, kh, kw=None, stride=1, pad=0, dtype="f16",
-                 kernel="auto", table=Table.MI355X):
+                 kernel="auto", table=Table.MI355X, act="silu"):
         kw = kh if kw is None else kw
         self.shape = (N, H, W, C_in, C_out, kh, kw, stride, pad)
         self.dtype = _as_dtype(dtype)
+        self.act = Activation[str(act).upper()] if not isinstance(act, Activation) else act
         self._lib = library()
         h = ctypes.c_void_p()
-        st = self._lib.tg_conv_bn_silu_create_with_table(
-            ctypes.byref(h), N, H, W, C_in, C_out, kh, kw, stride, pad, int(self.dtype),
-            _as_kernel(kernel), int(table))
+        if self.act == Activation.SILU:
+            st = self._lib.tg_conv_bn_silu_create_with_table(
+                ctypes.byref(h), N, H, W, C_in, C_out, kh, kw, stride, pad, int(self.dtype),
+                _as_kernel(kernel), int(table))
+        else:
+            if table != Table.MI355X:
+                raise ValueError("activations other than SiLU use the MI355X dispatch table")
+            st = self._lib.tg_conv_bn_act_create(
+                ctypes.byref(h), N, H, W, C_in, C_out, kh, kw, stride, pad, int(self.dtype),
+                _as_kernel(kernel), int(self.act))
         _check(st, "tg_conv_bn_silu_create")
         self._h = h
         P, Q, ch, ws = ctypes.c_int(), ctypes.c_int(), ctypes.c_int(), ctypes.c_size_t()

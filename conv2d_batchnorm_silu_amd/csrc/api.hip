@@ -13,6 +13,7 @@
 #include <new>
 
 #include "tg_conv_bn_silu.h"
+#include "tg_device.hpp"
 #include "tg_internal.hpp"
 
 using namespace tg;
@@ -23,6 +24,7 @@ struct tg_conv_bn_silu_plan {
     int kernel;      // TG_KERNEL_SCALAR / TILED / IGEMM (resolved)
     bool unfused;
     bool split;      // conv (identity epilogue) -> t1, then one bn+silu kernel
+    int epi;         // fused epilogue (tg::Epilogue) from the plan's activation
     bool forced;     // kernel was requested explicitly (alignment errors instead of fallback)
     int igemm_cfg;   // index into the igemm variant table (-1: register-weights variant)
     int dma_cfg;     // >= 0: direct-to-LDS pipelined variant with this tile
@@ -204,7 +206,7 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in, int C_out, int kh,
                       int kw, int stride, int pad, tg_dtype dtype, tg_kernel kernel,
-                      tg_dispatch table) {
+                      tg_dispatch table, tg_activation act = TG_ACT_SILU) {
     if (!out) return TG_ERR_INVALID_ARGUMENT;
     *out = nullptr;
     ConvGeom g;
@@ -216,6 +218,16 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
     bool unfused = (kv & TG_UNFUSED) != 0;
     bool split = (kv & TG_SPLIT) != 0;
     if (unfused && split) return TG_ERR_UNSUPPORTED;
+    int epi;
+    switch (act) {
+        case TG_ACT_SILU: epi = EPI_FUSED; break;
+        case TG_ACT_RELU: epi = EPI_RELU; break;
+        case TG_ACT_GELU: epi = EPI_GELU; break;
+        case TG_ACT_NONE: epi = EPI_BN; break;
+        default: return TG_ERR_UNSUPPORTED;
+    }
+    // The baselines' streaming kernels apply BatchNorm and SiLU only.
+    if ((unfused || split) && epi != EPI_FUSED) return TG_ERR_UNSUPPORTED;
     int base = kv & ~(TG_UNFUSED | TG_SPLIT);
     if (base < TG_KERNEL_AUTO || base > TG_KERNEL_IGEMM) return TG_ERR_UNSUPPORTED;
 
@@ -225,6 +237,7 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
     p.dtype = dtype;
     p.unfused = unfused;
     p.split = split;
+    p.epi = epi;
     p.forced = base != TG_KERNEL_AUTO;
     p.dma_cfg = -1;
     p.patch_cfg = -1;
@@ -296,8 +309,8 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
 }
 
 // Launch the plan's conv kernel (or `kernel`, after an alignment fallback)
-// writing `out`, with the fused or the identity epilogue.
-hipError_t launch_conv(const tg_conv_bn_silu_plan* plan, int kernel, bool identity, const void* x,
+// writing `out`, with epilogue `epi` (tg::Epilogue).
+hipError_t launch_conv(const tg_conv_bn_silu_plan* plan, int kernel, int epi, const void* x,
                        const void* w, const float* bn_scale, const float* bn_bias, void* conv_out,
                        hipStream_t s) {
     const ConvGeom& g = plan->g;
@@ -306,39 +319,40 @@ hipError_t launch_conv(const tg_conv_bn_silu_plan* plan, int kernel, bool identi
     switch (kernel) {
         case TG_KERNEL_IGEMM:
             if (plan->cu_waves > 0 && aligned16(bn_scale) && aligned16(bn_bias))
-                e = launch_igemm_cu(g, plan->cu_waves, plan->cu_pd, plan->rw_nt, identity, x, w,
+                e = launch_igemm_cu(g, plan->cu_waves, plan->cu_pd, plan->rw_nt, epi, x, w,
                                     bn_scale, bn_bias, conv_out, s);
-            else if (plan->igemm_cfg < 0 && env_int("TG_STREAM", 0) > 0)
-                e = launch_igemm_stream(g, env_int("TG_STREAM", 16), plan->rw_nt, identity, x, w,
+            else if (plan->igemm_cfg < 0 && env_int("TG_STREAM", 0) > 0 &&
+                     (epi == EPI_FUSED || epi == EPI_IDENTITY))
+                e = launch_igemm_stream(g, env_int("TG_STREAM", 16), plan->rw_nt, epi, x, w,
                                         bn_scale, bn_bias, conv_out, s);
             else if (plan->patch_cfg >= 0)
-                e = launch_igemm_patch(g, plan->patch_cfg, identity, x, w, bn_scale, bn_bias,
+                e = launch_igemm_patch(g, plan->patch_cfg, epi, x, w, bn_scale, bn_bias,
                                        conv_out, s);
             else if (plan->dma_cfg >= 0)
-                e = launch_igemm_dma(g, plan->dma_cfg, identity, x, w, bn_scale, bn_bias, conv_out,
+                e = launch_igemm_dma(g, plan->dma_cfg, epi, x, w, bn_scale, bn_bias, conv_out,
                                      s);
             else if (plan->igemm_cfg < 0)
                 e = launch_igemm_rw(g, plan->rw_grid, plan->rw_nf, plan->rw_cs, plan->rw_ncw,
-                                    plan->rw_nt, identity, x, w, bn_scale, bn_bias, conv_out, s);
+                                    plan->rw_nt, epi, x, w, bn_scale, bn_bias, conv_out, s);
             else
-                e = launch_igemm(g, plan->igemm_cfg, identity, x, w, bn_scale, bn_bias, conv_out,
+                e = launch_igemm(g, plan->igemm_cfg, epi, x, w, bn_scale, bn_bias, conv_out,
                                  s);
             break;
         case TG_KERNEL_TILED:
             if (plan->stem_wpc > 0)
-                e = launch_stem(g, plan->stem_wpc, plan->stem_rows, identity, x, w, bn_scale, bn_bias,
+                e = launch_stem(g, plan->stem_wpc, plan->stem_rows, epi, x, w, bn_scale, bn_bias,
                                 conv_out, s);
             else if (plan->tm_pipe_grid > 0)
-                e = launch_tiled_mfma_pipe(g, plan->tm_rows, plan->tm_pipe_grid, identity, x, w,
+                e = launch_tiled_mfma_pipe(g, plan->tm_rows, plan->tm_pipe_grid, epi, x, w,
                                            bn_scale, bn_bias, conv_out, s);
             else if (plan->tm_rows > 0)
-                e = launch_tiled_mfma(g, plan->tm_rows, identity, x, w, bn_scale, bn_bias,
+                e = launch_tiled_mfma(g, plan->tm_rows, epi, x, w, bn_scale, bn_bias,
                                       conv_out, s);
             else
-                e = launch_tiled(g, plan->tiled, identity, x, w, bn_scale, bn_bias, conv_out, s);
+                e = launch_tiled(g, plan->tiled, epi, x, w, bn_scale, bn_bias, conv_out, s);
             break;
         default:
-            e = launch_scalar(g, f32, identity, x, w, bn_scale, bn_bias, conv_out, s);
+            e = launch_scalar(g, f32, epi, x, w, bn_scale, bn_bias, conv_out, s);
             break;
     }
     return e;
@@ -380,6 +394,13 @@ tg_status tg_conv_bn_silu_create_with_table(tg_conv_bn_silu_plan** out, int N, i
     return create_impl(out, N, H, W, C_in, C_out, kh, kw, stride, pad, dtype, kernel, table);
 }
 
+tg_status tg_conv_bn_act_create(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
+                                int C_out, int kh, int kw, int stride, int pad, tg_dtype dtype,
+                                tg_kernel kernel, tg_activation act) {
+    return create_impl(out, N, H, W, C_in, C_out, kh, kw, stride, pad, dtype, kernel,
+                       TG_DISPATCH_MI355X, act);
+}
+
 tg_status tg_conv_bn_silu_destroy(tg_conv_bn_silu_plan* plan) {
     delete plan;
     return TG_OK;
@@ -409,8 +430,8 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, c
             kernel = TG_KERNEL_SCALAR;
         }
     }
-    bool identity = plan->unfused || plan->split;
-    hipError_t e = launch_conv(plan, kernel, identity, x, w, bn_scale, bn_bias, conv_out, s);
+    const int epi = plan->unfused || plan->split ? EPI_IDENTITY : plan->epi;
+    hipError_t e = launch_conv(plan, kernel, epi, x, w, bn_scale, bn_bias, conv_out, s);
     if (e != hipSuccess) {
         if (env_flag("TG_LOG")) fprintf(stderr, "[tgconv] launch failed: %s\n", hipGetErrorString(e));
         return TG_ERR_HIP;
@@ -445,6 +466,7 @@ tg_status tg_conv_bn_silu_train_run(const tg_conv_bn_silu_plan* plan, const void
     if (!(eps >= 0.0f) || !(momentum >= 0.0f && momentum <= 1.0f)) return TG_ERR_INVALID_ARGUMENT;
     const ConvGeom& g = plan->g;
     if (g.M < 2) return TG_ERR_INVALID_ARGUMENT;  // batch statistics need two values per channel
+    if (plan->epi != EPI_FUSED) return TG_ERR_UNSUPPORTED;  // SiLU only
     const TrainWs L = train_ws(plan);
     if (!workspace || workspace_bytes < L.total) return TG_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
@@ -461,7 +483,7 @@ tg_status tg_conv_bn_silu_train_run(const tg_conv_bn_silu_plan* plan, const void
     float* bias = (float*)(ws + L.bias);
     double* partial = (double*)(ws + L.partial);
     // 1. conv -> t1 (identity epilogue: scale/bias are not read)
-    hipError_t e = launch_conv(plan, kernel, true, x, w, scale, bias, t1, s);
+    hipError_t e = launch_conv(plan, kernel, EPI_IDENTITY, x, w, scale, bias, t1, s);
     if (e != hipSuccess) return TG_ERR_HIP;
     // 2-3. batch statistics -> scale, bias, running estimates
     e = launch_bn_train_stats(f32, t1, g.M, g.C_out, gamma, beta, eps, momentum, running_mean,
@@ -566,8 +588,11 @@ tg_status tg_conv_bn_silu_describe(const tg_conv_bn_silu_plan* plan, char* buf, 
     } else {
         snprintf(k, sizeof(k), "scalar grid=%d", (g.M * g.C_out + 255) / 256);
     }
-    snprintf(buf, len, "%s%s %s N=%d H=%d W=%d C_in=%d C_out=%d k=%dx%d s=%d p=%d -> %dx%d",
-             plan->unfused ? "unfused:" : (plan->split ? "split:" : ""), k, plan->dtype == TG_F16 ? "f16" : "f32", g.N, g.H,
+    const char* act = plan->epi == EPI_RELU ? " act=relu"
+                      : plan->epi == EPI_GELU ? " act=gelu"
+                      : plan->epi == EPI_BN   ? " act=none" : "";
+    snprintf(buf, len, "%s%s%s %s N=%d H=%d W=%d C_in=%d C_out=%d k=%dx%d s=%d p=%d -> %dx%d",
+             plan->unfused ? "unfused:" : (plan->split ? "split:" : ""), k, act, plan->dtype == TG_F16 ? "f16" : "f32", g.N, g.H,
              g.W, g.C_in, g.C_out, g.kh, g.kw, g.stride, g.pad, g.P, g.Q);
     return TG_OK;
 }

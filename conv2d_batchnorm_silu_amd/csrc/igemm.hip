@@ -226,25 +226,23 @@ int igemm_num_cfgs() { return (int)(sizeof(kCfgs) / sizeof(kCfgs[0])); }
 const IgemmCfg& igemm_cfg(int i) { return kCfgs[i]; }
 
 template <int BM, int BN, int BK, int WM, int WN>
-static hipError_t launch_one(const ConvGeom& g, bool identity, const void* x, const void* w,
+static hipError_t launch_one(const ConvGeom& g, int epi, const void* x, const void* w,
                              const float* scale, const float* bias, void* y, hipStream_t s) {
     int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.C_out + BN - 1) / BN;
     dim3 grid(tiles_m * tiles_n), block(256);
-    if (identity)
-        hipLaunchKernelGGL((conv2d_bn_silu_igemm<BM, BN, BK, WM, WN, EPI_IDENTITY>), grid, block, 0,
-                           s, (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, tiles_m,
-                           tiles_n);
-    else
-        hipLaunchKernelGGL((conv2d_bn_silu_igemm<BM, BN, BK, WM, WN, EPI_FUSED>), grid, block, 0, s,
-                           (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, tiles_m, tiles_n);
+#define TG_L(E)                                                                               \
+    hipLaunchKernelGGL((conv2d_bn_silu_igemm<BM, BN, BK, WM, WN, E>), grid, block, 0, s,        \
+                       (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, tiles_m, tiles_n)
+    TG_EPI_DISPATCH(epi, TG_L);
+#undef TG_L
     return hipGetLastError();
 }
 
-hipError_t launch_igemm(const ConvGeom& g, int cfg, bool identity, const void* x, const void* w,
+hipError_t launch_igemm(const ConvGeom& g, int cfg, int epi, const void* x, const void* w,
                         const float* scale, const float* bias, void* y, hipStream_t s) {
     int i = 0;
 #define X(bm, bn, bk, wm, wn)                                                                 \
-    if (cfg == i) return launch_one<bm, bn, bk, wm, wn>(g, identity, x, w, scale, bias, y, s); \
+    if (cfg == i) return launch_one<bm, bn, bk, wm, wn>(g, epi, x, w, scale, bias, y, s); \
     ++i;
     TG_IGEMM_CFGS(X)
 #undef X

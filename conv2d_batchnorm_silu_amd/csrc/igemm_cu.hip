@@ -178,8 +178,8 @@ __global__ __launch_bounds__(1024) void conv2d_bn_silu_igemm_cu(
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int o = c0 + 32 * j + 8 * lg + e;
-            sc[j][e] = EPI == EPI_FUSED ? ((const float*)(lds + L.s_off))[o] * kLog2e : 0.f;
-            bi[j][e] = EPI == EPI_FUSED ? ((const float*)(lds + L.b_off))[o] * kLog2e : 0.f;
+            sc[j][e] = epi_scale<EPI>(((const float*)(lds + L.s_off))[o]);
+            bi[j][e] = epi_scale<EPI>(((const float*)(lds + L.b_off))[o]);
         }
 
     f16* tl = (f16*)(lds + L.t_off) + wave * 16 * kCuTrow;
@@ -275,7 +275,7 @@ int igemm_cu_waves(const ConvGeom& g, int per_group) {
     return ng * r;
 }
 
-hipError_t launch_igemm_cu(const ConvGeom& g, int nwaves, int pd, bool nt, bool identity,
+hipError_t launch_igemm_cu(const ConvGeom& g, int nwaves, int pd, bool nt, int epi,
                            const void* x, const void* w, const float* scale, const float* bias,
                            void* y, hipStream_t s) {
     if (!igemm_cu_serves(g) || nwaves < 1 || nwaves > 16 || nwaves % (g.C_out / kCuCW) != 0)
@@ -291,11 +291,14 @@ hipError_t launch_igemm_cu(const ConvGeom& g, int nwaves, int pd, bool nt, bool 
         if (pd == 2) TG_CU(EPI, NTV, 2); \
         TG_CU(EPI, NTV, 3);             \
     } while (0)
-    if (identity) {
-        if (nt) TG_CU_PD(EPI_IDENTITY, true); else TG_CU_PD(EPI_IDENTITY, false);
-    } else {
-        if (nt) TG_CU_PD(EPI_FUSED, true); else TG_CU_PD(EPI_FUSED, false);
-    }
+#define TG_CU_NT(E)                       \
+    do {                                  \
+        if (nt) TG_CU_PD(E, true);        \
+        else TG_CU_PD(E, false);          \
+    } while (0)
+    TG_EPI_DISPATCH(epi, TG_CU_NT);
+#undef TG_CU_NT
+    return hipErrorInvalidValue;
 #undef TG_CU_PD
 #undef TG_CU
 }

@@ -296,20 +296,23 @@ bool igemm_dma_serves(const ConvGeom& g) {
 }
 
 template <int BM, int BN, int WM, int WN, int RING, int WK>
-static hipError_t dma_launch_one(const ConvGeom& g, bool identity, const void* x, const void* w,
+static hipError_t dma_launch_one(const ConvGeom& g, int epi, const void* x, const void* w,
                                  const float* scale, const float* bias, void* y, hipStream_t s) {
     using S = DmaShape<BM, BN, WM, WN, RING, WK>;
     const int tiles_m = (g.M + BM - 1) / BM, tiles_n = (g.C_out + BN - 1) / BN;
     const size_t lds = (size_t)S::SMEM * 2;
     static_assert(S::SMEM * 2 <= 160 * 1024, "LDS budget");
-    auto k = identity ? conv2d_bn_silu_igemm_dma<BM, BN, WM, WN, RING, WK, EPI_IDENTITY>
-                      : conv2d_bn_silu_igemm_dma<BM, BN, WM, WN, RING, WK, EPI_FUSED>;
-    static bool attr_set[2] = {false, false};
-    if (!attr_set[identity ? 1 : 0]) {
+    if (epi < 0 || epi >= kNumEpilogues) return hipErrorInvalidValue;
+    auto k = conv2d_bn_silu_igemm_dma<BM, BN, WM, WN, RING, WK, EPI_FUSED>;
+#define TG_K(E) k = conv2d_bn_silu_igemm_dma<BM, BN, WM, WN, RING, WK, E>
+    TG_EPI_DISPATCH(epi, TG_K);
+#undef TG_K
+    static bool attr_set[kNumEpilogues] = {};
+    if (!attr_set[epi]) {
         hipError_t e = hipFuncSetAttribute((const void*)k,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
-        attr_set[identity ? 1 : 0] = true;
+        attr_set[epi] = true;
     }
     hipLaunchKernelGGL(k, dim3(tiles_m * tiles_n), dim3(64 * S::NW), lds, s, (const f16*)x,
                        (const f16*)w,
@@ -317,12 +320,12 @@ static hipError_t dma_launch_one(const ConvGeom& g, bool identity, const void* x
     return hipGetLastError();
 }
 
-hipError_t launch_igemm_dma(const ConvGeom& g, int cfg, bool identity, const void* x,
+hipError_t launch_igemm_dma(const ConvGeom& g, int cfg, int epi, const void* x,
                             const void* w, const float* scale, const float* bias, void* y,
                             hipStream_t s) {
     int i = 0;
 #define X(bm, bn, wm, wn, ring, wk)                                                         \
-    if (cfg == i) return dma_launch_one<bm, bn, wm, wn, ring, wk>(g, identity, x, w, scale, \
+    if (cfg == i) return dma_launch_one<bm, bn, wm, wn, ring, wk>(g, epi, x, w, scale,      \
                                                                   bias, y, s);              \
     ++i;
     TG_DMA_CFGS(X)

@@ -520,17 +520,20 @@ size_t patch_lds_bytes(const ConvGeom& g, const PatchCfg& c) {
 }
 
 template <int BM, int BN, int WM, int WN, int WK, int RING>
-hipError_t patch_launch_one(const ConvGeom& g, bool identity, const void* x, const void* w,
+hipError_t patch_launch_one(const ConvGeom& g, int epi, const void* x, const void* w,
                             const float* scale, const float* bias, void* y, hipStream_t s) {
     using S = PatchShape<BM, BN, WM, WN, WK, RING>;
     const PatchCfg c = {BM, BN, WM, WN, WK, RING};
     const size_t lds = patch_lds_bytes(g, c);
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     const int tiles_per_img = (g.P * g.Q + BM - 1) / BM, tiles_n = (g.C_out + BN - 1) / BN;
-    auto k = identity ? conv2d_bn_silu_igemm_patch<BM, BN, WM, WN, WK, RING, EPI_IDENTITY>
-                      : conv2d_bn_silu_igemm_patch<BM, BN, WM, WN, WK, RING, EPI_FUSED>;
-    static size_t attr_bytes[2] = {0, 0};
-    size_t& ab = attr_bytes[identity ? 1 : 0];
+    if (epi < 0 || epi >= kNumEpilogues) return hipErrorInvalidValue;
+    auto k = conv2d_bn_silu_igemm_patch<BM, BN, WM, WN, WK, RING, EPI_FUSED>;
+#define TG_K(E) k = conv2d_bn_silu_igemm_patch<BM, BN, WM, WN, WK, RING, E>
+    TG_EPI_DISPATCH(epi, TG_K);
+#undef TG_K
+    static size_t attr_bytes[kNumEpilogues] = {};
+    size_t& ab = attr_bytes[epi];
     if (lds > ab) {
         hipError_t e = hipFuncSetAttribute((const void*)k,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -599,14 +602,14 @@ void igemm_patch_describe(int cfg, int* BM, int* BN, int* WM, int* WN, int* WK, 
     *BM = c.BM; *BN = c.BN; *WM = c.WM; *WN = c.WN; *WK = c.WK; *ring = c.RING;
 }
 
-hipError_t launch_igemm_patch(const ConvGeom& g, int cfg, bool identity, const void* x,
+hipError_t launch_igemm_patch(const ConvGeom& g, int cfg, int epi, const void* x,
                               const void* w, const float* scale, const float* bias, void* y,
                               hipStream_t s) {
     if (!igemm_patch_fits(g, cfg)) return hipErrorInvalidValue;
     int i = 0;
 #define X(bm, bn, wm, wn, wk, ring)                                                   \
     if (cfg == i)                                                                       \
-        return patch_launch_one<bm, bn, wm, wn, wk, ring>(g, identity, x, w, scale, bias, y, s); \
+        return patch_launch_one<bm, bn, wm, wn, wk, ring>(g, epi, x, w, scale, bias, y, s); \
     ++i;
     TG_PATCH_CFGS(X)
 #undef X

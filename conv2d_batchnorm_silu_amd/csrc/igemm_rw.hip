@@ -460,7 +460,7 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_igemm_stream(
     }
 }
 
-hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, bool nt, bool identity,
+hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, bool nt, int epi,
                                const void* x, const void* w, const float* scale,
                                const float* bias, void* y, hipStream_t s) {
     const int NF = 4, CW = 64;
@@ -496,6 +496,9 @@ hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, bool nt, boo
     hipLaunchKernelGGL((conv2d_bn_silu_igemm_stream<NF, KSV, EPI, NTV, XD, PDV>), dim3(grid),    \
                        dim3(256), 0, s, (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g,   \
                        nblocks, ngroups)
+    // (tuning variant: BatchNorm+SiLU and identity epilogues only)
+    if (epi != EPI_FUSED && epi != EPI_IDENTITY) return hipErrorInvalidValue;
+    const bool identity = epi == EPI_IDENTITY;
     if (ks == 1) {
         if (identity) { if (nt) TG_ST_LAUNCH(1, EPI_IDENTITY, true); else TG_ST_LAUNCH(1, EPI_IDENTITY, false); }
         else { if (nt) TG_ST_LAUNCH(1, EPI_FUSED, true); else TG_ST_LAUNCH(1, EPI_FUSED, false); }
@@ -543,7 +546,7 @@ int igemm_rw_grid(const ConvGeom& g, int slots) {
 }
 
 template <int NF, int KS, int CS, int NCW>
-static void launch_rw_one(const ConvGeom& g, int grid, bool identity, bool nt, const void* x,
+static void launch_rw_one(const ConvGeom& g, int grid, int epi, bool nt, const void* x,
                           const void* w, const float* scale, const float* bias, void* y,
                           hipStream_t s) {
     int nblocks = (g.M + 15) / 16;
@@ -551,22 +554,24 @@ static void launch_rw_one(const ConvGeom& g, int grid, bool identity, bool nt, c
     hipLaunchKernelGGL((conv2d_bn_silu_igemm_rw<NF, KS, CS, NCW, EPI, NTV>), dim3(grid),     \
                        dim3((NCW + 1) * 64), 0, s, (const f16*)x, (const f16*)w, scale, bias, \
                        (f16*)y, g, nblocks)
-    if (identity) {
-        if (nt) TG_RW_LAUNCH(EPI_IDENTITY, true); else TG_RW_LAUNCH(EPI_IDENTITY, false);
-    } else {
-        if (nt) TG_RW_LAUNCH(EPI_FUSED, true); else TG_RW_LAUNCH(EPI_FUSED, false);
-    }
+#define TG_RW_NT(E)                \
+    do {                           \
+        if (nt) TG_RW_LAUNCH(E, true); \
+        else TG_RW_LAUNCH(E, false);   \
+    } while (0)
+    TG_EPI_DISPATCH(epi, TG_RW_NT);
+#undef TG_RW_NT
 #undef TG_RW_LAUNCH
 }
 
 hipError_t launch_igemm_rw(const ConvGeom& g, int grid, int nf, int cs, int ncw, bool nt,
-                           bool identity, const void* x, const void* w, const float* scale,
+                           int epi, const void* x, const void* w, const float* scale,
                            const float* bias, void* y, hipStream_t s) {
     int ks = g.K <= 32 ? 1 : 2;
     if (nf * 16 * cs < g.C_out) return hipErrorInvalidValue;
 #define X(NF_, KS_, CS_, NCW_)                                                               \
     if (nf == NF_ && ks == KS_ && cs == CS_ && ncw == NCW_) {                                \
-        launch_rw_one<NF_, KS_, CS_, NCW_>(g, grid, identity, nt, x, w, scale, bias, y, s); \
+        launch_rw_one<NF_, KS_, CS_, NCW_>(g, grid, epi, nt, x, w, scale, bias, y, s);     \
         return hipGetLastError();                                                            \
     }
     TG_RW_CFGS(X)

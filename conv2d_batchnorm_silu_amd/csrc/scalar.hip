@@ -42,25 +42,22 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_scalar(
     y[idx] = from_f32<T>(epilogue<EPI>(acc, sc, bi));
 }
 
-hipError_t launch_scalar(const ConvGeom& g, bool f32, bool identity, const void* x, const void* w,
+hipError_t launch_scalar(const ConvGeom& g, bool f32, int epi, const void* x, const void* w,
                          const float* scale, const float* bias, void* y, hipStream_t s) {
     int total = g.M * g.C_out;  // < 2^31, checked at plan time
     dim3 grid((total + 255) / 256), block(256);
-    if (f32) {
-        if (identity)
-            hipLaunchKernelGGL((conv2d_bn_silu_scalar<float, EPI_IDENTITY>), grid, block, 0, s,
-                               (const float*)x, (const float*)w, scale, bias, (float*)y, g, total);
-        else
-            hipLaunchKernelGGL((conv2d_bn_silu_scalar<float, EPI_FUSED>), grid, block, 0, s,
-                               (const float*)x, (const float*)w, scale, bias, (float*)y, g, total);
-    } else {
-        if (identity)
-            hipLaunchKernelGGL((conv2d_bn_silu_scalar<f16, EPI_IDENTITY>), grid, block, 0, s,
-                               (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, total);
-        else
-            hipLaunchKernelGGL((conv2d_bn_silu_scalar<f16, EPI_FUSED>), grid, block, 0, s,
-                               (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, total);
-    }
+#define TG_S32(E)                                                                \
+    hipLaunchKernelGGL((conv2d_bn_silu_scalar<float, E>), grid, block, 0, s,       \
+                       (const float*)x, (const float*)w, scale, bias, (float*)y, g, total)
+#define TG_S16(E)                                                                \
+    hipLaunchKernelGGL((conv2d_bn_silu_scalar<f16, E>), grid, block, 0, s,         \
+                       (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, total)
+    if (f32)
+        TG_EPI_DISPATCH(epi, TG_S32);
+    else
+        TG_EPI_DISPATCH(epi, TG_S16);
+#undef TG_S16
+#undef TG_S32
     return hipGetLastError();
 }
 

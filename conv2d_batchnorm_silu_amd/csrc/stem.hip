@@ -312,7 +312,7 @@ bool stem_serves(const ConvGeom& g) {
            6LL * g.N * g.H * g.W < (1LL << 31);
 }
 
-hipError_t launch_stem(const ConvGeom& g, int wg_per_cu, int R, bool identity, const void* x,
+hipError_t launch_stem(const ConvGeom& g, int wg_per_cu, int R, int epi, const void* x,
                        const void* w, const float* scale, const float* bias, void* y,
                        hipStream_t s) {
     if (!stem_serves(g) || !stem_rows_ok(g, R)) return hipErrorInvalidValue;
@@ -350,14 +350,13 @@ hipError_t launch_stem(const ConvGeom& g, int wg_per_cu, int R, bool identity, c
         if (li <= 24) TG_STEM_K(NBV, EPI, 24); \
         TG_STEM_K(NBV, EPI, 31);               \
     } while (0)
-#define TG_STEM(NBV)                                 \
-    do {                                             \
-        if (identity) TG_STEM_LI(NBV, EPI_IDENTITY); \
-        else TG_STEM_LI(NBV, EPI_FUSED);             \
-    } while (0)
-    if (nb == 1) TG_STEM(1);
-    TG_STEM(2);
-#undef TG_STEM
+#define TG_STEM_1(E) TG_STEM_LI(1, E)
+#define TG_STEM_2(E) TG_STEM_LI(2, E)
+    if (nb == 1) TG_EPI_DISPATCH(epi, TG_STEM_1);
+    TG_EPI_DISPATCH(epi, TG_STEM_2);
+    return hipErrorInvalidValue;
+#undef TG_STEM_2
+#undef TG_STEM_1
 #undef TG_STEM_LI
 #undef TG_STEM_K
 }

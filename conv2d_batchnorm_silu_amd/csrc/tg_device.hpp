@@ -20,8 +20,25 @@ typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Epilogue selector: FUSED applies BatchNorm + SiLU; IDENTITY stores the raw
-// convolution (the first kernel of the unfused three-kernel baseline).
-enum Epilogue { EPI_FUSED = 0, EPI_IDENTITY = 1 };
+// convolution (the first kernel of the unfused, split and training-mode
+// paths); RELU, GELU and BN apply BatchNorm and then max(v, 0), the exact
+// GELU v * Phi(v), or nothing -- the other elementwise work "Fusing an
+// Epilogue" (section "What an epilogue is") lists as belonging in the
+// producer's epilogue (activations, bias adds, scaling).
+enum Epilogue { EPI_FUSED = 0, EPI_IDENTITY = 1, EPI_RELU = 2, EPI_GELU = 3, EPI_BN = 4 };
+constexpr int kNumEpilogues = 5;
+
+// Instantiate X(E) for the run-time epilogue `epi` (one of the above).
+#define TG_EPI_DISPATCH(epi, X)                               \
+    do {                                                      \
+        switch (epi) {                                        \
+            case ::tg::EPI_IDENTITY: X(::tg::EPI_IDENTITY); break; \
+            case ::tg::EPI_RELU: X(::tg::EPI_RELU); break;     \
+            case ::tg::EPI_GELU: X(::tg::EPI_GELU); break;     \
+            case ::tg::EPI_BN: X(::tg::EPI_BN); break;         \
+            default: X(::tg::EPI_FUSED); break;               \
+        }                                                     \
+    } while (0)
 
 // sigmoid(v) = 1 / (1 + e^-v), with e^-v = 2^(-v * log2 e) on the hardware
 // exp2 (v_exp_f32) and the hardware reciprocal (v_rcp_f32). For v below about
@@ -46,20 +63,30 @@ __device__ __forceinline__ float silu_f32(float v) {
 // of branching around the load, so all of a kernel's constant loads are in
 // flight together and its prologue waits for one memory latency, not one per
 // channel. The identity epilogue loads nothing.
+// The other BatchNorm epilogues keep scale and bias as they are (epi_scale).
+template <int EPI>
+__device__ __forceinline__ float epi_scale(float c) {
+    return EPI == EPI_FUSED ? c * kLog2e : (EPI == EPI_IDENTITY ? 0.0f : c);
+}
+
 template <int EPI>
 __device__ __forceinline__ void epi_consts(const float* __restrict__ scale,
                                            const float* __restrict__ bias, int o, int C_out,
                                            float& s2, float& b2) {
-    if (EPI != EPI_FUSED) {
+    if (EPI == EPI_IDENTITY) {
         s2 = b2 = 0.0f;
         return;
     }
     const bool ok = o < C_out;
     const int oc = ok ? o : C_out - 1;
     const float s = scale[oc], b = bias[oc];
-    s2 = ok ? s * kLog2e : 0.0f;
-    b2 = ok ? b * kLog2e : 0.0f;
+    s2 = ok ? epi_scale<EPI>(s) : 0.0f;
+    b2 = ok ? epi_scale<EPI>(b) : 0.0f;
 }
+
+// GELU(v) = v * Phi(v) = v/2 * (1 + erf(v / sqrt 2)), with the device
+// library's single-precision erf.
+constexpr float kRsqrt2 = 0.70710678118654752f;
 
 template <int EPI>
 __device__ __forceinline__ float epilogue(float acc, float s2, float b2) {
@@ -69,7 +96,11 @@ __device__ __forceinline__ float epilogue(float acc, float s2, float b2) {
         float d = __builtin_fmaf(e, kLog2e, kLog2e);
         return v2 * __builtin_amdgcn_rcpf(d);
     }
-    return acc;
+    if (EPI == EPI_IDENTITY) return acc;
+    const float v = __builtin_fmaf(acc, s2, b2);
+    if (EPI == EPI_RELU) return v > 0.0f ? v : 0.0f;
+    if (EPI == EPI_GELU) return 0.5f * v * (1.0f + erff(v * kRsqrt2));
+    return v;  // EPI_BN
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v) { return (float)v; }

@@ -35,12 +35,12 @@ struct TiledCfg {
 // Largest band that fits; returns false when the shape cannot be served.
 bool tiled_plan(const ConvGeom& g, TiledCfg* out);
 
-hipError_t launch_scalar(const ConvGeom& g, bool f32, bool identity, const void* x, const void* w,
+hipError_t launch_scalar(const ConvGeom& g, bool f32, int epi, const void* x, const void* w,
                          const float* scale, const float* bias, void* y, hipStream_t s);
-hipError_t launch_tiled(const ConvGeom& g, const TiledCfg& c, bool identity, const void* x,
+hipError_t launch_tiled(const ConvGeom& g, const TiledCfg& c, int epi, const void* x,
                         const void* w, const float* scale, const float* bias, void* y,
                         hipStream_t s);
-hipError_t launch_igemm(const ConvGeom& g, int cfg, bool identity, const void* x, const void* w,
+hipError_t launch_igemm(const ConvGeom& g, int cfg, int epi, const void* x, const void* w,
                         const float* scale, const float* bias, void* y, hipStream_t s);
 // Register-resident-weights implicit GEMM (igemm_rw.hip): K <= 64, C_out <= 256.
 bool igemm_rw_serves(const ConvGeom& g);
@@ -48,9 +48,9 @@ void igemm_rw_choose(const ConvGeom& g, int* nf, int* cs, int* ncw);
 bool igemm_rw_valid(const ConvGeom& g, int nf, int cs, int ncw);
 int igemm_rw_grid(const ConvGeom& g, int slots);
 hipError_t launch_igemm_rw(const ConvGeom& g, int grid, int nf, int cs, int ncw, bool nt,
-                           bool identity, const void* x, const void* w, const float* scale,
+                           int epi, const void* x, const void* w, const float* scale,
                            const float* bias, void* y, hipStream_t s);
-hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, bool nt, bool identity,
+hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, bool nt, int epi,
                                const void* x, const void* w, const float* scale,
                                const float* bias, void* y, hipStream_t s);
 
@@ -59,14 +59,14 @@ hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, bool nt, boo
 // multiple of C_out/64 (at most 16); pd is the input prefetch depth (1..3).
 bool igemm_cu_serves(const ConvGeom& g);
 int igemm_cu_waves(const ConvGeom& g, int per_group);
-hipError_t launch_igemm_cu(const ConvGeom& g, int nwaves, int pd, bool nt, bool identity,
+hipError_t launch_igemm_cu(const ConvGeom& g, int nwaves, int pd, bool nt, int epi,
                            const void* x, const void* w, const float* scale, const float* bias,
                            void* y, hipStream_t s);
 // Direct-to-LDS pipelined implicit GEMM (igemm_dma.hip): C_in % 64 == 0.
 bool igemm_dma_serves(const ConvGeom& g);
 int igemm_dma_num_cfgs();
 const IgemmCfg& igemm_dma_cfg(int i);
-hipError_t launch_igemm_dma(const ConvGeom& g, int cfg, bool identity, const void* x,
+hipError_t launch_igemm_dma(const ConvGeom& g, int cfg, int epi, const void* x,
                             const void* w, const float* scale, const float* bias, void* y,
                             hipStream_t s);
 // Patch-staged implicit GEMM (igemm_patch.hip): stride 1, C_in % 64 == 0,
@@ -76,7 +76,7 @@ int igemm_patch_num_cfgs();
 bool igemm_patch_fits(const ConvGeom& g, int cfg);
 int igemm_patch_choose(const ConvGeom& g);
 void igemm_patch_describe(int cfg, int* BM, int* BN, int* WM, int* WN, int* WK, int* ring);
-hipError_t launch_igemm_patch(const ConvGeom& g, int cfg, bool identity, const void* x,
+hipError_t launch_igemm_patch(const ConvGeom& g, int cfg, int epi, const void* x,
                               const void* w, const float* scale, const float* bias, void* y,
                               hipStream_t s);
 // Stem kernel (stem.hip): C_in = 3, 3x3, stride 2, pad 1, even W, C_out % 8 == 0
@@ -84,17 +84,17 @@ hipError_t launch_igemm_patch(const ConvGeom& g, int cfg, bool identity, const v
 bool stem_serves(const ConvGeom& g);
 int stem_rows(const ConvGeom& g);
 bool stem_rows_ok(const ConvGeom& g, int R);
-hipError_t launch_stem(const ConvGeom& g, int wg_per_cu, int R, bool identity, const void* x,
+hipError_t launch_stem(const ConvGeom& g, int wg_per_cu, int R, int epi, const void* x,
                        const void* w, const float* scale, const float* bias, void* y,
                        hipStream_t s);
 // Tiled direct conv on MFMA (tiled_mfma.hip): K <= 32, C_out <= 32.
 bool tiled_mfma_serves(const ConvGeom& g);
 int tiled_mfma_rows(const ConvGeom& g);
-hipError_t launch_tiled_mfma(const ConvGeom& g, int R, bool identity, const void* x,
+hipError_t launch_tiled_mfma(const ConvGeom& g, int R, int epi, const void* x,
                              const void* w, const float* scale, const float* bias, void* y,
                              hipStream_t s);
 bool tiled_mfma_pipe_serves(const ConvGeom& g);
-hipError_t launch_tiled_mfma_pipe(const ConvGeom& g, int R, int grid, bool identity,
+hipError_t launch_tiled_mfma_pipe(const ConvGeom& g, int R, int grid, int epi,
                                   const void* x, const void* w, const float* scale,
                                   const float* bias, void* y, hipStream_t s);
 hipError_t launch_bn_apply(bool f32, const void* t1, const float* scale, const float* bias, void* t2,

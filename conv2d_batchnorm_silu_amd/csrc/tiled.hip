@@ -129,17 +129,16 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_tiled(
     }
 }
 
-hipError_t launch_tiled(const ConvGeom& g, const TiledCfg& c, bool identity, const void* x,
+hipError_t launch_tiled(const ConvGeom& g, const TiledCfg& c, int epi, const void* x,
                         const void* w, const float* scale, const float* bias, void* y,
                         hipStream_t s) {
     int bands = (g.P + c.R - 1) / c.R;
     dim3 grid(g.N * bands), block(256);
-    if (identity)
-        hipLaunchKernelGGL(conv2d_bn_silu_tiled<EPI_IDENTITY>, grid, block, c.lds_bytes, s,
-                           (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, c.R, c.WPad);
-    else
-        hipLaunchKernelGGL(conv2d_bn_silu_tiled<EPI_FUSED>, grid, block, c.lds_bytes, s,
-                           (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, c.R, c.WPad);
+#define TG_T(E)                                                                        \
+    hipLaunchKernelGGL(conv2d_bn_silu_tiled<E>, grid, block, c.lds_bytes, s, (const f16*)x, \
+                       (const f16*)w, scale, bias, (f16*)y, g, c.R, c.WPad)
+    TG_EPI_DISPATCH(epi, TG_T);
+#undef TG_T
     return hipGetLastError();
 }
 

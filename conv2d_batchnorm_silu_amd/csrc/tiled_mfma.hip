@@ -340,7 +340,7 @@ int tiled_mfma_pipe_lds(const ConvGeom& g, int R, int* in_halves) {
     return 2 * chunks * 1024 + (R * g.Q * g.C_out * 2 + 15) / 16 * 16;
 }
 
-hipError_t launch_tiled_mfma_pipe(const ConvGeom& g, int R, int grid, bool identity,
+hipError_t launch_tiled_mfma_pipe(const ConvGeom& g, int R, int grid, int epi,
                                   const void* x, const void* w, const float* scale,
                                   const float* bias, void* y, hipStream_t s) {
     int in_halves = 0;
@@ -352,16 +352,19 @@ hipError_t launch_tiled_mfma_pipe(const ConvGeom& g, int R, int grid, bool ident
     hipLaunchKernelGGL((conv2d_bn_silu_tiled_mfma_pipe<NFV, EPI>), dim3(grid), dim3(256), lds, \
                        s, (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, R, in_halves, \
                        nbands)
-    if (nf == 1) {
-        if (identity) TG_TMP_LAUNCH(1, EPI_IDENTITY); else TG_TMP_LAUNCH(1, EPI_FUSED);
-    } else {
-        if (identity) TG_TMP_LAUNCH(2, EPI_IDENTITY); else TG_TMP_LAUNCH(2, EPI_FUSED);
-    }
+#define TG_TMP_1(E) TG_TMP_LAUNCH(1, E)
+#define TG_TMP_2(E) TG_TMP_LAUNCH(2, E)
+    if (nf == 1)
+        TG_EPI_DISPATCH(epi, TG_TMP_1);
+    else
+        TG_EPI_DISPATCH(epi, TG_TMP_2);
+#undef TG_TMP_2
+#undef TG_TMP_1
 #undef TG_TMP_LAUNCH
     return hipGetLastError();
 }
 
-hipError_t launch_tiled_mfma(const ConvGeom& g, int R, bool identity, const void* x,
+hipError_t launch_tiled_mfma(const ConvGeom& g, int R, int epi, const void* x,
                              const void* w, const float* scale, const float* bias, void* y,
                              hipStream_t s) {
     const int bands = (g.P + R - 1) / R;
@@ -371,11 +374,14 @@ hipError_t launch_tiled_mfma(const ConvGeom& g, int R, bool identity, const void
 #define TG_TM_LAUNCH(NFV, EPI)                                                            \
     hipLaunchKernelGGL((conv2d_bn_silu_tiled_mfma<NFV, EPI>), grid, block, lds, s,         \
                        (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, R)
-    if (nf == 1) {
-        if (identity) TG_TM_LAUNCH(1, EPI_IDENTITY); else TG_TM_LAUNCH(1, EPI_FUSED);
-    } else {
-        if (identity) TG_TM_LAUNCH(2, EPI_IDENTITY); else TG_TM_LAUNCH(2, EPI_FUSED);
-    }
+#define TG_TM_1(E) TG_TM_LAUNCH(1, E)
+#define TG_TM_2(E) TG_TM_LAUNCH(2, E)
+    if (nf == 1)
+        TG_EPI_DISPATCH(epi, TG_TM_1);
+    else
+        TG_EPI_DISPATCH(epi, TG_TM_2);
+#undef TG_TM_2
+#undef TG_TM_1
 #undef TG_TM_LAUNCH
     return hipGetLastError();
 }

@@ -136,7 +136,8 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan *plan, const void *x, c
  * tg_conv_bn_silu_train_workspace, 16-byte aligned for the vector kernels,
  * not aliasing any other argument. Errors: TG_ERR_INVALID_ARGUMENT for a
  * NULL plan/x/w/gamma/beta/y, only one of running_mean/running_var given,
- * eps < 0, momentum outside [0, 1], or M < 2; TG_ERR_WORKSPACE;
+ * eps < 0, momentum outside [0, 1], or M < 2; TG_ERR_UNSUPPORTED for a plan
+ * whose activation is not SiLU; TG_ERR_WORKSPACE;
  * TG_ERR_ALIGNMENT (forced kernels only, as for run); TG_ERR_HIP. */
 tg_status tg_conv_bn_silu_train_run(const tg_conv_bn_silu_plan *plan, const void *x,
                                     const void *w, const float *gamma, const float *beta,
@@ -148,6 +149,25 @@ tg_status tg_conv_bn_silu_train_run(const tg_conv_bn_silu_plan *plan, const void
 /* Workspace bytes tg_conv_bn_silu_train_run needs for this plan (host only).
  * TG_ERR_INVALID_ARGUMENT for NULL arguments. */
 tg_status tg_conv_bn_silu_train_workspace(const tg_conv_bn_silu_plan *plan, size_t *bytes);
+
+/* Activation in the epilogue. The fused kernels apply, after the folded
+ * BatchNorm v = acc*bn_scale[k] + bn_bias[k], one of: SiLU v*sigmoid(v)
+ * (the default of every other create), ReLU max(v, 0), GELU in its exact
+ * form v*Phi(v) = v/2*(1 + erf(v/sqrt 2)), or nothing (BatchNorm only, i.e.
+ * a conv with a per-channel scale and bias). "Fusing an Epilogue", section
+ * "What an epilogue is": activations, bias adds and scaling are the
+ * elementwise work that belongs in the producer's epilogue. */
+typedef enum { TG_ACT_SILU = 0, TG_ACT_RELU = 1, TG_ACT_GELU = 2, TG_ACT_NONE = 3 } tg_activation;
+
+/* Same as tg_conv_bn_silu_create (MI355X dispatch table) with the epilogue's
+ * activation chosen; run() then applies it. TG_ERR_UNSUPPORTED for an
+ * unknown activation, or an activation other than SiLU together with
+ * TG_UNFUSED or TG_SPLIT (whose streaming kernels apply SiLU); a plan with
+ * an activation other than SiLU is rejected by tg_conv_bn_silu_train_run
+ * (TG_ERR_UNSUPPORTED). */
+tg_status tg_conv_bn_act_create(tg_conv_bn_silu_plan **out, int N, int H, int W, int C_in,
+                                int C_out, int kh, int kw, int stride, int pad, tg_dtype dtype,
+                                tg_kernel kernel, tg_activation act);
 
 /* Free a plan. NULL is a no-op. */
 tg_status tg_conv_bn_silu_destroy(tg_conv_bn_silu_plan *plan);
