@@ -282,6 +282,43 @@ def COPY_BYTES_MIB():
     return COPY_BYTES // 2**20
 
 
+def write_bench_table(path_json):
+    """profiles/bench_per_workload.md from the JSON line of a default
+    `python bench.py` run."""
+    with open(path_json) as f:
+        r = json.loads(f.read().strip().splitlines()[-1])
+    lines = ["# bench.py per-workload results on one MI355X (fused kernel chosen by the MI355X "
+             "dispatch table)",
+             "# command: python bench.py   (defaults: --steps %d --warmup %d; %s rotating "
+             "input/output sets per workload)" % (r["steps"], r["warmup"],
+                                                  r["config"].get("buffer_sets", "?")),
+             "# times: HIP events over the timed steps on the launch stream, divided by the step "
+             "count (includes launch gaps); timed calls go straight to the C ABI",
+             "# split = conv kernel + one BatchNorm+SiLU kernel; unfused = conv, BatchNorm, SiLU; "
+             "nchw legs = x NCHW->NHWC + fused + y NHWC->NCHW; train = batch-statistics "
+             "BatchNorm (conv, statistics, fold, BatchNorm+SiLU)",
+             "workload | kernel | us | TFLOP/s | GB/s (algorithmic) | bound | frac of bound peak "
+             "| unfused us | x vs unfused | split us | x vs split | relu / gelu / none us | "
+             "nchw legs us (share) | train us"]
+    for c in r["per_config"]:
+        a = c.get("act_us", {})
+        lines.append(" | ".join(str(v) for v in [
+            c["workload"], c["kernel"].split(" f16 ")[0].split(" f32 ")[0], c["us"], c["tflops"],
+            c["gbs"], c["bound"], c["frac"], c.get("unfused_us"), c.get("speedup_vs_unfused"),
+            c.get("split_us"), c.get("speedup_vs_split"),
+            "%s / %s / %s" % (a.get("relu"), a.get("gelu"), a.get("none")),
+            "%s (%s)" % (c.get("nchw_legs_us"), c.get("nchw_legs_share")), c.get("train_us")]))
+    if r.get("cpu_baseline"):
+        lines.append("cpu_baseline (fp64 oracle, headline workload): " +
+                     json.dumps(r["cpu_baseline"]))
+    lines.append("roofline (headline): " + json.dumps(r["roofline"]))
+    lines.append("value: %s %s (%s)" % (r["value"], r["unit"], r["config"]["workload"]))
+    path = os.path.join(PROFILES, "bench_per_workload.md")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("wrote " + path)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--raw", required=True, help="directory for raw rocprofv3 output")
@@ -290,6 +327,8 @@ def main():
     ap.add_argument("--counters", action="store_true")
     ap.add_argument("--workloads", default=None, help="comma-separated (default: all)")
     ap.add_argument("--dest", default=None, help="where the summaries go (default: profiles/)")
+    ap.add_argument("--bench-json", default=None,
+                    help="format the JSON line of a bench.py run into bench_per_workload.md")
     ap.add_argument("--reuse", action="store_true",
                     help="summarise the raw output already under --raw without profiling")
     args = ap.parse_args()
@@ -310,6 +349,8 @@ def main():
         write_split(raw, names)
     if args.counters:
         write_counters(raw, WORKLOADS[HEADLINE], bench.source_hash())
+    if args.bench_json:
+        write_bench_table(args.bench_json)
 
 
 if __name__ == "__main__":
