@@ -24,6 +24,9 @@ What each function follows:
     Epilogue" (section "What an epilogue is") counts as epilogue work:
     max(v, 0) and the exact GELU v * Phi(v) = v/2 * (1 + erf(v / sqrt 2))
     (Phi the standard normal CDF), or none, after the same batch norm.
+  * ``round_fp8_e4m3`` -- a cast to a narrower dtype, the other epilogue
+    work of that section: OCP FP8 E4M3 (3 mantissa bits, exponent bias 7,
+    subnormal spacing 2^-9, largest finite 448), round to nearest even.
   * ``conv_bn_silu_train`` -- batch norm with batch statistics (training
     mode), the reduction case that "Kernel Fusion" (cheatsheet page, the
     passages on reductions and on synchronization boundaries) sets apart:
@@ -248,3 +251,19 @@ def conv_bn_act_at(x, w, gamma, beta, mean, var, eps: float, stride: int, pad: i
                      for i in range(idx.size)])
     g, b, m, v = (_f64(a).reshape(C_out)[k] for a in (gamma, beta, mean, var))
     return ACTIVATIONS[act](g * (conv - m) / np.sqrt(v + eps) + b)
+
+
+def round_fp8_e4m3(t) -> np.ndarray:
+    """Round to the nearest OCP FP8 E4M3 value, ties to even, as fp64: the
+    spacing of the representable values at |v| is 2^(e-3) with e =
+    max(floor(log2 |v|), -6) (below 2^-6 the subnormals, spacing 2^-9).
+    Values beyond 448 in magnitude are outside the format and returned as
+    NaN (there is no infinity in E4M3)."""
+    t = _f64(t)
+    a = np.abs(t)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    q = np.exp2(np.maximum(e, -6.0) - 3.0)
+    r = np.round(t / q) * q  # numpy rounds halves to even
+    # a value just below a power of two can round up to it: still exact.
+    return np.where(np.abs(r) > 448.0, np.nan, r)

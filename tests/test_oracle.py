@@ -418,3 +418,19 @@ def test_conv_bn_act_at_matches_full():
             idx = np.random.default_rng(1).integers(0, full.size, 300)
             np.testing.assert_allclose(oracle.conv_bn_act_at(d["x"], d["w"], *args, act, idx),
                                        full.ravel()[idx], rtol=1e-13, atol=1e-14)
+
+
+def test_fp8_e4m3_rounding():
+    """Hand-worked values (0.3 -> 5/16, a tie 3*2^-10 -> 2^-8, subnormals,
+    the largest finite 448, 464 the tie above it) and torch's float8_e4m3fn
+    cast on a dense sweep of values."""
+    import torch
+    got = oracle.round_fp8_e4m3(np.array([1.0, 0.3, -3.3, 2**-9, 3 * 2**-10, 2**-10, 448.0,
+                                           0.0, 17.0, 19.0]))
+    np.testing.assert_array_equal(got, [1.0, 0.3125, -3.25, 2**-9, 2**-8, 0.0, 448.0, 0.0, 16.0,
+                                        20.0])
+    assert np.isnan(oracle.round_fp8_e4m3(np.array([470.0]))[0])
+    v = np.concatenate([np.linspace(-440, 440, 20001), np.linspace(-0.05, 0.05, 4001),
+                        np.random.default_rng(5).normal(size=5000) * 4])
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).double().numpy()
+    np.testing.assert_array_equal(oracle.round_fp8_e4m3(v.astype(np.float32)), ref)
