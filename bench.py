@@ -241,6 +241,20 @@ def bench_workload(torch, wl, steps, warmup, with_unfused=True, plan_kind="auto"
                                wl.pad, wl.dtype, "auto", act=act)
             acts[act] = round(time_plan(torch, ap_, sets, steps, warmup) * 1e3, 2)
         row["act_us"] = acts
+        # The same fused kernel storing y as fp8 (E4M3): half the bytes of y.
+        if wl.dtype == "f16":
+            fp = B.ConvBnSilu(wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride,
+                              wl.pad, wl.dtype, "auto", out_dtype="f8")
+            y8 = [torch.empty(wl.y_shape, dtype=torch.float8_e4m3fn, device=sets.w.device)
+                  for _ in range(sets.n)]
+            y16, sets.y = sets.y, y8
+            try:
+                fms = time_plan(torch, fp, sets, steps, warmup)
+            finally:
+                sets.y = y16
+            del y8
+            row.update({"fp8_out_us": round(fms * 1e3, 2),
+                        "fp8_out_gbs": round(traffic.fused_bytes_fp8_out(wl) / fms / 1e6, 1)})
         # A caller whose activations stay NCHW (PyTorch's default layout):
         # the two per-call conversion legs around the same fused kernel.
         lms = time_nchw_legs(torch, plan, wl, sets, steps, warmup)

@@ -25,6 +25,7 @@ _lib = None
 class Dtype(enum.IntEnum):
     F16 = 0
     F32 = 1
+    F8_E4M3 = 2  # output only
 
 
 class Kernel(enum.IntEnum):
@@ -86,6 +87,8 @@ def library():
         lib.tg_conv_bn_silu_create_with_table.restype = i
         lib.tg_conv_bn_act_create.argtypes = [pp] + [i] * 9 + [i, i, i]
         lib.tg_conv_bn_act_create.restype = i
+        lib.tg_conv_bn_act_create_out.argtypes = [pp] + [i] * 9 + [i, i, i, i]
+        lib.tg_conv_bn_act_create_out.restype = i
         lib.tg_conv_bn_silu_run.argtypes = [vp] * 6 + [vp, sz, vp]
         lib.tg_conv_bn_silu_run.restype = i
         lib.tg_conv_bn_silu_destroy.argtypes = [vp]
@@ -155,14 +158,16 @@ _TORCH_DTYPE = {}
 
 def _torch_dtype(dt: Dtype):
     import torch
-    return torch.float16 if dt == Dtype.F16 else torch.float32
+    return {Dtype.F16: torch.float16, Dtype.F32: torch.float32,
+            Dtype.F8_E4M3: torch.float8_e4m3fn}[Dtype(dt)]
 
 
 def _as_dtype(d) -> Dtype:
     if isinstance(d, Dtype):
         return d
     return {"f16": Dtype.F16, "fp16": Dtype.F16, "float16": Dtype.F16,
-            "f32": Dtype.F32, "fp32": Dtype.F32, "float32": Dtype.F32}[str(d)]
+            "f32": Dtype.F32, "fp32": Dtype.F32, "float32": Dtype.F32,
+            "f8": Dtype.F8_E4M3, "fp8": Dtype.F8_E4M3, "f8_e4m3": Dtype.F8_E4M3}[str(d)]
 
 
 def _as_kernel(k) -> int:
@@ -186,14 +191,21 @@ class ConvBnSilu:
     """
 
     def __init__(self, N, H, W, C_in, C_out, kh, kw=None, stride=1, pad=0, dtype="f16",
-                 kernel="auto", table=Table.MI355X, act="silu"):
+                 kernel="auto", table=Table.MI355X, act="silu", out_dtype=None):
         kw = kh if kw is None else kw
         self.shape = (N, H, W, C_in, C_out, kh, kw, stride, pad)
         self.dtype = _as_dtype(dtype)
+        self.out_dtype = self.dtype if out_dtype is None else _as_dtype(out_dtype)
         self.act = Activation[str(act).upper()] if not isinstance(act, Activation) else act
         self._lib = library()
         h = ctypes.c_void_p()
-        if self.act == Activation.SILU:
+        if self.out_dtype != self.dtype:
+            if table != Table.MI355X:
+                raise ValueError("an fp8 output uses the MI355X dispatch table")
+            st = self._lib.tg_conv_bn_act_create_out(
+                ctypes.byref(h), N, H, W, C_in, C_out, kh, kw, stride, pad, int(self.dtype),
+                _as_kernel(kernel), int(self.act), int(self.out_dtype))
+        elif self.act == Activation.SILU:
             st = self._lib.tg_conv_bn_silu_create_with_table(
                 ctypes.byref(h), N, H, W, C_in, C_out, kh, kw, stride, pad, int(self.dtype),
                 _as_kernel(kernel), int(table))
@@ -250,9 +262,10 @@ class ConvBnSilu:
         self._check_tensor(w, (C_out, kh, kw, C_in), td, "w")
         self._check_tensor(scale, (C_out,), torch.float32, "scale")
         self._check_tensor(bias, (C_out,), torch.float32, "bias")
+        yd = _torch_dtype(self.out_dtype)
         if out is None:
-            out = torch.empty(self.y_shape, dtype=td, device=x.device)
-        self._check_tensor(out, self.y_shape, td, "out")
+            out = torch.empty(self.y_shape, dtype=yd, device=x.device)
+        self._check_tensor(out, self.y_shape, yd, "out")
         ws_ptr, ws_bytes = 0, 0
         if self.workspace_bytes:
             if workspace is None:

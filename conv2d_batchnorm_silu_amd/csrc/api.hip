@@ -92,6 +92,7 @@ tg_status make_geom(int N, int H, int W, int C_in, int C_out, int kh, int kw, in
     g->P = (int)P; g->Q = (int)Q;
     g->M = (int)(N * P * Q);
     g->K = kh * kw * C_in;
+    g->out8 = 0;
     return TG_OK;
 }
 
@@ -206,7 +207,8 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in, int C_out, int kh,
                       int kw, int stride, int pad, tg_dtype dtype, tg_kernel kernel,
-                      tg_dispatch table, tg_activation act = TG_ACT_SILU) {
+                      tg_dispatch table, tg_activation act = TG_ACT_SILU,
+                      bool out_fp8 = false) {
     if (!out) return TG_ERR_INVALID_ARGUMENT;
     *out = nullptr;
     ConvGeom g;
@@ -226,8 +228,10 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
         case TG_ACT_NONE: epi = EPI_BN; break;
         default: return TG_ERR_UNSUPPORTED;
     }
-    // The baselines' streaming kernels apply BatchNorm and SiLU only.
-    if ((unfused || split) && epi != EPI_FUSED) return TG_ERR_UNSUPPORTED;
+    // The baselines' streaming kernels apply BatchNorm and SiLU only, and
+    // write y in the input dtype.
+    if ((unfused || split) && (epi != EPI_FUSED || out_fp8)) return TG_ERR_UNSUPPORTED;
+    if (out_fp8 && dtype != TG_F16) return TG_ERR_UNSUPPORTED;
     int base = kv & ~(TG_UNFUSED | TG_SPLIT);
     if (base < TG_KERNEL_AUTO || base > TG_KERNEL_IGEMM) return TG_ERR_UNSUPPORTED;
 
@@ -238,6 +242,7 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
     p.unfused = unfused;
     p.split = split;
     p.epi = epi;
+    p.g.out8 = out_fp8 ? 1 : 0;
     p.forced = base != TG_KERNEL_AUTO;
     p.dma_cfg = -1;
     p.patch_cfg = -1;
@@ -401,6 +406,18 @@ tg_status tg_conv_bn_act_create(tg_conv_bn_silu_plan** out, int N, int H, int W,
                        TG_DISPATCH_MI355X, act);
 }
 
+tg_status tg_conv_bn_act_create_out(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
+                                    int C_out, int kh, int kw, int stride, int pad,
+                                    tg_dtype dtype, tg_kernel kernel, tg_activation act,
+                                    tg_dtype y_dtype) {
+    if (y_dtype != dtype && y_dtype != TG_F8_E4M3) {
+        if (out) *out = nullptr;
+        return TG_ERR_UNSUPPORTED;
+    }
+    return create_impl(out, N, H, W, C_in, C_out, kh, kw, stride, pad, dtype, kernel,
+                       TG_DISPATCH_MI355X, act, y_dtype == TG_F8_E4M3);
+}
+
 tg_status tg_conv_bn_silu_destroy(tg_conv_bn_silu_plan* plan) {
     delete plan;
     return TG_OK;
@@ -466,7 +483,7 @@ tg_status tg_conv_bn_silu_train_run(const tg_conv_bn_silu_plan* plan, const void
     if (!(eps >= 0.0f) || !(momentum >= 0.0f && momentum <= 1.0f)) return TG_ERR_INVALID_ARGUMENT;
     const ConvGeom& g = plan->g;
     if (g.M < 2) return TG_ERR_INVALID_ARGUMENT;  // batch statistics need two values per channel
-    if (plan->epi != EPI_FUSED) return TG_ERR_UNSUPPORTED;  // SiLU only
+    if (plan->epi != EPI_FUSED || plan->g.out8) return TG_ERR_UNSUPPORTED;  // SiLU, y in dtype
     const TrainWs L = train_ws(plan);
     if (!workspace || workspace_bytes < L.total) return TG_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
@@ -591,8 +608,9 @@ tg_status tg_conv_bn_silu_describe(const tg_conv_bn_silu_plan* plan, char* buf, 
     const char* act = plan->epi == EPI_RELU ? " act=relu"
                       : plan->epi == EPI_GELU ? " act=gelu"
                       : plan->epi == EPI_BN   ? " act=none" : "";
-    snprintf(buf, len, "%s%s%s %s N=%d H=%d W=%d C_in=%d C_out=%d k=%dx%d s=%d p=%d -> %dx%d",
-             plan->unfused ? "unfused:" : (plan->split ? "split:" : ""), k, act, plan->dtype == TG_F16 ? "f16" : "f32", g.N, g.H,
+    snprintf(buf, len, "%s%s%s%s %s N=%d H=%d W=%d C_in=%d C_out=%d k=%dx%d s=%d p=%d -> %dx%d",
+             plan->unfused ? "unfused:" : (plan->split ? "split:" : ""), k, act,
+             plan->g.out8 ? " y=fp8" : "", plan->dtype == TG_F16 ? "f16" : "f32", g.N, g.H,
              g.W, g.C_in, g.C_out, g.kh, g.kw, g.stride, g.pad, g.P, g.Q);
     return TG_OK;
 }

@@ -102,7 +102,7 @@ __host__ __device__ inline CuLayout cu_layout(int C_out, int nwaves, int pd) {
 template <int EPI, bool NT, int PD>
 __global__ __launch_bounds__(1024) void conv2d_bn_silu_igemm_cu(
     const f16* __restrict__ x, const f16* __restrict__ w, const float* __restrict__ scale,
-    const float* __restrict__ bias, f16* __restrict__ y, int M, int C_out, int nwaves) {
+    const float* __restrict__ bias, f16* __restrict__ y, int M, int C_out, int nwaves, int out8) {
     constexpr int NF = 4, KS = 2;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ int next_blk[4];
@@ -231,13 +231,7 @@ __global__ __launch_bounds__(1024) void conv2d_bn_silu_igemm_cu(
             const int row = orow + 8 * i;
             const int m = blk * 16 + row;
             const half8_t v = *(const half8_t*)(tl + row * kCuTrow + ocs);
-            if (m < M) {
-                f16* dst = y + (size_t)m * C_out + c0 + ocs;
-                if (NT)
-                    __builtin_nontemporal_store(v, (half8_t*)dst);
-                else
-                    *(half8_t*)dst = v;
-            }
+            if (m < M) store_y8(y, (long long)m * C_out + c0 + ocs, v, out8, NT);
         }
         cu_wave_sync();
     }
@@ -257,7 +251,8 @@ hipError_t launch_cu_t(const ConvGeom& g, int grid, int nwaves, const void* x, c
         attr_bytes = lds;
     }
     hipLaunchKernelGGL((conv2d_bn_silu_igemm_cu<EPI, NT, PD>), dim3(grid), dim3(64 * nwaves), lds,
-                       s, (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g.M, g.C_out, nwaves);
+                       s, (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g.M, g.C_out, nwaves,
+                       g.out8);
     return hipGetLastError();
 }
 

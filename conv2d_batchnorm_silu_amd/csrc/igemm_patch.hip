@@ -433,20 +433,22 @@ __global__ __launch_bounds__(64 * (WM * WN * WK + 1), 1) void conv2d_bn_silu_ige
     {
         const f16* out = (const f16*)(pt_smem + S::RED_BYTES);
         const int rows = r1 - r0;
-        f16* yt = y + ((size_t)n * PQ + r0) * g.C_out;
         constexpr int CV = BN / 8;
         if ((g.C_out & 7) == 0) {
             for (int v = threadIdx.x; v < BM * CV; v += 64 * S::NW) {
                 const int row = v / CV, cv = v - (v / CV) * CV;
                 const int o = n0 + cv * 8;
                 if (row < rows && o < g.C_out)
-                    *(half8_t*)(yt + row * g.C_out + o) = *(const half8_t*)(out + row * S::OROW + cv * 8);
+                    store_y8(y, ((long long)n * PQ + r0 + row) * g.C_out + o,
+                             *(const half8_t*)(out + row * S::OROW + cv * 8), g.out8, false);
             }
         } else {
             for (int v = threadIdx.x; v < BM * BN; v += 64 * S::NW) {
                 const int row = v / BN, c = v - (v / BN) * BN;
                 const int o = n0 + c;
-                if (row < rows && o < g.C_out) yt[row * g.C_out + o] = out[row * S::OROW + c];
+                if (row < rows && o < g.C_out)
+                    store_y1(y, ((long long)n * PQ + r0 + row) * g.C_out + o, out[row * S::OROW + c],
+                             g.out8);
             }
         }
     }

@@ -263,15 +263,11 @@ __global__ __launch_bounds__((NCW + 1) * 64) void conv2d_bn_silu_igemm_rw(
                 const int m = blk * 16 + row;
                 const half8_t v = *(const half8_t*)(tl + row * TROW + ocs);
                 if (m < g.M && ocs < g.C_out) {
-                    f16* dst = y + m * g.C_out + ocs;
                     if (vec_store) {
-                        if (NT)
-                            __builtin_nontemporal_store(v, (half8_t*)dst);
-                        else
-                            *(half8_t*)dst = v;
+                        store_y8(y, m * g.C_out + ocs, v, g.out8, NT);
                     } else {
                         for (int e = 0; e < 8; ++e)
-                            if (ocs + e < g.C_out) dst[e] = v[e];
+                            if (ocs + e < g.C_out) store_y1(y, m * g.C_out + ocs + e, v[e], g.out8);
                     }
                 }
             }
@@ -440,15 +436,11 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_igemm_stream(
             const half8_t v = *(const half8_t*)(tl + row * TROW + ocs);
             const int o = c0 + ocs;
             if (m < g.M && o < g.C_out) {
-                f16* dst = y + m * g.C_out + o;
                 if (vec_store) {
-                    if (NT)
-                        __builtin_nontemporal_store(v, (half8_t*)dst);
-                    else
-                        *(half8_t*)dst = v;
+                    store_y8(y, m * g.C_out + o, v, g.out8, NT);
                 } else {
                     for (int e = 0; e < 8; ++e)
-                        if (o + e < g.C_out) dst[e] = v[e];
+                        if (o + e < g.C_out) store_y1(y, m * g.C_out + o + e, v[e], g.out8);
                 }
             }
         }

@@ -7,6 +7,8 @@
 // Lane -> (n, p, q, k) with k fastest, so the C_out lanes that share an
 // output pixel read the same x values (one fetch serves them all) and the y
 // stores of a wavefront are contiguous in NHWC.
+#include <type_traits>
+
 #include "tg_device.hpp"
 #include "tg_internal.hpp"
 
@@ -39,7 +41,11 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_scalar(
     }
     float sc, bi;
     epi_consts<EPI>(scale, bias, k, g.C_out, sc, bi);
-    y[idx] = from_f32<T>(epilogue<EPI>(acc, sc, bi));
+    const T v = from_f32<T>(epilogue<EPI>(acc, sc, bi));
+    if constexpr (std::is_same<T, f16>::value)
+        store_y1(y, idx, v, g.out8);
+    else
+        y[idx] = v;
 }
 
 hipError_t launch_scalar(const ConvGeom& g, bool f32, int epi, const void* x, const void* w,

@@ -260,12 +260,11 @@ __global__ __launch_bounds__(320) void conv2d_bn_silu_stem(
                 // The group's 32 x C_out halves are contiguous in y.
                 const int valid = npx - grp * 32 < 32 ? npx - grp * 32 : 32;
                 const int pieces = valid * g.C_out / 8;
-                f16* yg = y + (m_base + grp * 32) * g.C_out;
+                const long long yg = (m_base + grp * 32) * g.C_out;  // first element of y
 #pragma unroll
                 for (int i = 0; i < (4 * kMaxC + 63) / 64; ++i) {
                     const int v = lane + 64 * i;
-                    if (v < pieces)
-                        __builtin_nontemporal_store(*(const half8_t*)(tl + v * 8), (half8_t*)(yg + v * 8));
+                    if (v < pieces) store_y8(y, yg + v * 8, *(const half8_t*)(tl + v * 8), g.out8, true);
                 }
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_wave_barrier();

@@ -103,6 +103,44 @@ __device__ __forceinline__ float epilogue(float acc, float s2, float b2) {
     return v;  // EPI_BN
 }
 
+// fp8 output ("Fusing an Epilogue", section "What an epilogue is": casts to
+// a narrower dtype belong in the epilogue): OCP E4M3, round to nearest even,
+// with gfx950's v_cvt_pk_fp8_f32. Element e of y is then byte e. The kernels
+// keep their fp16 output tiles and convert at the store; `out8` comes from
+// the kernel arguments, so the branch is uniform and each store site issues
+// exactly one store instruction either way.
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ u32x2_t fp8x8(half8_t v) {
+    int lo = __builtin_amdgcn_cvt_pk_fp8_f32((float)v[0], (float)v[1], 0, false);
+    lo = __builtin_amdgcn_cvt_pk_fp8_f32((float)v[2], (float)v[3], lo, true);
+    int hi = __builtin_amdgcn_cvt_pk_fp8_f32((float)v[4], (float)v[5], 0, false);
+    hi = __builtin_amdgcn_cvt_pk_fp8_f32((float)v[6], (float)v[7], hi, true);
+    return (u32x2_t){(unsigned)lo, (unsigned)hi};
+}
+
+// Eight outputs from element e (a multiple of 8) of y.
+__device__ __forceinline__ void store_y8(_Float16* y, long long e, half8_t v, int out8, bool nt) {
+    if (out8) {
+        u32x2_t* p = (u32x2_t*)((unsigned char*)y + e);
+        if (nt) __builtin_nontemporal_store(fp8x8(v), p);
+        else *p = fp8x8(v);
+    } else {
+        half8_t* p = (half8_t*)(y + e);
+        if (nt) __builtin_nontemporal_store(v, p);
+        else *p = v;
+    }
+}
+
+// One output, element e of y.
+__device__ __forceinline__ void store_y1(_Float16* y, long long e, _Float16 v, int out8) {
+    if (out8)
+        ((unsigned char*)y)[e] =
+            (unsigned char)(__builtin_amdgcn_cvt_pk_fp8_f32((float)v, 0.0f, 0, false) & 0xff);
+    else
+        y[e] = v;
+}
+
 template <typename T> __device__ __forceinline__ float to_f32(T v) { return (float)v; }
 template <typename T> __device__ __forceinline__ T from_f32(float v) { return (T)v; }  // RNE
 

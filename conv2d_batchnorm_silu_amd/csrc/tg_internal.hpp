@@ -14,6 +14,7 @@ struct ConvGeom {
     int P, Q;  // output extent
     int M;     // N * P * Q output pixels
     int K;     // kh * kw * C_in reduction length
+    int out8;  // 1: y is fp8 (E4M3), one byte per element; 0: y in the input dtype
 };
 
 // Implicit-GEMM tile variants compiled into the library (see igemm.hip).

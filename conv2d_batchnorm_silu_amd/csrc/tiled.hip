@@ -106,7 +106,7 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_tiled(
             }
         }
         const int o0 = gi * CG;
-        f16* yp = y + ((n * g.P + p0 + pl) * g.Q + q) * g.C_out + o0;
+        const int yp = ((n * g.P + p0 + pl) * g.Q + q) * g.C_out + o0;  // element of y
         if ((g.C_out & 7) == 0) {
             half8_t h;
 #pragma unroll
@@ -115,14 +115,14 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_tiled(
                 epi_consts<EPI>(scale, bias, o0 + j, g.C_out, sc, bi);
                 h[j] = (f16)epilogue<EPI>(acc[j], sc, bi);
             }
-            *(half8_t*)yp = h;
+            store_y8(y, yp, h, g.out8, false);
         } else {
 #pragma unroll
             for (int j = 0; j < CG; ++j) {
                 if (o0 + j < g.C_out) {
                     float sc, bi;
                     epi_consts<EPI>(scale, bias, o0 + j, g.C_out, sc, bi);
-                    yp[j] = (f16)epilogue<EPI>(acc[j], sc, bi);
+                    store_y1(y, yp + j, (f16)epilogue<EPI>(acc[j], sc, bi), g.out8);
                 }
             }
         }

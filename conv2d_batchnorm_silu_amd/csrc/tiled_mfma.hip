@@ -178,15 +178,15 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_tiled_mfma(
 
     // 3. The band's output is one contiguous NHWC range: stream it out.
     const int total = rows_out * g.Q * g.C_out;
-    f16* ydst = y + (size_t)(n * g.P + p0) * g.Q * g.C_out;
-    const bool vout = ((((uintptr_t)ydst) | ((uintptr_t)yout)) & 15) == 0;
+    const long long y0 = (long long)(n * g.P + p0) * g.Q * g.C_out;  // first element of y
+    const bool vout = ((((uintptr_t)(y + y0)) | ((uintptr_t)yout)) & 15) == 0;
     if (vout) {
         const int nv = total / 8;
         for (int i = tid; i < nv; i += 256)
-            __builtin_nontemporal_store(*(const half8_t*)(yout + 8 * i), (half8_t*)(ydst + 8 * i));
-        for (int i = nv * 8 + tid; i < total; i += 256) ydst[i] = yout[i];
+            store_y8(y, y0 + 8 * i, *(const half8_t*)(yout + 8 * i), g.out8, true);
+        for (int i = nv * 8 + tid; i < total; i += 256) store_y1(y, y0 + i, yout[i], g.out8);
     } else {
-        for (int i = tid; i < total; i += 256) ydst[i] = yout[i];
+        for (int i = tid; i < total; i += 256) store_y1(y, y0 + i, yout[i], g.out8);
     }
 }
 
@@ -315,12 +315,12 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_tiled_mfma_pipe(
         }
         __syncthreads();  // output tile complete
         const int total = rows_out * g.Q * g.C_out;
-        f16* ydst = y + (size_t)(n * g.P + p0) * g.Q * g.C_out;
-        if (((((uintptr_t)ydst) & 15) == 0) && (total & 7) == 0) {
+        const long long y0 = (long long)(n * g.P + p0) * g.Q * g.C_out;  // first element of y
+        if (((((uintptr_t)(y + y0)) & 15) == 0) && (total & 7) == 0) {
             for (int i = tid; i < total / 8; i += 256)
-                __builtin_nontemporal_store(*(const half8_t*)(yout + 8 * i), (half8_t*)(ydst + 8 * i));
+                store_y8(y, y0 + 8 * i, *(const half8_t*)(yout + 8 * i), g.out8, true);
         } else {
-            for (int i = tid; i < total; i += 256) ydst[i] = yout[i];
+            for (int i = tid; i < total; i += 256) store_y1(y, y0 + i, yout[i], g.out8);
         }
         // The next iteration's first barrier orders these LDS reads before the
         // next band's writes to the output tile.

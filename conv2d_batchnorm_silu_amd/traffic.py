@@ -48,6 +48,12 @@ def fused_bytes(wl) -> int:
     return b["x"] + b["w"] + b["bn"] + b["y"]
 
 
+def fused_bytes_fp8_out(wl) -> int:
+    """Fused path with y stored as fp8 (one byte per element)."""
+    b = workload_bytes(wl)
+    return b["x"] + b["w"] + b["bn"] + b["y"] // ELEM_BYTES[wl.dtype]
+
+
 def unfused_bytes(wl) -> int:
     """conv writes t1, bn reads t1 and writes t2, silu reads t2 and writes y;
     t1 and t2 have y's shape and dtype, so two intermediates are added."""

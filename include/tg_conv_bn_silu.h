@@ -53,7 +53,11 @@ typedef enum {
     TG_ERR_HIP = 5               /* a HIP runtime call or kernel launch failed */
 } tg_status;
 
-typedef enum { TG_F16 = 0, TG_F32 = 1 } tg_dtype;
+/* TG_F8_E4M3 is an output dtype only (tg_conv_bn_act_create_out): OCP FP8
+ * E4M3 (1 sign, 4 exponent, 3 mantissa bits, bias 7, largest finite 448),
+ * one byte per element, rounded to nearest even; results beyond +-448 are
+ * outside the format and not specified. */
+typedef enum { TG_F16 = 0, TG_F32 = 1, TG_F8_E4M3 = 2 } tg_dtype;
 
 /* Kernel selection ("Fusing an Epilogue", section "Three kernels for one
  * operation": one scalar, one spatially tiled, one GEMM-shaped kernel, picked
@@ -168,6 +172,18 @@ typedef enum { TG_ACT_SILU = 0, TG_ACT_RELU = 1, TG_ACT_GELU = 2, TG_ACT_NONE = 
 tg_status tg_conv_bn_act_create(tg_conv_bn_silu_plan **out, int N, int H, int W, int C_in,
                                 int C_out, int kh, int kw, int stride, int pad, tg_dtype dtype,
                                 tg_kernel kernel, tg_activation act);
+
+/* Same as tg_conv_bn_act_create, with y stored in y_dtype: the input dtype,
+ * or TG_F8_E4M3 for fp16 inputs -- a cast to a narrower dtype done in the
+ * epilogue ("Fusing an Epilogue", section "What an epilogue is"), which
+ * halves the bytes of y. y is then N*P*Q*C_out bytes, 16-byte aligned for
+ * the vector kernels as before. TG_ERR_UNSUPPORTED for another y_dtype,
+ * fp8 with fp32 inputs, or fp8 with TG_UNFUSED / TG_SPLIT; an fp8 plan is
+ * rejected by tg_conv_bn_silu_train_run. */
+tg_status tg_conv_bn_act_create_out(tg_conv_bn_silu_plan **out, int N, int H, int W, int C_in,
+                                    int C_out, int kh, int kw, int stride, int pad,
+                                    tg_dtype dtype, tg_kernel kernel, tg_activation act,
+                                    tg_dtype y_dtype);
 
 /* Free a plan. NULL is a no-op. */
 tg_status tg_conv_bn_silu_destroy(tg_conv_bn_silu_plan *plan);

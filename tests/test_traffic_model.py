@@ -43,6 +43,7 @@ def test_workload_bytes_hand_counted():
     assert traffic.unfused_bytes(wl) == 64260096 + 4 * 51380224
     assert traffic.split_bytes(wl) == 64260096 + 2 * 51380224
     assert traffic.train_bytes(wl) == 64260096 + 3 * 51380224
+    assert traffic.fused_bytes_fp8_out(wl) == 12845056 + 32768 + 2048 + 51380224 // 2
     assert traffic.conv_flops(wl) == 3288334336
     wl = WORKLOADS["stem3x3s2_k16"]
     assert traffic.fused_bytes(wl) == 19267584 + 864 + 128 + 25690112
