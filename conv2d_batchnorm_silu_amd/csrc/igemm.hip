@@ -196,8 +196,7 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_igemm(
             int row = v / CV, cv = v - (v / CV) * CV;
             int m = m0 + row, o = n0 + cv * 8;
             if (m < g.M && o < g.C_out)
-                store_y8(y, m * g.C_out + o, *(const half8_t*)(out + row * S::LDO + cv * 8), g.out8,
-                         false);
+                store_y8<false>(y, m * g.C_out + o, *(const half8_t*)(out + row * S::LDO + cv * 8), g.out8);
         }
     } else {
         for (int v = tid; v < BM * BN; v += 256) {

@@ -255,8 +255,7 @@ store_phase:
             const int row = v / CV, cv = v - (v / CV) * CV;
             const int m = m0 + row, o = n0 + cv * 8;
             if (m < g.M && o < g.C_out)
-                store_y8(y, m * g.C_out + o, *(const half8_t*)(out + row * S::OROW + cv * 8), g.out8,
-                         false);
+                store_y8<false>(y, m * g.C_out + o, *(const half8_t*)(out + row * S::OROW + cv * 8), g.out8);
         }
     } else {
         for (int v = threadIdx.x; v < BM * BN; v += 64 * S::NW) {

@@ -119,15 +119,19 @@ __device__ __forceinline__ u32x2_t fp8x8(half8_t v) {
     return (u32x2_t){(unsigned)lo, (unsigned)hi};
 }
 
-// Eight outputs from element e (a multiple of 8) of y.
-__device__ __forceinline__ void store_y8(_Float16* y, long long e, half8_t v, int out8, bool nt) {
+// Eight outputs from element e (a multiple of 8) of y; NT: non-temporal
+// store. NT is a template parameter on purpose: with a run-time flag the
+// compiler merges the two stores of an if/else into one and drops the
+// non-temporal hint (measured: 25% slower on the 1x1 layer).
+template <bool NT>
+__device__ __forceinline__ void store_y8(_Float16* y, long long e, half8_t v, int out8) {
     if (out8) {
         u32x2_t* p = (u32x2_t*)((unsigned char*)y + e);
-        if (nt) __builtin_nontemporal_store(fp8x8(v), p);
+        if constexpr (NT) __builtin_nontemporal_store(fp8x8(v), p);
         else *p = fp8x8(v);
     } else {
         half8_t* p = (half8_t*)(y + e);
-        if (nt) __builtin_nontemporal_store(v, p);
+        if constexpr (NT) __builtin_nontemporal_store(v, p);
         else *p = v;
     }
 }
