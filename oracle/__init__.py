@@ -24,6 +24,9 @@ What each function follows:
     Epilogue" (section "What an epilogue is") counts as epilogue work:
     max(v, 0) and the exact GELU v * Phi(v) = v/2 * (1 + erf(v / sqrt 2))
     (Phi the standard normal CDF), or none, after the same batch norm.
+  * ``conv_bn_act_residual`` -- a residual add after the activation, the
+    last of the elementwise steps "Kernel Fusion" (cheatsheet page) lists as
+    fusing freely: act(batchnorm(conv2d(x, w))) + r.
   * ``round_fp8_e4m3`` -- a cast to a narrower dtype, the other epilogue
     work of that section: OCP FP8 E4M3 (3 mantissa bits, exponent bias 7,
     subnormal spacing 2^-9, largest finite 448), round to nearest even.
@@ -267,3 +270,13 @@ def round_fp8_e4m3(t) -> np.ndarray:
     r = np.round(t / q) * q  # numpy rounds halves to even
     # a value just below a power of two can round up to it: still exact.
     return np.where(np.abs(r) > 448.0, np.nan, r)
+
+
+def conv_bn_act_residual(x, w, gamma, beta, mean, var, eps: float, stride: int, pad: int,
+                         act: str, residual, threads: int | None = None) -> np.ndarray:
+    """act(batchnorm(conv2d(x, w))) + residual (residual of the output's shape)."""
+    out = conv_bn_act(x, w, gamma, beta, mean, var, eps, stride, pad, act, threads)
+    r = _f64(residual)
+    if r.shape != out.shape:
+        raise ValueError("residual shape %s differs from the output's %s" % (r.shape, out.shape))
+    return out + r

@@ -434,3 +434,21 @@ def test_fp8_e4m3_rounding():
                         np.random.default_rng(5).normal(size=5000) * 4])
     ref = torch.from_numpy(v.astype(np.float32)).to(torch.float8_e4m3fn).double().numpy()
     np.testing.assert_array_equal(oracle.round_fp8_e4m3(v.astype(np.float32)), ref)
+
+
+def test_residual_add():
+    """The residual enters once, additively: zero residual gives conv_bn_act,
+    the result is linear in the residual, and a wrong shape is rejected."""
+    wl = WORKLOADS["tiny_f32_3x3"]
+    d = make_inputs(wl)
+    args = (d["gamma"], d["beta"], d["mean"], d["var"], float(d["eps"]), wl.stride, wl.pad)
+    base = oracle.conv_bn_act(d["x"], d["w"], *args, "silu")
+    rng = np.random.default_rng(2)
+    r1, r2 = rng.normal(size=base.shape), rng.normal(size=base.shape)
+    z = oracle.conv_bn_act_residual(d["x"], d["w"], *args, "silu", np.zeros_like(base))
+    np.testing.assert_array_equal(z, base)
+    a = oracle.conv_bn_act_residual(d["x"], d["w"], *args, "silu", r1 + r2)
+    b = oracle.conv_bn_act_residual(d["x"], d["w"], *args, "silu", r1)
+    np.testing.assert_allclose(a - b, r2, rtol=0, atol=1e-12)
+    with pytest.raises(ValueError):
+        oracle.conv_bn_act_residual(d["x"], d["w"], *args, "silu", np.zeros(3))
