@@ -241,6 +241,18 @@ def bench_workload(torch, wl, steps, warmup, with_unfused=True, plan_kind="auto"
                                wl.pad, wl.dtype, "auto", act=act)
             acts[act] = round(time_plan(torch, ap_, sets, steps, warmup) * 1e3, 2)
         row["act_us"] = acts
+        # The same fused kernel adding a residual (y's shape) in its epilogue.
+        res = [torch.empty_like(sets.y[i]).normal_() for i in range(sets.n)]
+        lib = plan._lib
+        stream = torch.cuda.current_stream().cuda_stream
+        rargs = [(plan._h, sets.x[i].data_ptr(), sets.w.data_ptr(), sets.scale.data_ptr(),
+                  sets.bias.data_ptr(), res[i].data_ptr(), sets.y[i].data_ptr(), stream)
+                 for i in range(sets.n)]
+        rms = _timed(torch, lambda i: lib.tg_conv_bn_silu_run_residual(*rargs[i]), sets.n, steps,
+                     warmup)
+        row.update({"residual_us": round(rms * 1e3, 2),
+                    "residual_gbs": round((fb + traffic.workload_bytes(wl)["y"]) / rms / 1e6, 1)})
+        del res, rargs
         # The same fused kernel storing y as fp8 (E4M3): half the bytes of y.
         if wl.dtype == "f16":
             fp = B.ConvBnSilu(wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride,

@@ -91,6 +91,8 @@ def library():
         lib.tg_conv_bn_act_create_out.restype = i
         lib.tg_conv_bn_silu_run.argtypes = [vp] * 6 + [vp, sz, vp]
         lib.tg_conv_bn_silu_run.restype = i
+        lib.tg_conv_bn_silu_run_residual.argtypes = [vp] * 7 + [vp]
+        lib.tg_conv_bn_silu_run_residual.restype = i
         lib.tg_conv_bn_silu_destroy.argtypes = [vp]
         lib.tg_conv_bn_silu_destroy.restype = i
         lib.tg_bn_fold.argtypes = [vp] * 4 + [ctypes.c_float, i, vp, vp, vp]
@@ -254,7 +256,8 @@ class ConvBnSilu:
         return self._lib.tg_conv_bn_silu_run(self._h, x, w, scale, bias, y, workspace,
                                              workspace_bytes, _stream_handle(stream))
 
-    def run(self, x, w, scale, bias, out=None, workspace=None, stream=None):
+    def run(self, x, w, scale, bias, out=None, workspace=None, stream=None, residual=None):
+        """y = act(BN(conv(x, w))) (+ residual, a tensor of y's shape and dtype)."""
         import torch
         N, H, W, C_in, C_out, kh, kw, stride, pad = self.shape
         td = _torch_dtype(self.dtype)
@@ -273,6 +276,13 @@ class ConvBnSilu:
                     self._ws = torch.empty(self.workspace_bytes, dtype=torch.uint8, device=x.device)
                 workspace = self._ws
             ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+        if residual is not None:
+            self._check_tensor(residual, self.y_shape, yd, "residual")
+            st = self._lib.tg_conv_bn_silu_run_residual(
+                self._h, x.data_ptr(), w.data_ptr(), scale.data_ptr(), bias.data_ptr(),
+                residual.data_ptr(), out.data_ptr(), _stream_handle(stream))
+            _check(st, "tg_conv_bn_silu_run_residual")
+            return out
         st = self.run_ptr(x.data_ptr(), w.data_ptr(), scale.data_ptr(), bias.data_ptr(),
                           out.data_ptr(), ws_ptr, ws_bytes, stream)
         _check(st, "tg_conv_bn_silu_run")

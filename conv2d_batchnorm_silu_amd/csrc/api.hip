@@ -93,6 +93,7 @@ tg_status make_geom(int N, int H, int W, int C_in, int C_out, int kh, int kw, in
     g->M = (int)(N * P * Q);
     g->K = kh * kw * C_in;
     g->out8 = 0;
+    g->res = nullptr;
     return TG_OK;
 }
 
@@ -315,10 +316,10 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
 
 // Launch the plan's conv kernel (or `kernel`, after an alignment fallback)
 // writing `out`, with epilogue `epi` (tg::Epilogue).
-hipError_t launch_conv(const tg_conv_bn_silu_plan* plan, int kernel, int epi, const void* x,
+hipError_t launch_conv(const tg_conv_bn_silu_plan* plan, const ConvGeom& g, int kernel, int epi,
+                       const void* x,
                        const void* w, const float* bn_scale, const float* bn_bias, void* conv_out,
                        hipStream_t s) {
-    const ConvGeom& g = plan->g;
     const bool f32 = plan->dtype == TG_F32;
     hipError_t e;
     switch (kernel) {
@@ -423,15 +424,16 @@ tg_status tg_conv_bn_silu_destroy(tg_conv_bn_silu_plan* plan) {
     return TG_OK;
 }
 
-tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, const void* w,
-                              const float* bn_scale, const float* bn_bias, void* y,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+static tg_status run_impl(const tg_conv_bn_silu_plan* plan, const void* x, const void* w,
+                          const float* bn_scale, const float* bn_bias, const void* residual,
+                          void* y, void* workspace, size_t workspace_bytes, void* stream) {
     if (!plan || !x || !w || !bn_scale || !bn_bias || !y) return TG_ERR_INVALID_ARGUMENT;
     const ConvGeom& g = plan->g;
     hipStream_t s = (hipStream_t)stream;
     bool f32 = plan->dtype == TG_F32;
     int kernel = plan->kernel;
-    if (kernel != TG_KERNEL_SCALAR && !(aligned16(x) && aligned16(w) && aligned16(y))) {
+    if (kernel != TG_KERNEL_SCALAR &&
+        !(aligned16(x) && aligned16(w) && aligned16(y) && (!residual || aligned16(residual)))) {
         if (plan->forced) return TG_ERR_ALIGNMENT;
         kernel = TG_KERNEL_SCALAR;
     }
@@ -448,7 +450,9 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, c
         }
     }
     const int epi = plan->unfused || plan->split ? EPI_IDENTITY : plan->epi;
-    hipError_t e = launch_conv(plan, kernel, epi, x, w, bn_scale, bn_bias, conv_out, s);
+    ConvGeom gr = g;
+    gr.res = residual;
+    hipError_t e = launch_conv(plan, gr, kernel, epi, x, w, bn_scale, bn_bias, conv_out, s);
     if (e != hipSuccess) {
         if (env_flag("TG_LOG")) fprintf(stderr, "[tgconv] launch failed: %s\n", hipGetErrorString(e));
         return TG_ERR_HIP;
@@ -500,7 +504,7 @@ tg_status tg_conv_bn_silu_train_run(const tg_conv_bn_silu_plan* plan, const void
     float* bias = (float*)(ws + L.bias);
     double* partial = (double*)(ws + L.partial);
     // 1. conv -> t1 (identity epilogue: scale/bias are not read)
-    hipError_t e = launch_conv(plan, kernel, EPI_IDENTITY, x, w, scale, bias, t1, s);
+    hipError_t e = launch_conv(plan, g, kernel, EPI_IDENTITY, x, w, scale, bias, t1, s);
     if (e != hipSuccess) return TG_ERR_HIP;
     // 2-3. batch statistics -> scale, bias, running estimates
     e = launch_bn_train_stats(f32, t1, g.M, g.C_out, gamma, beta, eps, momentum, running_mean,
@@ -537,6 +541,20 @@ tg_status tg_filter_oihw_to_ohwi(const void* src, void* dst, int C_out, int C_in
                                  tg_dtype dtype, void* stream) {
     if (C_out < 1 || C_in < 1 || kh < 1 || kw < 1) return TG_ERR_INVALID_ARGUMENT;
     return transpose_entry(src, dst, C_out, C_in, (long long)kh * kw, dtype, stream);
+}
+
+tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, const void* w,
+                              const float* bn_scale, const float* bn_bias, void* y,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    return run_impl(plan, x, w, bn_scale, bn_bias, nullptr, y, workspace, workspace_bytes, stream);
+}
+
+tg_status tg_conv_bn_silu_run_residual(const tg_conv_bn_silu_plan* plan, const void* x,
+                                       const void* w, const float* bn_scale, const float* bn_bias,
+                                       const void* residual, void* y, void* stream) {
+    if (!residual) return TG_ERR_INVALID_ARGUMENT;
+    if (plan && (plan->unfused || plan->split || plan->g.out8)) return TG_ERR_UNSUPPORTED;
+    return run_impl(plan, x, w, bn_scale, bn_bias, residual, y, nullptr, 0, stream);
 }
 
 tg_status tg_bn_fold(const float* gamma, const float* beta, const float* mean, const float* var,

@@ -196,13 +196,13 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_igemm(
             int row = v / CV, cv = v - (v / CV) * CV;
             int m = m0 + row, o = n0 + cv * 8;
             if (m < g.M && o < g.C_out)
-                store_y8<false>(y, m * g.C_out + o, *(const half8_t*)(out + row * S::LDO + cv * 8), g.out8);
+                store_y8<false>(y, m * g.C_out + o, *(const half8_t*)(out + row * S::LDO + cv * 8), g.out8, g.res);
         }
     } else {
         for (int v = tid; v < BM * BN; v += 256) {
             int row = v / BN, cc = v - (v / BN) * BN;
             int m = m0 + row, o = n0 + cc;
-            if (m < g.M && o < g.C_out) store_y1(y, m * g.C_out + o, out[row * S::LDO + cc], g.out8);
+            if (m < g.M && o < g.C_out) store_y1(y, m * g.C_out + o, out[row * S::LDO + cc], g.out8, g.res);
         }
     }
 }

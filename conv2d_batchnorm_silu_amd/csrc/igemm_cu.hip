@@ -99,10 +99,11 @@ __host__ __device__ inline CuLayout cu_layout(int C_out, int nwaves, int pd) {
     return L;
 }
 
-template <int EPI, bool NT, int PD, bool OUT8>
+template <int EPI, bool NT, int PD, bool OUT8, bool RES>
 __global__ __launch_bounds__(1024) void conv2d_bn_silu_igemm_cu(
     const f16* __restrict__ x, const f16* __restrict__ w, const float* __restrict__ scale,
-    const float* __restrict__ bias, f16* __restrict__ y, int M, int C_out, int nwaves) {
+    const float* __restrict__ bias, f16* __restrict__ y, int M, int C_out, int nwaves,
+    const f16* __restrict__ res) {
     constexpr int NF = 4, KS = 2;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ int next_blk[4];
@@ -231,13 +232,15 @@ __global__ __launch_bounds__(1024) void conv2d_bn_silu_igemm_cu(
             const int row = orow + 8 * i;
             const int m = blk * 16 + row;
             const half8_t v = *(const half8_t*)(tl + row * kCuTrow + ocs);
-            if (m < M) store_y8<NT>(y, (long long)m * C_out + c0 + ocs, v, OUT8 ? 1 : 0);
+            if (m < M)
+                store_y8<NT>(y, (long long)m * C_out + c0 + ocs, v, OUT8 ? 1 : 0,
+                             RES ? (const void*)res : nullptr);
         }
         cu_wave_sync();
     }
 }
 
-template <int EPI, bool NT, int PD, bool OUT8>
+template <int EPI, bool NT, int PD, bool OUT8, bool RES>
 hipError_t launch_cu_t(const ConvGeom& g, int grid, int nwaves, const void* x, const void* w,
                        const float* scale, const float* bias, void* y, hipStream_t s) {
     const CuLayout L = cu_layout(g.C_out, nwaves, PD);
@@ -245,13 +248,14 @@ hipError_t launch_cu_t(const ConvGeom& g, int grid, int nwaves, const void* x, c
     const int lds = L.bytes > kCuMinLdsBytes ? L.bytes : kCuMinLdsBytes;
     static int attr_bytes = 0;  // largest dynamic LDS size enabled so far
     if (lds > attr_bytes) {
-        hipError_t e = hipFuncSetAttribute((const void*)conv2d_bn_silu_igemm_cu<EPI, NT, PD, OUT8>,
+        hipError_t e = hipFuncSetAttribute((const void*)conv2d_bn_silu_igemm_cu<EPI, NT, PD, OUT8, RES>,
                                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
         attr_bytes = lds;
     }
-    hipLaunchKernelGGL((conv2d_bn_silu_igemm_cu<EPI, NT, PD, OUT8>), dim3(grid), dim3(64 * nwaves), lds,
-                       s, (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g.M, g.C_out, nwaves);
+    hipLaunchKernelGGL((conv2d_bn_silu_igemm_cu<EPI, NT, PD, OUT8, RES>), dim3(grid), dim3(64 * nwaves), lds,
+                       s, (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g.M, g.C_out, nwaves,
+                       (const f16*)g.res);
     return hipGetLastError();
 }
 
@@ -278,8 +282,9 @@ hipError_t launch_igemm_cu(const ConvGeom& g, int nwaves, int pd, bool nt, int e
     const int grid = nblocks < 256 ? nblocks : 256;
     if (grid == 0) return hipSuccess;
 #define TG_CU(EPI, NTV, PDV) \
-    return g.out8 ? launch_cu_t<EPI, NTV, PDV, true>(g, grid, nwaves, x, w, scale, bias, y, s) \
-                  : launch_cu_t<EPI, NTV, PDV, false>(g, grid, nwaves, x, w, scale, bias, y, s)
+    return g.out8  ? launch_cu_t<EPI, NTV, PDV, true, false>(g, grid, nwaves, x, w, scale, bias, y, s) \
+           : g.res ? launch_cu_t<EPI, NTV, PDV, false, true>(g, grid, nwaves, x, w, scale, bias, y, s) \
+                   : launch_cu_t<EPI, NTV, PDV, false, false>(g, grid, nwaves, x, w, scale, bias, y, s)
 #define TG_CU_PD(EPI, NTV)              \
     do {                                \
         if (pd <= 1) TG_CU(EPI, NTV, 1); \

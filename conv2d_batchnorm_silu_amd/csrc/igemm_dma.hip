@@ -255,13 +255,13 @@ store_phase:
             const int row = v / CV, cv = v - (v / CV) * CV;
             const int m = m0 + row, o = n0 + cv * 8;
             if (m < g.M && o < g.C_out)
-                store_y8<false>(y, m * g.C_out + o, *(const half8_t*)(out + row * S::OROW + cv * 8), g.out8);
+                store_y8<false>(y, m * g.C_out + o, *(const half8_t*)(out + row * S::OROW + cv * 8), g.out8, g.res);
         }
     } else {
         for (int v = threadIdx.x; v < BM * BN; v += 64 * S::NW) {
             const int row = v / BN, cc = v - (v / BN) * BN;
             const int m = m0 + row, o = n0 + cc;
-            if (m < g.M && o < g.C_out) store_y1(y, m * g.C_out + o, out[row * S::OROW + cc], g.out8);
+            if (m < g.M && o < g.C_out) store_y1(y, m * g.C_out + o, out[row * S::OROW + cc], g.out8, g.res);
         }
     }
     }

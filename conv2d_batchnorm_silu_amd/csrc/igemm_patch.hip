@@ -440,7 +440,7 @@ __global__ __launch_bounds__(64 * (WM * WN * WK + 1), 1) void conv2d_bn_silu_ige
                 const int o = n0 + cv * 8;
                 if (row < rows && o < g.C_out)
                     store_y8<false>(y, ((long long)n * PQ + r0 + row) * g.C_out + o,
-                             *(const half8_t*)(out + row * S::OROW + cv * 8), g.out8);
+                             *(const half8_t*)(out + row * S::OROW + cv * 8), g.out8, g.res);
             }
         } else {
             for (int v = threadIdx.x; v < BM * BN; v += 64 * S::NW) {
@@ -448,7 +448,7 @@ __global__ __launch_bounds__(64 * (WM * WN * WK + 1), 1) void conv2d_bn_silu_ige
                 const int o = n0 + c;
                 if (row < rows && o < g.C_out)
                     store_y1(y, ((long long)n * PQ + r0 + row) * g.C_out + o, out[row * S::OROW + c],
-                             g.out8);
+                             g.out8, g.res);
             }
         }
     }

@@ -264,10 +264,10 @@ __global__ __launch_bounds__((NCW + 1) * 64) void conv2d_bn_silu_igemm_rw(
                 const half8_t v = *(const half8_t*)(tl + row * TROW + ocs);
                 if (m < g.M && ocs < g.C_out) {
                     if (vec_store) {
-                        store_y8<NT>(y, m * g.C_out + ocs, v, g.out8);
+                        store_y8<NT>(y, m * g.C_out + ocs, v, g.out8, g.res);
                     } else {
                         for (int e = 0; e < 8; ++e)
-                            if (ocs + e < g.C_out) store_y1(y, m * g.C_out + ocs + e, v[e], g.out8);
+                            if (ocs + e < g.C_out) store_y1(y, m * g.C_out + ocs + e, v[e], g.out8, g.res);
                     }
                 }
             }
@@ -437,10 +437,10 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_igemm_stream(
             const int o = c0 + ocs;
             if (m < g.M && o < g.C_out) {
                 if (vec_store) {
-                    store_y8<NT>(y, m * g.C_out + o, v, g.out8);
+                    store_y8<NT>(y, m * g.C_out + o, v, g.out8, g.res);
                 } else {
                     for (int e = 0; e < 8; ++e)
-                        if (o + e < g.C_out) store_y1(y, m * g.C_out + o + e, v[e], g.out8);
+                        if (o + e < g.C_out) store_y1(y, m * g.C_out + o + e, v[e], g.out8, g.res);
                 }
             }
         }

@@ -43,9 +43,9 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_scalar(
     epi_consts<EPI>(scale, bias, k, g.C_out, sc, bi);
     const T v = from_f32<T>(epilogue<EPI>(acc, sc, bi));
     if constexpr (std::is_same<T, f16>::value)
-        store_y1(y, idx, v, g.out8);
+        store_y1(y, idx, v, g.out8, g.res);
     else
-        y[idx] = v;
+        y[idx] = g.res ? v + ((const T*)g.res)[idx] : v;
 }
 
 hipError_t launch_scalar(const ConvGeom& g, bool f32, int epi, const void* x, const void* w,

@@ -264,7 +264,7 @@ __global__ __launch_bounds__(320) void conv2d_bn_silu_stem(
 #pragma unroll
                 for (int i = 0; i < (4 * kMaxC + 63) / 64; ++i) {
                     const int v = lane + 64 * i;
-                    if (v < pieces) store_y8<true>(y, yg + v * 8, *(const half8_t*)(tl + v * 8), g.out8);
+                    if (v < pieces) store_y8<true>(y, yg + v * 8, *(const half8_t*)(tl + v * 8), g.out8, g.res);
                 }
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_wave_barrier();

@@ -15,6 +15,9 @@ struct ConvGeom {
     int M;     // N * P * Q output pixels
     int K;     // kh * kw * C_in reduction length
     int out8;  // 1: y is fp8 (E4M3), one byte per element; 0: y in the input dtype
+    // Residual added to the epilogue's output (y's shape and dtype), or null.
+    // Set per call (tg_conv_bn_silu_run_residual), never in a plan.
+    const void* res;
 };
 
 // Implicit-GEMM tile variants compiled into the library (see igemm.hip).

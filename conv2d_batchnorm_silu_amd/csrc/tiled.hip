@@ -115,14 +115,14 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_tiled(
                 epi_consts<EPI>(scale, bias, o0 + j, g.C_out, sc, bi);
                 h[j] = (f16)epilogue<EPI>(acc[j], sc, bi);
             }
-            store_y8<false>(y, yp, h, g.out8);
+            store_y8<false>(y, yp, h, g.out8, g.res);
         } else {
 #pragma unroll
             for (int j = 0; j < CG; ++j) {
                 if (o0 + j < g.C_out) {
                     float sc, bi;
                     epi_consts<EPI>(scale, bias, o0 + j, g.C_out, sc, bi);
-                    store_y1(y, yp + j, (f16)epilogue<EPI>(acc[j], sc, bi), g.out8);
+                    store_y1(y, yp + j, (f16)epilogue<EPI>(acc[j], sc, bi), g.out8, g.res);
                 }
             }
         }

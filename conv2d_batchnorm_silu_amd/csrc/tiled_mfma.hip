@@ -183,10 +183,10 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_tiled_mfma(
     if (vout) {
         const int nv = total / 8;
         for (int i = tid; i < nv; i += 256)
-            store_y8<true>(y, y0 + 8 * i, *(const half8_t*)(yout + 8 * i), g.out8);
-        for (int i = nv * 8 + tid; i < total; i += 256) store_y1(y, y0 + i, yout[i], g.out8);
+            store_y8<true>(y, y0 + 8 * i, *(const half8_t*)(yout + 8 * i), g.out8, g.res);
+        for (int i = nv * 8 + tid; i < total; i += 256) store_y1(y, y0 + i, yout[i], g.out8, g.res);
     } else {
-        for (int i = tid; i < total; i += 256) store_y1(y, y0 + i, yout[i], g.out8);
+        for (int i = tid; i < total; i += 256) store_y1(y, y0 + i, yout[i], g.out8, g.res);
     }
 }
 
@@ -318,9 +318,9 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_tiled_mfma_pipe(
         const long long y0 = (long long)(n * g.P + p0) * g.Q * g.C_out;  // first element of y
         if (((((uintptr_t)(y + y0)) & 15) == 0) && (total & 7) == 0) {
             for (int i = tid; i < total / 8; i += 256)
-                store_y8<true>(y, y0 + 8 * i, *(const half8_t*)(yout + 8 * i), g.out8);
+                store_y8<true>(y, y0 + 8 * i, *(const half8_t*)(yout + 8 * i), g.out8, g.res);
         } else {
-            for (int i = tid; i < total; i += 256) store_y1(y, y0 + i, yout[i], g.out8);
+            for (int i = tid; i < total; i += 256) store_y1(y, y0 + i, yout[i], g.out8, g.res);
         }
         // The next iteration's first barrier orders these LDS reads before the
         // next band's writes to the output tile.

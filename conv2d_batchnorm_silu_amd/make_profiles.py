@@ -299,7 +299,7 @@ def write_bench_table(path_json):
              "BatchNorm (conv, statistics, fold, BatchNorm+SiLU)",
              "workload | kernel | us | TFLOP/s | GB/s (algorithmic) | bound | frac of bound peak "
              "| unfused us | x vs unfused | split us | x vs split | relu / gelu / none us | "
-             "nchw legs us (share) | train us | fp8 y us (GB/s)"]
+             "nchw legs us (share) | train us | fp8 y us (GB/s) | + residual us (GB/s)"]
     for c in r["per_config"]:
         a = c.get("act_us", {})
         lines.append(" | ".join(str(v) for v in [
@@ -308,7 +308,8 @@ def write_bench_table(path_json):
             c.get("split_us"), c.get("speedup_vs_split"),
             "%s / %s / %s" % (a.get("relu"), a.get("gelu"), a.get("none")),
             "%s (%s)" % (c.get("nchw_legs_us"), c.get("nchw_legs_share")), c.get("train_us"),
-            "%s (%s)" % (c.get("fp8_out_us"), c.get("fp8_out_gbs"))]))
+            "%s (%s)" % (c.get("fp8_out_us"), c.get("fp8_out_gbs")),
+            "%s (%s)" % (c.get("residual_us"), c.get("residual_gbs"))]))
     if r.get("cpu_baseline"):
         lines.append("cpu_baseline (fp64 oracle, headline workload): " +
                      json.dumps(r["cpu_baseline"]))

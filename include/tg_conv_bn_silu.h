@@ -185,6 +185,20 @@ tg_status tg_conv_bn_act_create_out(tg_conv_bn_silu_plan **out, int N, int H, in
                                     tg_dtype dtype, tg_kernel kernel, tg_activation act,
                                     tg_dtype y_dtype);
 
+/* Same as tg_conv_bn_silu_run, adding a residual in the epilogue:
+ * y = act(acc*bn_scale + bn_bias) + residual, elementwise -- the residual add
+ * that "Kernel Fusion" (cheatsheet page, the passage on elementwise chains)
+ * counts among the operations that fuse freely. residual: device, y's shape
+ * and dtype (NHWC [N][P][Q][C_out]); it is read once, and y must not alias
+ * it. For fp16 the activated value is rounded to fp16 first and the sum is
+ * formed in fp32 and rounded once more. Errors as for run, plus
+ * TG_ERR_INVALID_ARGUMENT for a NULL residual and TG_ERR_UNSUPPORTED for an
+ * unfused, split or fp8-output plan. */
+tg_status tg_conv_bn_silu_run_residual(const tg_conv_bn_silu_plan *plan, const void *x,
+                                       const void *w, const float *bn_scale,
+                                       const float *bn_bias, const void *residual, void *y,
+                                       void *stream);
+
 /* Free a plan. NULL is a no-op. */
 tg_status tg_conv_bn_silu_destroy(tg_conv_bn_silu_plan *plan);
 
