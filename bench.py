@@ -19,6 +19,13 @@ whose total size exceeds the 256 MB Infinity Cache several times, so a step
 cannot be served from the cache that a previous step filled. The BatchNorm
 fold runs once per weight load, before timing. Times come from HIP events
 recorded on the stream the kernels are launched on.
+
+Clock settling: the GPU lowers its clocks while the host prepares the next
+workload, and a few hundred microseconds of warmup steps do not bring them
+back (measured on MI355X: 10-20% slower for the first ms after an idle gap).
+Every timed measurement is therefore preceded, besides its W warmup steps, by
+repeating the same call for --settle-ms milliseconds (untimed; reported as
+"settle_ms" in the JSON line).
 """
 from __future__ import annotations
 
@@ -89,10 +96,32 @@ class Sets:
         torch.cuda.synchronize()
 
 
+SETTLE_MS = 30.0  # set from --settle-ms
+
+
+def set_settle_ms(ms):
+    global SETTLE_MS
+    SETTLE_MS = max(0.0, float(ms))
+
+
+def _settle(torch, call, n):
+    """Repeat call(i % n) in rounds of 100 until SETTLE_MS of wall time has
+    passed (each round synchronised, so the launch queue stays short)."""
+    t_end = time.perf_counter() + SETTLE_MS / 1e3
+    i = 0
+    while time.perf_counter() < t_end:
+        for _ in range(100):
+            assert call(i % n) == 0
+            i += 1
+        torch.cuda.synchronize()
+
+
 def _timed(torch, call, n, steps, warmup):
-    """Average ms per call(i % n) over `steps` calls after `warmup`, with HIP
-    events on the current stream (the one the calls launch on). Every call
-    returns a tg_status, checked after the timed region."""
+    """Average ms per call(i % n) over `steps` calls after the clock-settling
+    phase and `warmup` calls, with HIP events on the current stream (the one
+    the calls launch on). Every call returns a tg_status, checked after the
+    timed region."""
+    _settle(torch, call, n)
     for i in range(warmup):
         assert call(i % n) == 0
     torch.cuda.synchronize()
@@ -287,6 +316,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
+                    help="untimed repetitions of each timed call before its warmup (ms)")
     ap.add_argument("--workload", default=None, help="headline workload name")
     ap.add_argument("--only", action="store_true",
                     help="time only the headline workload's fused kernel (for profiling)")
@@ -294,6 +325,7 @@ def main():
     ap.add_argument("--plan", default="auto",
                     help="with --only: the plan to time (auto, split, unfused, scalar, ...)")
     args = ap.parse_args()
+    set_settle_ms(args.settle_ms)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -341,6 +373,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_ms": SETTLE_MS,
         "ms_per_step": round(ms, 5),
         "higher_is_better": True,
         "scaling": "weak",

@@ -87,17 +87,22 @@ def fused_row(stats):
     return max(rows, key=lambda r: r["calls"])
 
 
+TRACE_STEPS = 50  # timed steps of every profiled bench.py --only run
+
+
 def write_trace(raw, wl):
     prof = ["--kernel-trace", "--stats", "-T"]
-    prog = [BENCH, "--only", "--workload", wl.name, "--steps", "50", "--warmup", "5"]
+    prog = [BENCH, "--only", "--workload", wl.name, "--steps", str(TRACE_STEPS), "--warmup", "5"]
     out = run_profiled(raw, "trace_" + wl.name, prof, prog, 180)
     stats = profiling.kernel_stats(find_csv(out, "_kernel_stats.csv"))
+    timed = profiling.timed_region(find_csv(out, "_kernel_trace.csv"), TRACE_STEPS)
     fb, fl = traffic.fused_bytes(wl), traffic.conv_flops(wl)
     lines = ["# rocprofv3 kernel-trace summary: fused conv2d+BN+SiLU, workload %s" % wl.name,
              "# shape: N=%d H=%d W=%d C_in=%d C_out=%d k=%dx%d s=%d p=%d (%s)" % (
                  wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride, wl.pad, wl.dtype),
              "# command: " + cmd_text(prof, prog),
              "# algorithmic bytes per launch %d, conv FLOP per launch %d" % (fb, fl),
+             "# all dispatches of the run (clock-settling phase, warmup and timed steps):",
              "# kernel | calls | avg us | min us | max us | % of GPU time | "
              "GB/s (algorithmic, avg) | TFLOP/s (avg)"]
     fr = fused_row(stats)
@@ -107,6 +112,12 @@ def write_trace(raw, wl):
         if r is fr:
             cells += ["%.1f" % (fb / r["avg_ns"]), "%.2f" % (fl / r["avg_ns"] / 1e3)]
         lines.append(" | ".join(cells))
+    t = timed[fr["name"]]
+    lines += ["# timed region (the fused kernel's last %d dispatches = bench.py's timed steps):"
+              % t["n"],
+              "# avg duration %.2f us (%.1f GB/s algorithmic, %.2f TFLOP/s), start-to-start "
+              "%.2f us per step" % (t["avg_ns"] / 1e3, fb / t["avg_ns"], fl / t["avg_ns"] / 1e3,
+                                    t["spacing_ns"] / 1e3)]
     path = os.path.join(PROFILES, "kernel_trace_%s.txt" % wl.name)
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -163,15 +174,17 @@ def write_split(raw, names):
              "Split = the conv kernel with an identity epilogue writing t1 (fp16), then one "
              "BatchNorm+SiLU streaming kernel; unfused = conv, BatchNorm, SiLU as three kernels. "
              "Durations are rocprofv3 kernel-trace averages per launch (kernel time only, no "
-             "launch gaps); the sum over a plan's kernels is its GPU time per step. Registers, "
+             "launch gaps) over the timed steps (each kernel's last %d dispatches; the earlier "
+             "ones are bench.py's clock-settling and warmup calls); the sum over a plan's "
+             "kernels is its GPU time per step. Registers, "
              "spills, static LDS and scratch come from the code-object metadata of the "
              "library's gfx950 build (dynamic LDS is requested per launch by the plan and is "
              "not included); VGPR+AGPR sets the waves a SIMD can hold (512 registers per "
-             "lane: 2 waves at 256, 3 at 168, 4 at 128).",
+             "lane: 2 waves at 256, 3 at 168, 4 at 128)." % TRACE_STEPS,
              "",
              "command per workload W and plan K: " +
-             cmd_text(prof, [BENCH, "--only", "--workload", "W", "--plan", "K", "--steps", "50",
-                             "--warmup", "5"]),
+             cmd_text(prof, [BENCH, "--only", "--workload", "W", "--plan", "K", "--steps",
+                             str(TRACE_STEPS), "--warmup", "5"]),
              ""]
     for name in names:
         wl = WORKLOADS[name]
@@ -182,10 +195,11 @@ def write_split(raw, names):
                   "---|---|---|---|---|---|---|---|---|---"]
         totals = {}
         for kind in ("auto", "split", "unfused"):
-            prog = [BENCH, "--only", "--workload", name, "--plan", kind, "--steps", "50",
-                    "--warmup", "5"]
+            prog = [BENCH, "--only", "--workload", name, "--plan", kind, "--steps",
+                    str(TRACE_STEPS), "--warmup", "5"]
             out = run_profiled(raw, "split_%s_%s" % (name, kind), prof, prog, 180)
             stats = profiling.kernel_stats(find_csv(out, "_kernel_stats.csv"))
+            timed = profiling.timed_region(find_csv(out, "_kernel_trace.csv"), TRACE_STEPS)
             calls = max(r["calls"] for r in stats if "conv2d_bn_silu" in r["name"])
             tot = 0.0
             for r in stats:
@@ -196,10 +210,10 @@ def write_split(raw, names):
                 g = lambda k: v.get(k, "n/a")
                 lines.append("%s | %s | %d | %.2f | %s | %s | %s | %s/%s | %s | %s" % (
                     "fused" if kind == "auto" else kind, r["name"][:90], r["calls"],
-                    r["avg_ns"] / 1e3, g("vgpr_count"), g("agpr_count"), g("sgpr_count"),
+                    timed[r["name"]]["avg_ns"] / 1e3, g("vgpr_count"), g("agpr_count"), g("sgpr_count"),
                     g("vgpr_spill_count"), g("sgpr_spill_count"),
                     g("group_segment_fixed_size"), g("private_segment_fixed_size")))
-                tot += r["avg_ns"] / 1e3
+                tot += timed[r["name"]]["avg_ns"] / 1e3
             totals[kind] = tot
         lines += ["", "GPU time per step: fused %.2f us, split %.2f us (%.2fx), unfused %.2f us "
                   "(%.2fx)" % (totals["auto"], totals["split"], totals["split"] / totals["auto"],
