@@ -155,6 +155,22 @@ def time_plan(torch, plan, sets, steps, warmup):
     return _timed(torch, lambda i: lib.tg_conv_bn_silu_run(*args[i]), n, steps, warmup)
 
 
+def time_packed(torch, plan, sets, steps, warmup):
+    """Average ms per call of tg_conv_bn_silu_run_packed with the filter
+    packed once, before timing (load-time work), rotating sets; None when the
+    plan's kernel takes no packed filter."""
+    if plan.packed_filter_bytes() == 0:
+        return None
+    wp = plan.pack_filter(sets.w)
+    n = sets.n
+    plan.run_packed(sets.x[0], wp, sets.scale, sets.bias, out=sets.y[0])  # checked call
+    lib = plan._lib
+    stream = torch.cuda.current_stream().cuda_stream
+    args = [(plan._h, sets.x[i].data_ptr(), wp.data_ptr(), sets.scale.data_ptr(),
+             sets.bias.data_ptr(), sets.y[i].data_ptr(), stream) for i in range(n)]
+    return _timed(torch, lambda i: lib.tg_conv_bn_silu_run_packed(*args[i]), n, steps, warmup)
+
+
 def time_nchw_legs(torch, plan, wl, sets, steps, warmup):
     """Average ms per step for a caller whose activations stay NCHW: x
     NCHW -> NHWC, the fused kernel, y NHWC -> NCHW (three launches; the
@@ -296,6 +312,12 @@ def bench_workload(torch, wl, steps, warmup, with_unfused=True, plan_kind="auto"
             del y8
             row.update({"fp8_out_us": round(fms * 1e3, 2),
                         "fp8_out_gbs": round(traffic.fused_bytes_fp8_out(wl) / fms / 1e6, 1)})
+        # The same fused kernel reading a filter packed once at load time
+        # into its tile order (patch-staged plans only).
+        pms = time_packed(torch, plan, sets, steps, warmup)
+        if pms is not None:
+            row.update({"packed_us": round(pms * 1e3, 2),
+                        "speedup_packed": round(ms / pms, 3)})
         # A caller whose activations stay NCHW (PyTorch's default layout):
         # the two per-call conversion legs around the same fused kernel.
         lms = time_nchw_legs(torch, plan, wl, sets, steps, warmup)

@@ -51,6 +51,7 @@ class Table(enum.IntEnum):
 
 STATUS = {0: "TG_OK", 1: "TG_ERR_INVALID_ARGUMENT", 2: "TG_ERR_UNSUPPORTED",
           3: "TG_ERR_ALIGNMENT", 4: "TG_ERR_WORKSPACE", 5: "TG_ERR_HIP"}
+ERR_UNSUPPORTED = 2
 
 
 class TgError(RuntimeError):
@@ -93,6 +94,12 @@ def library():
         lib.tg_conv_bn_silu_run.restype = i
         lib.tg_conv_bn_silu_run_residual.argtypes = [vp] * 7 + [vp]
         lib.tg_conv_bn_silu_run_residual.restype = i
+        lib.tg_conv_bn_silu_packed_filter_bytes.argtypes = [vp, ctypes.POINTER(sz)]
+        lib.tg_conv_bn_silu_packed_filter_bytes.restype = i
+        lib.tg_conv_bn_silu_pack_filter.argtypes = [vp, vp, vp, sz, vp]
+        lib.tg_conv_bn_silu_pack_filter.restype = i
+        lib.tg_conv_bn_silu_run_packed.argtypes = [vp] * 6 + [vp]
+        lib.tg_conv_bn_silu_run_packed.restype = i
         lib.tg_conv_bn_silu_destroy.argtypes = [vp]
         lib.tg_conv_bn_silu_destroy.restype = i
         lib.tg_bn_fold.argtypes = [vp] * 4 + [ctypes.c_float, i, vp, vp, vp]
@@ -289,6 +296,51 @@ class ConvBnSilu:
         return out
 
     __call__ = run
+
+    def packed_filter_bytes(self) -> int:
+        """Bytes of this plan's load-time packed filter; 0 if its kernel takes
+        only the OHWI filter."""
+        n = ctypes.c_size_t()
+        st = self._lib.tg_conv_bn_silu_packed_filter_bytes(self._h, ctypes.byref(n))
+        if st == ERR_UNSUPPORTED:
+            return 0
+        _check(st, "tg_conv_bn_silu_packed_filter_bytes")
+        return n.value
+
+    def pack_filter(self, w, out=None, stream=None):
+        """The OHWI filter w re-packed once into this plan's kernel tile order
+        (a uint8 device tensor of packed_filter_bytes())."""
+        import torch
+        N, H, W, C_in, C_out, kh, kw, stride, pad = self.shape
+        self._check_tensor(w, (C_out, kh, kw, C_in), _torch_dtype(self.dtype), "w")
+        n = self.packed_filter_bytes()
+        if n == 0:
+            raise TgError(ERR_UNSUPPORTED, "tg_conv_bn_silu_packed_filter_bytes")
+        if out is None:
+            out = torch.empty(n, dtype=torch.uint8, device=w.device)
+        self._check_tensor(out, (n,), torch.uint8, "out")
+        _check(self._lib.tg_conv_bn_silu_pack_filter(self._h, w.data_ptr(), out.data_ptr(), n,
+                                                     _stream_handle(stream)),
+               "tg_conv_bn_silu_pack_filter")
+        return out
+
+    def run_packed(self, x, w_packed, scale, bias, out=None, stream=None):
+        """run() with a filter from pack_filter(); bit-identical output."""
+        import torch
+        N, H, W, C_in, C_out, kh, kw, stride, pad = self.shape
+        self._check_tensor(x, (N, H, W, C_in), _torch_dtype(self.dtype), "x")
+        self._check_tensor(w_packed, (self.packed_filter_bytes(),), torch.uint8, "w_packed")
+        self._check_tensor(scale, (C_out,), torch.float32, "scale")
+        self._check_tensor(bias, (C_out,), torch.float32, "bias")
+        yd = _torch_dtype(self.out_dtype)
+        if out is None:
+            out = torch.empty(self.y_shape, dtype=yd, device=x.device)
+        self._check_tensor(out, self.y_shape, yd, "out")
+        _check(self._lib.tg_conv_bn_silu_run_packed(self._h, x.data_ptr(), w_packed.data_ptr(),
+                                                    scale.data_ptr(), bias.data_ptr(),
+                                                    out.data_ptr(), _stream_handle(stream)),
+               "tg_conv_bn_silu_run_packed")
+        return out
 
     def train_workspace_bytes(self) -> int:
         ws = ctypes.c_size_t()

@@ -557,6 +557,47 @@ tg_status tg_conv_bn_silu_run_residual(const tg_conv_bn_silu_plan* plan, const v
     return run_impl(plan, x, w, bn_scale, bn_bias, residual, y, nullptr, 0, stream);
 }
 
+static bool takes_packed_filter(const tg_conv_bn_silu_plan* plan) {
+    return plan->kernel == TG_KERNEL_IGEMM && plan->patch_cfg >= 0 && plan->cu_waves <= 0 &&
+           !plan->unfused && !plan->split && plan->dtype == TG_F16 &&
+           igemm_patch_packed_bytes(plan->g, plan->patch_cfg) > 0;
+}
+
+tg_status tg_conv_bn_silu_packed_filter_bytes(const tg_conv_bn_silu_plan* plan, size_t* bytes) {
+    if (!plan || !bytes) return TG_ERR_INVALID_ARGUMENT;
+    *bytes = 0;
+    if (!takes_packed_filter(plan)) return TG_ERR_UNSUPPORTED;
+    *bytes = igemm_patch_packed_bytes(plan->g, plan->patch_cfg);
+    return TG_OK;
+}
+
+tg_status tg_conv_bn_silu_pack_filter(const tg_conv_bn_silu_plan* plan, const void* w,
+                                      void* w_packed, size_t w_packed_bytes, void* stream) {
+    if (!plan || !w || !w_packed || w == w_packed) return TG_ERR_INVALID_ARGUMENT;
+    if (!takes_packed_filter(plan)) return TG_ERR_UNSUPPORTED;
+    if (w_packed_bytes < igemm_patch_packed_bytes(plan->g, plan->patch_cfg))
+        return TG_ERR_WORKSPACE;
+    if (!aligned16(w) || !aligned16(w_packed)) return TG_ERR_ALIGNMENT;
+    hipError_t e = launch_pack_patch_filter(plan->g, plan->patch_cfg, w, w_packed,
+                                            (hipStream_t)stream);
+    return e == hipSuccess ? TG_OK : TG_ERR_HIP;
+}
+
+tg_status tg_conv_bn_silu_run_packed(const tg_conv_bn_silu_plan* plan, const void* x,
+                                     const void* w_packed, const float* bn_scale,
+                                     const float* bn_bias, void* y, void* stream) {
+    if (!plan || !x || !w_packed || !bn_scale || !bn_bias || !y) return TG_ERR_INVALID_ARGUMENT;
+    if (!takes_packed_filter(plan)) return TG_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w_packed) || !aligned16(y)) return TG_ERR_ALIGNMENT;
+    hipError_t e = launch_igemm_patch(plan->g, plan->patch_cfg, plan->epi, x, w_packed,
+                                      bn_scale, bn_bias, y, (hipStream_t)stream, true);
+    if (e != hipSuccess) {
+        if (env_flag("TG_LOG")) fprintf(stderr, "[tgconv] launch failed: %s\n", hipGetErrorString(e));
+        return TG_ERR_HIP;
+    }
+    return TG_OK;
+}
+
 tg_status tg_bn_fold(const float* gamma, const float* beta, const float* mean, const float* var,
                      float eps, int C_out, float* bn_scale, float* bn_bias, void* stream) {
     if (!gamma || !beta || !mean || !var || !bn_scale || !bn_bias || C_out < 1 || !(eps >= 0.0f))

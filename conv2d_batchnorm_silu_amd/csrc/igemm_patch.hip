@@ -34,6 +34,21 @@
 //     chunk (two waves per SIMD: one's fragment reads overlap the other's
 //     MFMAs); their partial tiles are summed through LDS before the epilogue,
 //     so the epilogue sees the complete K sum.
+//
+// Load-time filter pre-pack ("When the fusion you want is impossible, fuse
+// into the producer", section "The general form": work repeated at every call
+// that could be done once at load time belongs at load time; there the
+// channels-last filters left the output bit-identical): pack_patch_filter rewrites
+// the OHWI filter into the order in which this kernel's direct-to-LDS loads
+// land in its filter ring -- per 64-channel chunk kc, per block of 16 output
+// channels ob, per K-group kg, 16 rows of 128/WK bytes whose 16-byte pieces
+// are already XOR-swizzled -- so that every filter load instruction of a
+// wave reads one contiguous kilobyte instead of 16 (or 8) row fragments:
+//   byte ((kc*NB + ob)*WK + kg)*(2048/WK) + rr*(128/WK) + s*16 holds
+//   w[16*ob + rr][64*kc + kg*(64/WK) + 8*(s ^ swz(rr)) .. + 7]
+// (NB = ceil(C_out/16); rows past C_out are zero; swz is pt_wswz<WK>). The
+// kernel's LDS contents, and therefore its arithmetic, are the same for both
+// forms.
 #include "tg_device.hpp"
 #include "tg_internal.hpp"
 
@@ -114,7 +129,7 @@ template <int BM, int BN, int WM, int WN, int WK, int RING, int EPI>
 __global__ __launch_bounds__(64 * (WM * WN * WK + 1), 1) void conv2d_bn_silu_igemm_patch(
     const f16* __restrict__ x, const f16* __restrict__ w, const float* __restrict__ scale,
     const float* __restrict__ bias, f16* __restrict__ y, ConvGeom g, int tiles_per_img,
-    int tiles_n, int PW, int pstride) {
+    int tiles_n, int PW, int pstride, int packed) {
     using S = PatchShape<BM, BN, WM, WN, WK, RING>;
     extern __shared__ __attribute__((aligned(16))) unsigned char pt_smem[];
 
@@ -159,23 +174,36 @@ __global__ __launch_bounds__(64 * (WM * WN * WK + 1), 1) void conv2d_bn_silu_ige
     // Filter chunk loads: this wave needs rows wn*FN*16 .. +FN*16 of the
     // BN-row tile and pieces kg*PPR .. +PPR of each 128-byte chunk row.
     // Instruction i moves 64/PPR rows; lane l takes row i*64/PPR + l/PPR,
-    // piece (l%PPR) ^ pt_wswz(row) -> slot l%PPR.
-    const u32x4_t wrs = pt_rsrc(w, (unsigned)g.C_out * (unsigned)g.K * 2u);
+    // piece (l%PPR) ^ pt_wswz(row) -> slot l%PPR. From a packed filter the
+    // same bytes are lane l's 16 bytes of one contiguous kilobyte.
+    const int NB = (g.C_out + 15) / 16;
+    const unsigned kstride = packed ? (unsigned)NB * 2048u : 128u;  // bytes per chunk
+    const u32x4_t wrs = pt_rsrc(w, packed ? (unsigned)nk * kstride
+                                          : (unsigned)g.C_out * (unsigned)g.K * 2u);
     unsigned woff[S::LI];
 #pragma unroll
     for (int i = 0; i < S::LI; ++i) {
-        const int row = i * (64 / S::PPR) + lane / S::PPR;
-        const int piece = (lane % S::PPR) ^ pt_wswz<WK>(row);
-        const int o = n0 + wn * S::FN * 16 + row;
-        const int kp = (WK == 2 ? kg * S::PPR : 0) + piece;
-        woff[i] = o < g.C_out ? (unsigned)((o * g.K + kp * 8) * 2) : 0x80000000u;
+        const int rb = i * (64 / S::PPR);  // first wave-local row of instruction i
+        if (packed) {
+            const int ob = (n0 + wn * S::FN * 16 + rb) / 16;
+            woff[i] = ob < NB ? (unsigned)((ob * WK + (WK == 2 ? kg : 0)) * (2048 / WK) +
+                                           (rb % 16) * (128 / WK) + 16 * lane)
+                              : 0x80000000u;
+        } else {
+            const int row = rb + lane / S::PPR;
+            const int piece = (lane % S::PPR) ^ pt_wswz<WK>(row);
+            const int o = n0 + wn * S::FN * 16 + row;
+            const int kp = (WK == 2 ? kg * S::PPR : 0) + piece;
+            woff[i] = o < g.C_out ? (unsigned)((o * g.K + kp * 8) * 2) : 0x80000000u;
+        }
     }
     // Chunk kc's filter loads; past the last chunk they read zeros (out of
     // the buffer's range) so that every step issues the same loads.
     auto issue = [&](int kc) {
         // Chunk kc is K range [64 kc, 64 kc + 64) (tap kc / cchunks, channel
-        // chunk kc % cchunks, since C_in = 64 cchunks): 128 bytes per chunk.
-        const unsigned koff = kc < nk ? (unsigned)kc * 128u : 0x80000000u;
+        // chunk kc % cchunks, since C_in = 64 cchunks): 128 bytes of each
+        // OHWI row, or one packed slab of NB * 2048 bytes.
+        const unsigned koff = kc < nk ? (unsigned)kc * kstride : 0x80000000u;
         const unsigned dst = ring_lds + (unsigned)(kc % RING) * S::WSTAGE;
 #pragma unroll
         for (int i = 0; i < S::LI; ++i) pt_dma16(wrs, woff[i] + koff, dst + i * 1024);
@@ -525,7 +553,8 @@ size_t patch_lds_bytes(const ConvGeom& g, const PatchCfg& c) {
 
 template <int BM, int BN, int WM, int WN, int WK, int RING>
 hipError_t patch_launch_one(const ConvGeom& g, int epi, const void* x, const void* w,
-                            const float* scale, const float* bias, void* y, hipStream_t s) {
+                            const float* scale, const float* bias, void* y, bool packed,
+                            hipStream_t s) {
     using S = PatchShape<BM, BN, WM, WN, WK, RING>;
     const PatchCfg c = {BM, BN, WM, WN, WK, RING};
     const size_t lds = patch_lds_bytes(g, c);
@@ -546,8 +575,33 @@ hipError_t patch_launch_one(const ConvGeom& g, int epi, const void* x, const voi
     }
     hipLaunchKernelGGL(k, dim3(g.N * tiles_per_img * tiles_n), dim3(64 * (S::NW + 1)), lds, s,
                        (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, tiles_per_img,
-                       tiles_n, patch_layout(g, c).pw, patch_layout(g, c).pstride);
+                       tiles_n, patch_layout(g, c).pw, patch_layout(g, c).pstride,
+                       packed ? 1 : 0);
     return hipGetLastError();
+}
+
+// One thread per 16-byte piece of the packed filter (layout in the header
+// comment); WK = 1 or 2.
+__global__ __launch_bounds__(256) void pack_patch_filter(const f16* __restrict__ w,
+                                                         f16* __restrict__ wp, int C_out, int K,
+                                                         int NB, int WK, long long npieces) {
+    const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (i >= npieces) return;
+    const int ppr = 8 / WK;
+    long long t = i / ppr;
+    const int sl = (int)(i - t * ppr);
+    const int rr = (int)(t % 16);
+    t /= 16;
+    const int kg = (int)(t % WK);
+    t /= WK;
+    const int ob = (int)(t % NB);
+    const long long kc = t / NB;
+    const int piece = sl ^ (WK == 2 ? pt_wswz<2>(rr) : pt_wswz<1>(rr));
+    const int o = ob * 16 + rr;
+    const long long k = kc * 64 + kg * (64 / WK) + 8 * piece;
+    half8_t v = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (o < C_out) v = *(const half8_t*)(w + (long long)o * K + k);
+    *(half8_t*)(wp + i * 8) = v;
 }
 
 }  // namespace
@@ -606,14 +660,34 @@ void igemm_patch_describe(int cfg, int* BM, int* BN, int* WM, int* WN, int* WK, 
     *BM = c.BM; *BN = c.BN; *WM = c.WM; *WN = c.WN; *WK = c.WK; *ring = c.RING;
 }
 
+size_t igemm_patch_packed_bytes(const ConvGeom& g, int cfg) {
+    if (cfg < 0 || cfg >= kNumPatchCfgs) return 0;
+    const size_t nk = (size_t)g.kh * g.kw * (g.C_in / 64), NB = (size_t)(g.C_out + 15) / 16;
+    const size_t bytes = nk * NB * 2048;
+    return bytes < (1ull << 31) ? bytes : 0;  // 32-bit buffer offsets
+}
+
+hipError_t launch_pack_patch_filter(const ConvGeom& g, int cfg, const void* w, void* wp,
+                                    hipStream_t s) {
+    const size_t bytes = igemm_patch_packed_bytes(g, cfg);
+    if (bytes == 0) return hipErrorInvalidValue;
+    const long long npieces = (long long)(bytes / 16);
+    const int NB = (g.C_out + 15) / 16;
+    hipLaunchKernelGGL(pack_patch_filter, dim3((unsigned)((npieces + 255) / 256)), dim3(256), 0,
+                       s, (const f16*)w, (f16*)wp, g.C_out, g.K, NB, kPatchCfgs[cfg].WK, npieces);
+    return hipGetLastError();
+}
+
 hipError_t launch_igemm_patch(const ConvGeom& g, int cfg, int epi, const void* x,
                               const void* w, const float* scale, const float* bias, void* y,
-                              hipStream_t s) {
+                              hipStream_t s, bool packed) {
     if (!igemm_patch_fits(g, cfg)) return hipErrorInvalidValue;
+    if (packed && igemm_patch_packed_bytes(g, cfg) == 0) return hipErrorInvalidValue;
     int i = 0;
-#define X(bm, bn, wm, wn, wk, ring)                                                   \
-    if (cfg == i)                                                                       \
-        return patch_launch_one<bm, bn, wm, wn, wk, ring>(g, epi, x, w, scale, bias, y, s); \
+#define X(bm, bn, wm, wn, wk, ring)                                                          \
+    if (cfg == i)                                                                              \
+        return patch_launch_one<bm, bn, wm, wn, wk, ring>(g, epi, x, w, scale, bias, y, packed, \
+                                                          s);                                   \
     ++i;
     TG_PATCH_CFGS(X)
 #undef X

@@ -82,7 +82,12 @@ int igemm_patch_choose(const ConvGeom& g);
 void igemm_patch_describe(int cfg, int* BM, int* BN, int* WM, int* WN, int* WK, int* ring);
 hipError_t launch_igemm_patch(const ConvGeom& g, int cfg, int epi, const void* x,
                               const void* w, const float* scale, const float* bias, void* y,
-                              hipStream_t s);
+                              hipStream_t s, bool packed = false);
+// Bytes of tile cfg's packed filter (0: none fits 32-bit offsets), and the
+// load-time pack kernel that writes it from the OHWI filter.
+size_t igemm_patch_packed_bytes(const ConvGeom& g, int cfg);
+hipError_t launch_pack_patch_filter(const ConvGeom& g, int cfg, const void* w, void* wp,
+                                    hipStream_t s);
 // Stem kernel (stem.hip): C_in = 3, 3x3, stride 2, pad 1, even W, C_out % 8 == 0
 // and <= 64; one workgroup per CU walks bands of R output rows.
 bool stem_serves(const ConvGeom& g);

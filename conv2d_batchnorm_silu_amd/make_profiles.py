@@ -303,17 +303,20 @@ def write_bench_table(path_json):
         r = json.loads(f.read().strip().splitlines()[-1])
     lines = ["# bench.py per-workload results on one MI355X (fused kernel chosen by the MI355X "
              "dispatch table)",
-             "# command: python bench.py   (defaults: --steps %d --warmup %d; %s rotating "
-             "input/output sets per workload)" % (r["steps"], r["warmup"],
-                                                  r["config"].get("buffer_sets", "?")),
+             "# command: python bench.py   (defaults: --steps %d --warmup %d, settle %s ms; %s "
+             "rotating input/output sets per workload)" % (
+                 r["steps"], r["warmup"], r.get("settle_ms"),
+                 r["config"].get("buffer_sets", "?")),
              "# times: HIP events over the timed steps on the launch stream, divided by the step "
              "count (includes launch gaps); timed calls go straight to the C ABI",
              "# split = conv kernel + one BatchNorm+SiLU kernel; unfused = conv, BatchNorm, SiLU; "
              "nchw legs = x NCHW->NHWC + fused + y NHWC->NCHW; train = batch-statistics "
-             "BatchNorm (conv, statistics, fold, BatchNorm+SiLU)",
+             "BatchNorm (conv, statistics, fold, BatchNorm+SiLU); packed = the fused kernel "
+             "reading a filter packed once at load time into its tile order",
              "workload | kernel | us | TFLOP/s | GB/s (algorithmic) | bound | frac of bound peak "
              "| unfused us | x vs unfused | split us | x vs split | relu / gelu / none us | "
-             "nchw legs us (share) | train us | fp8 y us (GB/s) | + residual us (GB/s)"]
+             "nchw legs us (share) | train us | fp8 y us (GB/s) | + residual us (GB/s) | "
+             "packed us"]
     for c in r["per_config"]:
         a = c.get("act_us", {})
         lines.append(" | ".join(str(v) for v in [
@@ -323,7 +326,7 @@ def write_bench_table(path_json):
             "%s / %s / %s" % (a.get("relu"), a.get("gelu"), a.get("none")),
             "%s (%s)" % (c.get("nchw_legs_us"), c.get("nchw_legs_share")), c.get("train_us"),
             "%s (%s)" % (c.get("fp8_out_us"), c.get("fp8_out_gbs")),
-            "%s (%s)" % (c.get("residual_us"), c.get("residual_gbs"))]))
+            "%s (%s)" % (c.get("residual_us"), c.get("residual_gbs")), c.get("packed_us")]))
     if r.get("cpu_baseline"):
         lines.append("cpu_baseline (fp64 oracle, headline workload): " +
                      json.dumps(r["cpu_baseline"]))

@@ -199,6 +199,34 @@ tg_status tg_conv_bn_silu_run_residual(const tg_conv_bn_silu_plan *plan, const v
                                        const float *bn_bias, const void *residual, void *y,
                                        void *stream);
 
+/* Load-time filter pre-pack ("When the fusion you want is impossible, fuse
+ * into the producer", section "The general form": work that would repeat at
+ * every call is done once, when the weights are loaded). For a plan whose
+ * kernel is the patch-staged implicit GEMM (fp16, stride 1, C_in % 64 == 0:
+ * the 3x3 and 7x7 layers), the OHWI filter is rewritten once into the order
+ * in which that kernel's filter loads land in its LDS ring, so every load
+ * instruction reads one contiguous kilobyte; the packed form is specific to
+ * the plan (its tile) and the output of tg_conv_bn_silu_run_packed is
+ * bit-identical to tg_conv_bn_silu_run with the OHWI filter.
+ *   tg_conv_bn_silu_packed_filter_bytes: *bytes = size of the packed filter
+ *     (TG_ERR_UNSUPPORTED, *bytes = 0, for a plan whose kernel takes no packed
+ *     filter, including unfused and split plans; TG_ERR_INVALID_ARGUMENT for
+ *     NULL pointers). Host only.
+ *   tg_conv_bn_silu_pack_filter: w (device OHWI [C_out][kh][kw][C_in] fp16)
+ *     -> w_packed (device, w_packed_bytes >= the size above, 16-byte
+ *     aligned, not overlapping w). TG_ERR_WORKSPACE for a short buffer,
+ *     TG_ERR_ALIGNMENT, TG_ERR_HIP on launch failure. Asynchronous.
+ *   tg_conv_bn_silu_run_packed: tg_conv_bn_silu_run with the packed filter
+ *     (the plan's activation and output dtype apply; no workspace). x, y and
+ *     w_packed must be 16-byte aligned (TG_ERR_ALIGNMENT: there is no scalar
+ *     fallback for a packed filter); other errors as for run. */
+tg_status tg_conv_bn_silu_packed_filter_bytes(const tg_conv_bn_silu_plan *plan, size_t *bytes);
+tg_status tg_conv_bn_silu_pack_filter(const tg_conv_bn_silu_plan *plan, const void *w,
+                                      void *w_packed, size_t w_packed_bytes, void *stream);
+tg_status tg_conv_bn_silu_run_packed(const tg_conv_bn_silu_plan *plan, const void *x,
+                                     const void *w_packed, const float *bn_scale,
+                                     const float *bn_bias, void *y, void *stream);
+
 /* Free a plan. NULL is a no-op. */
 tg_status tg_conv_bn_silu_destroy(tg_conv_bn_silu_plan *plan);
 

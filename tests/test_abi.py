@@ -167,6 +167,47 @@ def test_run_argument_errors_before_any_launch(lib):
     lib.tg_conv_bn_silu_destroy(h)
 
 
+def test_packed_filter_host_logic(lib):
+    """Packed-filter sizes (nk chunks x ceil(C_out/16) blocks x 2 KB) for the
+    patch-staged plans, and every error that returns before a launch."""
+    sz = ctypes.c_size_t()
+    q = lib.tg_conv_bn_silu_packed_filter_bytes
+    for shape, kernel, want in [
+            ((32, 28, 28, 128, 128, 3, 3, 1, 1), 0, 18 * 8 * 2048),   # the 3x3 layer
+            ((16, 56, 56, 64, 64, 7, 7, 1, 3), 0, 49 * 4 * 2048),     # the 7x7 layer
+            ((2, 12, 12, 64, 33, 3, 3, 1, 1), 3, 9 * 3 * 2048)]:      # partial block
+        st, h = _create(lib, *shape, kernel=kernel)
+        assert st == OK
+        buf = ctypes.create_string_buffer(256)
+        lib.tg_conv_bn_silu_describe(h, buf, 256)
+        assert b"igemm_patch" in buf.value, buf.value
+        assert q(h, ctypes.byref(sz)) == OK and sz.value == want
+        assert q(h, None) == INVAL
+        a = 1 << 20
+        pack = lib.tg_conv_bn_silu_pack_filter
+        assert pack(None, a, 2 * a, want, None) == INVAL
+        assert pack(h, a, a, want, None) == INVAL
+        assert pack(h, a, 2 * a, want - 16, None) == WS
+        assert pack(h, a + 8, 2 * a, want, None) == ALIGN
+        runp = lib.tg_conv_bn_silu_run_packed
+        assert runp(h, None, a, a, a, a, None) == INVAL
+        assert runp(h, a + 2, a, a, a, a, None) == ALIGN
+        assert runp(h, a, a + 8, a, a, a, None) == ALIGN
+        lib.tg_conv_bn_silu_destroy(h)
+    assert q(None, ctypes.byref(sz)) == INVAL
+    for shape, kernel in [((32, 56, 56, 64, 256, 1, 1, 1, 0), 0),    # 1x1 kernel
+                          ((32, 28, 28, 128, 128, 3, 3, 1, 1), 0x100),  # unfused
+                          ((2, 16, 16, 16, 32, 3, 3, 1, 1), 0)]:     # C_in % 64 != 0
+        st, h = _create(lib, *shape, kernel=kernel)
+        assert st == OK
+        sz.value = 7
+        assert q(h, ctypes.byref(sz)) == UNSUP and sz.value == 0
+        a = 1 << 20
+        assert lib.tg_conv_bn_silu_pack_filter(h, a, 2 * a, 1 << 30, None) == UNSUP
+        assert lib.tg_conv_bn_silu_run_packed(h, a, a, a, a, a, None) == UNSUP
+        lib.tg_conv_bn_silu_destroy(h)
+
+
 def test_train_argument_errors_before_any_launch(lib):
     """Training-mode entry: argument checks return before any launch."""
     st, h = _create(lib, 2, 16, 16, 16, 32, 3, 3, 1, 1)
