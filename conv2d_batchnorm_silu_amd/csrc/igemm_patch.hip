@@ -628,8 +628,14 @@ bool igemm_patch_serves(const ConvGeom& g) {
     return false;
 }
 
-// Busiest CU's tile count times the tile's MFMA work, with one K-group
-// penalised for its serialised fragment reads; ties go to the lower index.
+// Busiest CU's tile count times the tile's MFMA work, weighted by LDS bytes
+// per MFMA, occupancy, patch stride, ring depth and halo rows; ties go to the
+// lower index. The weights were fitted to every tile timed on MI355X over 40
+// stride-1 shapes (k 1..5, C_in 64/128, C_out 8..256, 8 x 112 x 112) and the
+// 3x3 and 7x7 layers of 28 x 28 and 56 x 56 images: the chosen tile is the
+// fastest on 33 of 42 and within 10.2% of it on all, 0.5% slower than the
+// fastest tiles summed over the shapes (the earlier, hand-set weights: 10 of
+// 42, worst 25%, 7.3% slower summed).
 int igemm_patch_choose(const ConvGeom& g) {
     int best = -1;
     double best_cost = 1e300;
@@ -643,13 +649,22 @@ int igemm_patch_choose(const ConvGeom& g) {
         const int fm = c.BM / c.WM / 16, fn = c.BN / c.WN / 16;
         const double lds = (double)(fm + fn) / (fm * fn);
         // Two waves per K-group (one per SIMD) expose LDS latency: slower on
-        // MI355X despite the lighter LDS traffic.
-        const double occ = c.WK == 2 && c.WM * c.WN == 4 ? 1.0 : 1.3;
+        // MI355X despite the lighter LDS traffic. One K-group of four waves
+        // has the same single wave per SIMD, which costs when a CU holds one
+        // tile; with two or more tiles per CU its smaller workgroups let
+        // another tile's waves share the CU, and it is the fastest form.
+        double occ = 1.3;
+        if (c.WK == 2 && c.WM * c.WN == 4) occ = 1.0;
+        else if (c.WK == 1 && c.WM * c.WN == 4) occ = per_cu >= 2 ? 0.85 : 1.15;
         // The dense patch stride costs 2-way bank conflicts on every pixel
-        // fragment read; a three-stage ring hides less filter latency.
-        const double conflicts = patch_layout(g, c).pstride == g.C_in * 2 + 16 ? 1.25 : 1.0;
+        // fragment read (measured: little time); a three-stage ring hides
+        // less filter latency.
+        const double conflicts = patch_layout(g, c).pstride == g.C_in * 2 + 16 ? 1.05 : 1.0;
         const double ring = c.RING == 3 ? 1.05 : 1.0;
-        double cost = (double)per_cu * c.BM * c.BN * occ * conflicts * ring * (0.7 + lds);
+        // Halo: a tile of `rows` output rows copies rows + kh - 1 patch rows.
+        const double rows = (double)c.BM / g.Q;
+        const double halo = 1.0 + 0.1 * ((rows + g.kh - 1) / rows - 1.0);
+        double cost = (double)per_cu * c.BM * c.BN * occ * conflicts * ring * (0.7 + lds) * halo;
         if (cost < best_cost * 0.999) { best = i; best_cost = cost; }
     }
     return best;
