@@ -104,6 +104,11 @@ def set_settle_ms(ms):
     SETTLE_MS = max(0.0, float(ms))
 
 
+def set_cold_reps(n):
+    global COLD_REPS
+    COLD_REPS = max(0, int(n))
+
+
 def _settle(torch, call, n):
     """Repeat call(i % n) in rounds of 100 until SETTLE_MS of wall time has
     passed (each round synchronised, so the launch queue stays short)."""
@@ -135,6 +140,83 @@ def _timed(torch, call, n, steps, warmup):
     torch.cuda.synchronize()
     assert not any(st), "a timed call failed: status %s" % max(st)
     return e0.elapsed_time(e1) / steps
+
+
+COLD_REPS = 100  # set from --cold-reps
+FLUSH_BYTES = 1 << 30
+
+
+def time_cold(torch, call, n, reps, flush):
+    """Cold timing: before every rep, `flush` (a 1 GiB read-modify-write of a
+    scratch buffer, more than four times the 256 MB Infinity Cache) evicts
+    every cached byte; HIP events then bracket the single call. Returns
+    {p10, p50, p90} in us over `reps` reps (after 10 untimed ones)."""
+    for i in range(10):
+        flush()
+        assert call(i % n) == 0
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    st = []
+    for i, (a, b) in enumerate(ev):
+        flush()
+        a.record()
+        st.append(call(i % n))
+        b.record()
+    torch.cuda.synchronize()
+    assert not any(st), "a timed call failed: status %s" % max(st)
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    q = lambda f: round(us[min(len(us) - 1, int(f * len(us)))], 2)
+    return {"p10": q(0.1), "p50": q(0.5), "p90": q(0.9), "reps": reps}
+
+
+def plan_call(torch, plan, sets):
+    """call(i) -> tg_status of one tg_conv_bn_silu_run on set i (device
+    addresses taken once; shapes checked through the binding first)."""
+    plan.run(sets.x[0], sets.w, sets.scale, sets.bias, out=sets.y[0])  # checked call
+    ws = None
+    if plan.workspace_bytes:
+        ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=sets.w.device)
+    lib = plan._lib
+    stream = torch.cuda.current_stream().cuda_stream
+    args = [(plan._h, sets.x[i].data_ptr(), sets.w.data_ptr(), sets.scale.data_ptr(),
+             sets.bias.data_ptr(), sets.y[i].data_ptr(), ws.data_ptr() if ws is not None else 0,
+             plan.workspace_bytes, stream) for i in range(sets.n)]
+    return lambda i: lib.tg_conv_bn_silu_run(*args[i]), ws
+
+
+def launch_overhead_us(torch, C=256, reps=2000):
+    """Per-launch cost of a tiny kernel of this library (tg_bn_fold on C
+    channels) launched back to back: the launch time that fusing two
+    kernels away removes."""
+    from conv2d_batchnorm_silu_amd import binding as B
+    lib = B.library()
+    v = [torch.rand(C, device="cuda") + 0.5 for _ in range(6)]
+    stream = torch.cuda.current_stream().cuda_stream
+    args = tuple(t.data_ptr() for t in v[:4]) + (1e-5, C, v[4].data_ptr(), v[5].data_ptr(),
+                                                 stream)
+    return _timed(torch, lambda i: lib.tg_bn_fold(*args), 1, reps, 100) * 1e3
+
+
+_COPY_GBS = None
+
+
+def copy_gbs(torch, nbytes=256 << 20):
+    """Device-to-device copy rate (read + write bytes per second, GB/s) of a
+    256 MiB buffer: the streaming rate at which the intermediate tensors of
+    the unfused form would move. Measured once per process."""
+    global _COPY_GBS
+    if _COPY_GBS is None:
+        a = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+        b = torch.empty_like(a)
+        def copy(i):
+            b.copy_(a)
+            return 0  # a status of 0, as _timed expects
+
+        ms = _timed(torch, copy, 1, 20, 5)
+        _COPY_GBS = 2 * nbytes / ms / 1e6
+        del a, b
+    return _COPY_GBS
 
 
 def time_plan(torch, plan, sets, steps, warmup):
@@ -273,6 +355,27 @@ def bench_workload(torch, wl, steps, warmup, with_unfused=True, plan_kind="auto"
         ums = time_plan(torch, up, sets, steps, warmup)
         row.update({"unfused_us": round(ums * 1e3, 2), "speedup_vs_unfused": round(ums / ms, 3),
                     "unfused_gbs_effective": round(traffic.unfused_bytes(wl) / ums / 1e6, 1)})
+        # Cold protocol: caches flushed before every single call.
+        if COLD_REPS > 0:
+            scratch = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=sets.w.device)
+            scratch.zero_()
+            flush = lambda: scratch.add_(1.0)
+            fcall, _ = plan_call(torch, plan, sets)
+            ucall, uws = plan_call(torch, up, sets)
+            row["cold_us"] = time_cold(torch, fcall, sets.n, COLD_REPS, flush)
+            row["unfused_cold_us"] = time_cold(torch, ucall, sets.n, COLD_REPS, flush)
+            row["speedup_vs_unfused_cold"] = round(
+                row["unfused_cold_us"]["p50"] / row["cold_us"]["p50"], 3)
+            del scratch, uws
+        # The pages' prediction of the fusion benefit: the two launches it
+        # removes plus the 4|y| bytes of t1 and t2 at the measured streaming
+        # (device copy) bandwidth, added to the fused time, over the fused time.
+        lo = launch_overhead_us(torch)
+        cg = copy_gbs(torch)
+        ybytes = traffic.workload_bytes(wl)["y"]
+        pred = (ms * 1e3 + 2 * lo + 4 * ybytes / (cg * 1e3)) / (ms * 1e3)
+        row.update({"launch_overhead_us": round(lo, 2), "copy_gbs": round(cg, 1),
+                    "predicted_speedup_vs_unfused": round(pred, 3)})
         # Split form: the same conv kernel writing t1, then one bn+silu kernel.
         sp = B.ConvBnSilu(wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride, wl.pad,
                           wl.dtype, "split")
@@ -338,6 +441,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--cold-reps", type=int, default=COLD_REPS,
+                    help="reps of the cold (cache-flushed) protocol per plan (0: skip)")
     ap.add_argument("--settle-ms", type=float, default=SETTLE_MS,
                     help="untimed repetitions of each timed call before its warmup (ms)")
     ap.add_argument("--workload", default=None, help="headline workload name")
@@ -348,6 +453,7 @@ def main():
                     help="with --only: the plan to time (auto, split, unfused, scalar, ...)")
     args = ap.parse_args()
     set_settle_ms(args.settle_ms)
+    set_cold_reps(args.cold_reps)
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -409,6 +515,7 @@ def main():
                    "buffer_sets": head_row["sets"]},
         "tflops": head_row["tflops"],
         "speedup_vs_unfused": head_row.get("speedup_vs_unfused"),
+        "cold_us": head_row.get("cold_us"),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": hbm_bytes, "algorithmic_bytes": fb},

@@ -296,6 +296,10 @@ def COPY_BYTES_MIB():
     return COPY_BYTES // 2**20
 
 
+def _cold(q):
+    return "%s (%s-%s)" % (q["p50"], q["p10"], q["p90"]) if q else None
+
+
 def write_bench_table(path_json):
     """profiles/bench_per_workload.md from the JSON line of a default
     `python bench.py` run."""
@@ -313,10 +317,14 @@ def write_bench_table(path_json):
              "nchw legs = x NCHW->NHWC + fused + y NHWC->NCHW; train = batch-statistics "
              "BatchNorm (conv, statistics, fold, BatchNorm+SiLU); packed = the fused kernel "
              "reading a filter packed once at load time into its tile order",
+             "# cold = a 1 GiB cache flush before every single call, events around that call "
+             "(p50, with p10-p90); predicted x = (fused + 2 launches + 4|y| at the measured "
+             "device-copy bandwidth) / fused",
              "workload | kernel | us | TFLOP/s | GB/s (algorithmic) | bound | frac of bound peak "
              "| unfused us | x vs unfused | split us | x vs split | relu / gelu / none us | "
              "nchw legs us (share) | train us | fp8 y us (GB/s) | + residual us (GB/s) | "
-             "packed us"]
+             "packed us | cold us p50 (p10-p90) | unfused cold us p50 | x vs unfused cold | "
+             "predicted x"]
     for c in r["per_config"]:
         a = c.get("act_us", {})
         lines.append(" | ".join(str(v) for v in [
@@ -326,7 +334,9 @@ def write_bench_table(path_json):
             "%s / %s / %s" % (a.get("relu"), a.get("gelu"), a.get("none")),
             "%s (%s)" % (c.get("nchw_legs_us"), c.get("nchw_legs_share")), c.get("train_us"),
             "%s (%s)" % (c.get("fp8_out_us"), c.get("fp8_out_gbs")),
-            "%s (%s)" % (c.get("residual_us"), c.get("residual_gbs")), c.get("packed_us")]))
+            "%s (%s)" % (c.get("residual_us"), c.get("residual_gbs")), c.get("packed_us"),
+            _cold(c.get("cold_us")), (c.get("unfused_cold_us") or {}).get("p50"),
+            c.get("speedup_vs_unfused_cold"), c.get("predicted_speedup_vs_unfused")]))
     if r.get("cpu_baseline"):
         lines.append("cpu_baseline (fp64 oracle, headline workload): " +
                      json.dumps(r["cpu_baseline"]))
