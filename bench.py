@@ -376,6 +376,8 @@ def bench_workload(torch, wl, steps, warmup, with_unfused=True, plan_kind="auto"
         pred = (ms * 1e3 + 2 * lo + 4 * ybytes / (cg * 1e3)) / (ms * 1e3)
         row.update({"launch_overhead_us": round(lo, 2), "copy_gbs": round(cg, 1),
                     "predicted_speedup_vs_unfused": round(pred, 3)})
+        if bound == "hbm":  # against the measured streaming rate as well as the spec
+            row["frac_of_copy"] = round(gbs / cg, 4)
         # Split form: the same conv kernel writing t1, then one bn+silu kernel.
         sp = B.ConvBnSilu(wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride, wl.pad,
                           wl.dtype, "split")
@@ -516,6 +518,10 @@ def main():
         "tflops": head_row["tflops"],
         "speedup_vs_unfused": head_row.get("speedup_vs_unfused"),
         "cold_us": head_row.get("cold_us"),
+        "frac_of_copy": head_row.get("frac_of_copy"),
+        "device": {"name": torch.cuda.get_device_name(0),
+                   "compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
+                   "hip": torch.version.hip, "torch": torch.__version__},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": hbm_bytes, "algorithmic_bytes": fb},

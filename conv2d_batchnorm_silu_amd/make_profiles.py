@@ -341,6 +341,12 @@ def write_bench_table(path_json):
         lines.append("cpu_baseline (fp64 oracle, headline workload): " +
                      json.dumps(r["cpu_baseline"]))
     lines.append("roofline (headline): " + json.dumps(r["roofline"]))
+    if r.get("frac_of_copy") is not None:
+        lines.append("headline against the measured device-copy rate (%s GB/s): %s" % (
+            r["per_config"][[c["workload"] for c in r["per_config"]].index(
+                r["config"]["workload"])].get("copy_gbs"), r["frac_of_copy"]))
+    if r.get("device"):
+        lines.append("device: " + json.dumps(r["device"]))
     lines.append("value: %s %s (%s)" % (r["value"], r["unit"], r["config"]["workload"]))
     path = os.path.join(PROFILES, "bench_per_workload.md")
     with open(path, "w") as f:
