@@ -262,13 +262,16 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
             p.rw_grid = igemm_rw_grid(g, kCUs * env_int("TG_RW_WG_PER_CU", 1));
             p.rw_nt = env_int("TG_NT", 1) != 0;
             // TG_CU: wavefronts per 64-channel slice of the one-workgroup-per-CU
-            // kernel (0 disables it); 3 (12 wavefronts for 256 channels)
-            // measured best on MI355X for the 1x1 C_in=64 layer. The
-            // register-weights kernel stays the fallback for BatchNorm vectors
-            // that are not 16-byte aligned.
+            // kernel (0 disables it); TG_CU_PD: input blocks in flight per
+            // wavefront (1..3). 3 and 3 (12 wavefronts for 256 channels, three
+            // blocks ahead) measured best on MI355X for the 1x1 C_in=64 layer
+            // with settled clocks (12.9 us mean over four runs against 13.5 us
+            // two blocks ahead, and a tighter spread). The register-weights
+            // kernel stays the fallback for BatchNorm vectors that are not
+            // 16-byte aligned.
             if (igemm_cu_serves(g) && env_int("TG_CU", 3) > 0) {
                 p.cu_waves = igemm_cu_waves(g, env_int("TG_CU", 3));
-                p.cu_pd = env_int("TG_CU_PD", 2);
+                p.cu_pd = env_int("TG_CU_PD", 3);
             }
         } else if (igemm_patch_serves(g) && env_int("TG_IGEMM_PATCH", 1) != 0 &&
                    env_int("TG_IGEMM_CFG", -1) < 0) {

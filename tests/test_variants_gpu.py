@@ -53,7 +53,8 @@ ONE_BY_ONE = [
              ("uniform", -3.0, 3.0)),
 ]
 
-CU_CFGS = [("2", "1"), ("2", "2"), ("2", "3"), ("3", "2"), ("4", "1"), ("4", "2"), ("1", "2")]
+CU_CFGS = [("2", "1"), ("2", "2"), ("2", "3"), ("3", "2"), ("3", "3"), ("4", "1"), ("4", "2"),
+           ("1", "2")]
 
 
 @pytest.mark.parametrize("per_group,pd", CU_CFGS, ids=["r%s_pd%s" % c for c in CU_CFGS])
@@ -66,7 +67,8 @@ def test_cu_kernel(monkeypatch, wl, per_group, pd):
     check_workload(wl, "unfused")
 
 
-@pytest.mark.parametrize("per_group,pd", [("2", "2"), ("3", "2"), ("4", "2")])
+@pytest.mark.parametrize("per_group,pd", [("2", "2"), ("3", "2"), ("3", "3"), ("4", "1"),
+                                          ("4", "2")])
 def test_cu_kernel_headline(monkeypatch, per_group, pd):
     monkeypatch.setenv("TG_CU", per_group)
     monkeypatch.setenv("TG_CU_PD", pd)
