@@ -41,7 +41,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
-MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+MFMA_F16_PEAK_TFLOPS = 2516.6  # MI355X dense fp16 MFMA, published (256 CUs x 2.4 GHz x 4096)
 RIDGE = MFMA_F16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 METRIC = ("fused conv+BN+SiLU TFLOP/s & HBM GB/s (% roofline); speedup vs unfused 3-kernel")
 
@@ -79,7 +79,7 @@ def load_traffic(workload: str):
 class Sets:
     """Several device copies of one workload's input x and output y."""
 
-    def __init__(self, torch, wl, d, min_bytes=1 << 30, max_sets=16):
+    def __init__(self, torch, wl, d, min_bytes=1 << 30, max_sets=128):
         from conv2d_batchnorm_silu_amd import traffic
         b = traffic.workload_bytes(wl)
         per = b["x"] + b["y"]
@@ -334,13 +334,48 @@ def cpu_baseline(wl, d, budget_s=12.0):
                 n, wl.N, wl.name, reps, dt, threads, reps * traffic.conv_flops(sub) / dt / 1e9)}
 
 
-def bench_workload(torch, wl, steps, warmup, with_unfused=True, plan_kind="auto"):
+TOL = {"f16": 1e-2, "f32": 1e-4}  # |gpu - oracle| <= TOL * max(1, |oracle|)
+
+
+def parity(torch, plan, sets, wl, ref):
+    """Run the plan once on buffer set 0 and compare every output element
+    with the fp64 oracle's result `ref`; the plan is timed only if this
+    passes (the criterion the tests apply)."""
+    import numpy as np
+    plan.run(sets.x[0], sets.w, sets.scale, sets.bias, out=sets.y[0])
+    torch.cuda.synchronize()
+    got = sets.y[0].float().cpu().numpy().astype(np.float64)
+    nan = int(np.isnan(got).sum())
+    scaled = np.abs(got - ref) / np.maximum(1.0, np.abs(ref))
+    worst = float(np.nanmax(scaled)) if scaled.size else 0.0
+    viol = int((scaled > TOL[wl.dtype]).sum()) + nan
+    return {"n": int(got.size), "max_scaled_err": worst, "violations": viol, "nan": nan,
+            "tol": TOL[wl.dtype], "ok": viol == 0}
+
+
+def oracle_ref(wl, d):
+    import oracle
+    return oracle.conv_bn_silu(d["x"], d["w"], d["gamma"], d["beta"], d["mean"], d["var"],
+                               float(d["eps"]), wl.stride, wl.pad)
+
+
+class ParityError(RuntimeError):
+    pass
+
+
+def bench_workload(torch, wl, steps, warmup, with_unfused=True, plan_kind="auto",
+                   check=True):
     from conv2d_batchnorm_silu_amd import binding as B, traffic
     from conv2d_batchnorm_silu_amd.inputs import make_inputs
     d = make_inputs(wl)
     sets = Sets(torch, wl, d)
     plan = B.ConvBnSilu(wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride, wl.pad,
                         wl.dtype, plan_kind)
+    ref = oracle_ref(wl, d) if check else None
+    par = parity(torch, plan, sets, wl, ref) if check else None
+    if par is not None and not par["ok"]:
+        raise ParityError("%s (%s): %d of %d outputs beyond the tolerance (worst %.3g)" % (
+            wl.name, plan.describe(), par["violations"], par["n"], par["max_scaled_err"]))
     ms = time_plan(torch, plan, sets, steps, warmup)
     fb, fl = traffic.fused_bytes(wl), traffic.conv_flops(wl)
     bound, ai = binding_roof(wl)
@@ -348,10 +383,16 @@ def bench_workload(torch, wl, steps, warmup, with_unfused=True, plan_kind="auto"
     frac = gbs / HBM_PEAK_GBS if bound == "hbm" else tfl / MFMA_F16_PEAK_TFLOPS
     row = {"workload": wl.name, "kernel": plan.describe(), "ms": round(ms, 5),
            "us": round(ms * 1e3, 2), "tflops": round(tfl, 2), "gbs": round(gbs, 1),
-           "bound": bound, "ai": round(ai, 1), "frac": round(frac, 4), "sets": sets.n}
+           "bound": bound, "ai": round(ai, 1), "frac": round(frac, 4), "sets": sets.n,
+           "parity": par}
     if with_unfused:
         up = B.ConvBnSilu(wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride, wl.pad,
                           wl.dtype, "unfused")
+        upar = parity(torch, up, sets, wl, ref) if check else None
+        if upar is not None and not upar["ok"]:
+            raise ParityError("%s unfused: %d outputs beyond the tolerance (worst %.3g)" % (
+                wl.name, upar["violations"], upar["max_scaled_err"]))
+        row["unfused_parity"] = upar
         ums = time_plan(torch, up, sets, steps, warmup)
         row.update({"unfused_us": round(ums * 1e3, 2), "speedup_vs_unfused": round(ums / ms, 3),
                     "unfused_gbs_effective": round(traffic.unfused_bytes(wl) / ums / 1e6, 1)})
@@ -433,7 +474,7 @@ def bench_workload(torch, wl, steps, warmup, with_unfused=True, plan_kind="auto"
         tms = time_train(torch, plan, sets, steps, warmup)
         row.update({"train_us": round(tms * 1e3, 2),
                     "train_gbs_effective": round(traffic.train_bytes(wl) / tms / 1e6, 1)})
-    del sets
+    del sets, ref
     torch.cuda.empty_cache()
     return row, d
 
@@ -481,10 +522,15 @@ def main():
     rows = []
     head_row, head_d = None, None
     for name, wl in WORKLOADS.items():
-        if wl.dtype != "f16" and name != head.name:
-            # fp32 3x3 on a 16x16 image: launch-latency bound, timed but not graded
-            pass
-        row, d = bench_workload(torch, wl, args.steps, args.warmup)
+        # The fp32 16x16 workload is launch-latency bound: timed, not graded.
+        try:
+            row, d = bench_workload(torch, wl, args.steps, args.warmup)
+        except ParityError as e:
+            log("[bench] PARITY FAILED: %s" % e)
+            print(json.dumps({"metric": METRIC, "value": None, "unit": None, "n_gpus": 1,
+                              "parity": {"ok": False, "error": str(e)},
+                              "per_config": rows}), flush=True)
+            sys.exit(1)
         log("[bench] %s" % json.dumps(row))
         rows.append(row)
         if name == head.name:
@@ -493,13 +539,17 @@ def main():
             del d
 
     ms = head_row["ms"]
-    fb = traffic.fused_bytes(head)
-    achieved = fb / ms / 1e6
+    fb, fl = traffic.fused_bytes(head), traffic.conv_flops(head)
+    bound, _ = binding_roof(head)
+    if bound == "hbm":
+        achieved, peak, unit = fb / ms / 1e6, HBM_PEAK_GBS, "GB/s"
+    else:
+        achieved, peak, unit = fl / ms / 1e9, MFMA_F16_PEAK_TFLOPS, "TFLOP/s"
     hbm_bytes = load_traffic(head.name)
     out = {
         "metric": METRIC,
         "value": round(achieved, 1),
-        "unit": "GB/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -522,9 +572,12 @@ def main():
         "device": {"name": torch.cuda.get_device_name(0),
                    "compute_units": torch.cuda.get_device_properties(0).multi_processor_count,
                    "hip": torch.version.hip, "torch": torch.__version__},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": hbm_bytes, "algorithmic_bytes": fb},
+        "roofline": {"bound": bound, "achieved": round(achieved, 1), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4),
+                     "traffic": hbm_bytes, "algorithmic_bytes": fb, "flop": fl},
+        "parity": dict(head_row["parity"], all_configs_ok=all(r["parity"]["ok"] for r in rows),
+                       configs=len(rows)),
+        "frac_per_config": {r["workload"]: [r["bound"], r["frac"]] for r in rows},
         "per_config": rows,
     }
     if not args.no_cpu:

@@ -90,6 +90,8 @@ def library():
         lib.tg_conv_bn_act_create.restype = i
         lib.tg_conv_bn_act_create_out.argtypes = [pp] + [i] * 9 + [i, i, i, i]
         lib.tg_conv_bn_act_create_out.restype = i
+        lib.tg_conv_bn_silu_create_tuned.argtypes = [pp] + [i] * 9 + [i, i, i, i, ctypes.c_char_p]
+        lib.tg_conv_bn_silu_create_tuned.restype = i
         lib.tg_conv_bn_silu_run.argtypes = [vp] * 6 + [vp, sz, vp]
         lib.tg_conv_bn_silu_run.restype = i
         lib.tg_conv_bn_silu_run_residual.argtypes = [vp] * 7 + [vp]
@@ -179,6 +181,16 @@ def _as_dtype(d) -> Dtype:
             "f8": Dtype.F8_E4M3, "fp8": Dtype.F8_E4M3, "f8_e4m3": Dtype.F8_E4M3}[str(d)]
 
 
+def tuning_string(tuning) -> bytes | None:
+    """A dict {key: int} (or a ready "key=value,..." string) as the tuning
+    text tg_conv_bn_silu_create_tuned takes; None for no overrides."""
+    if tuning is None:
+        return None
+    if isinstance(tuning, (str, bytes)):
+        return tuning.encode() if isinstance(tuning, str) else tuning
+    return ",".join("%s=%d" % (k, int(v)) for k, v in sorted(tuning.items())).encode()
+
+
 def _as_kernel(k) -> int:
     if isinstance(k, (int, Kernel)):
         return int(k)
@@ -197,10 +209,13 @@ class ConvBnSilu:
     ``run(x, w, scale, bias)`` takes device tensors: x NHWC [N,H,W,C_in], w
     OHWI [C_out,kh,kw,C_in] in the plan's dtype, scale/bias fp32 [C_out]
     (from ``bn_fold``); it returns y NHWC [N,P,Q,C_out] (or writes ``out``).
+    ``tuning`` ({key: int} or "key=value,...") selects kernel variants
+    explicitly (tg_conv_bn_silu_create_tuned); the library reads no
+    environment variables.
     """
 
     def __init__(self, N, H, W, C_in, C_out, kh, kw=None, stride=1, pad=0, dtype="f16",
-                 kernel="auto", table=Table.MI355X, act="silu", out_dtype=None):
+                 kernel="auto", table=Table.MI355X, act="silu", out_dtype=None, tuning=None):
         kw = kh if kw is None else kw
         self.shape = (N, H, W, C_in, C_out, kh, kw, stride, pad)
         self.dtype = _as_dtype(dtype)
@@ -208,7 +223,14 @@ class ConvBnSilu:
         self.act = Activation[str(act).upper()] if not isinstance(act, Activation) else act
         self._lib = library()
         h = ctypes.c_void_p()
-        if self.out_dtype != self.dtype:
+        self.tuning = tuning_string(tuning)
+        if self.tuning is not None:
+            if table != Table.MI355X:
+                raise ValueError("tuning overrides use the MI355X dispatch table")
+            st = self._lib.tg_conv_bn_silu_create_tuned(
+                ctypes.byref(h), N, H, W, C_in, C_out, kh, kw, stride, pad, int(self.dtype),
+                _as_kernel(kernel), int(self.act), int(self.out_dtype), self.tuning)
+        elif self.out_dtype != self.dtype:
             if table != Table.MI355X:
                 raise ValueError("an fp8 output uses the MI355X dispatch table")
             st = self._lib.tg_conv_bn_act_create_out(

@@ -10,13 +10,44 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
+#include <vector>
 
 #include "tg_conv_bn_silu.h"
 #include "tg_device.hpp"
 #include "tg_internal.hpp"
 
 using namespace tg;
+
+namespace tg {
+
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes) {
+    struct Entry {
+        const void* kernel;
+        int device;
+        size_t bytes;
+    };
+    static std::mutex mu;
+    static std::vector<Entry> set;  // limits raised so far
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    for (Entry& en : set)
+        if (en.kernel == kernel && en.device == dev) {
+            if (en.bytes >= bytes) return hipSuccess;
+            e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)bytes);
+            if (e == hipSuccess) en.bytes = bytes;
+            return e;
+        }
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) set.push_back({kernel, dev, bytes});
+    return e;
+}
+
+}  // namespace tg
 
 struct tg_conv_bn_silu_plan {
     ConvGeom g;
@@ -33,6 +64,8 @@ struct tg_conv_bn_silu_plan {
     int rw_grid;     // persistent grid of the register-weights variant
     int rw_nf, rw_cs, rw_ncw;  // its weight fragments per wave, waves per block, waves per WG
     bool rw_nt;      // non-temporal y stores in the register-weights variant
+    int stream_waves;  // > 0: the streaming 1x1 kernel with this many waves per CU
+    int xdma;        // ... staging x through LDS with this prefetch depth (0: off)
     int cu_waves;    // > 0: one-workgroup-per-CU variant with this many wavefronts
     int cu_pd;       // ... and this input prefetch depth
     int patch_cfg;   // >= 0: patch-staged implicit GEMM with this tile
@@ -56,15 +89,74 @@ const double kLdsBytesPerClkCu = 213.0;     // ds_read_b128, conflict-free
 const double kHbmBytesPerSec = 5.0e12;      // mixed read/write streaming
 const double kL2FillBytesPerClkCu = 64.0;
 
-bool env_flag(const char* name) {
-    const char* v = getenv(name);
-    return v && v[0] && strcmp(v, "0") != 0;
+// Kernel-variant overrides for measurement and tests
+// (tg_conv_bn_silu_create_tuned). Each field is -1 unless the caller's tuning
+// string sets it; plans never read the process environment.
+struct Tuning {
+    int cu = -1, cu_pd = -1, igemm_rw = -1, rw_nf = -1, rw_cs = -1, rw_ncw = -1;
+    int rw_wg_per_cu = -1, nt = -1, stream = -1, xdma = -1, igemm_patch = -1;
+    int patch_cfg = -1, igemm_dma = -1, dma_cfg = -1, igemm_cfg = -1, stem = -1;
+    int stem_rows = -1, tiled_mfma = -1, tm_rows = -1, tm_pipe = -1, tm_wg_per_cu = -1;
+};
+
+struct TuningKey {
+    const char* name;
+    int Tuning::*field;
+};
+const TuningKey kTuningKeys[] = {
+    {"cu", &Tuning::cu}, {"cu_pd", &Tuning::cu_pd}, {"igemm_rw", &Tuning::igemm_rw},
+    {"rw_nf", &Tuning::rw_nf}, {"rw_cs", &Tuning::rw_cs}, {"rw_ncw", &Tuning::rw_ncw},
+    {"rw_wg_per_cu", &Tuning::rw_wg_per_cu}, {"nt", &Tuning::nt}, {"stream", &Tuning::stream},
+    {"xdma", &Tuning::xdma}, {"igemm_patch", &Tuning::igemm_patch},
+    {"patch_cfg", &Tuning::patch_cfg}, {"igemm_dma", &Tuning::igemm_dma},
+    {"dma_cfg", &Tuning::dma_cfg}, {"igemm_cfg", &Tuning::igemm_cfg}, {"stem", &Tuning::stem},
+    {"stem_rows", &Tuning::stem_rows}, {"tiled_mfma", &Tuning::tiled_mfma},
+    {"tm_rows", &Tuning::tm_rows}, {"tm_pipe", &Tuning::tm_pipe},
+    {"tm_wg_per_cu", &Tuning::tm_wg_per_cu},
+};
+
+// "key=value[,key=value...]" with known keys and values in [0, 2^20); NULL or
+// "" is no override. Returns false for anything else.
+bool parse_tuning(const char* s, Tuning* t) {
+    *t = Tuning();
+    if (!s) return true;
+    while (*s) {
+        const char* eq = strchr(s, '=');
+        if (!eq) return false;
+        const size_t klen = (size_t)(eq - s);
+        const TuningKey* key = nullptr;
+        for (const TuningKey& k : kTuningKeys)
+            if (strlen(k.name) == klen && strncmp(k.name, s, klen) == 0) key = &k;
+        if (!key) return false;
+        const char* v = eq + 1;
+        long val = 0;
+        int digits = 0;
+        while (*v >= '0' && *v <= '9' && digits < 8) {
+            val = val * 10 + (*v - '0');
+            ++v;
+            ++digits;
+        }
+        if (digits == 0 || val >= (1L << 20) || (*v != ',' && *v != '\0')) return false;
+        if (*v == ',' && v[1] == '\0') return false;  // trailing comma
+        t->*(key->field) = (int)val;
+        s = *v == ',' ? v + 1 : v;
+    }
+    return true;
 }
 
-int env_int(const char* name, int dflt) {
-    const char* v = getenv(name);
-    if (!v || !v[0]) return dflt;
-    return atoi(v);
+// The override if given, else the default.
+int tuned(int v, int dflt) { return v >= 0 ? v : dflt; }
+
+// An enum argument as the int the caller passed. C callers may pass any int
+// where the header names an enum; reading such a value through the C++ enum
+// type is undefined when it lies outside the enum's range, so entry points
+// take the bits as an int first and validate that.
+template <class E>
+int ival(const E& e) {
+    static_assert(sizeof(E) == sizeof(int), "enum arguments are int-sized");
+    int v;
+    memcpy(&v, &e, sizeof(v));
+    return v;
 }
 
 long long out_extent(long long in, long long k, long long stride, long long pad) {
@@ -141,8 +233,8 @@ double igemm_dma_cost(const ConvGeom& g, const IgemmCfg& c) {
     return per_cu * (double)c.BM * c.BN * g.K * lds_factor * overlap;
 }
 
-int choose_igemm_dma_cfg(const ConvGeom& g) {
-    int forced = env_int("TG_DMA_CFG", -1);
+int choose_igemm_dma_cfg(const ConvGeom& g, const Tuning& tu) {
+    int forced = tu.dma_cfg;
     if (forced >= 0 && forced < igemm_dma_num_cfgs()) return forced;
     int best = 0;
     double best_cost = 1e300;
@@ -153,8 +245,8 @@ int choose_igemm_dma_cfg(const ConvGeom& g) {
     return best;
 }
 
-int choose_igemm_cfg(const ConvGeom& g) {
-    int forced = env_int("TG_IGEMM_CFG", -1);
+int choose_igemm_cfg(const ConvGeom& g, const Tuning& tu) {
+    int forced = tu.igemm_cfg;
     if (forced >= 0 && forced < igemm_num_cfgs()) return forced;
     int best = 0;
     double best_cost = 1e300;
@@ -207,17 +299,23 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in, int C_out, int kh,
-                      int kw, int stride, int pad, tg_dtype dtype, tg_kernel kernel,
-                      tg_dispatch table, tg_activation act = TG_ACT_SILU,
-                      bool out_fp8 = false) {
+                      int kw, int stride, int pad, int dtype_v, int kernel_v, int table_v,
+                      int act_v = TG_ACT_SILU, bool out_fp8 = false,
+                      const char* tuning = nullptr) {
     if (!out) return TG_ERR_INVALID_ARGUMENT;
     *out = nullptr;
+    Tuning tu;
+    if (!parse_tuning(tuning, &tu)) return TG_ERR_INVALID_ARGUMENT;
     ConvGeom g;
     tg_status st = make_geom(N, H, W, C_in, C_out, kh, kw, stride, pad, &g);
     if (st != TG_OK) return st;
-    if (dtype != TG_F16 && dtype != TG_F32) return TG_ERR_UNSUPPORTED;
-    if (table != TG_DISPATCH_MI355X && table != TG_DISPATCH_PAGES) return TG_ERR_UNSUPPORTED;
-    int kv = (int)kernel;
+    if (dtype_v != TG_F16 && dtype_v != TG_F32) return TG_ERR_UNSUPPORTED;
+    if (table_v != TG_DISPATCH_MI355X && table_v != TG_DISPATCH_PAGES) return TG_ERR_UNSUPPORTED;
+    if (act_v < TG_ACT_SILU || act_v > TG_ACT_NONE) return TG_ERR_UNSUPPORTED;
+    const tg_dtype dtype = (tg_dtype)dtype_v;
+    const tg_dispatch table = (tg_dispatch)table_v;
+    const tg_activation act = (tg_activation)act_v;
+    int kv = kernel_v;
     bool unfused = (kv & TG_UNFUSED) != 0;
     bool split = (kv & TG_SPLIT) != 0;
     if (unfused && split) return TG_ERR_UNSUPPORTED;
@@ -250,56 +348,57 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
     p.kernel = p.forced ? base : (int)dispatch(g, dtype, table);
     if (p.kernel == TG_KERNEL_IGEMM) {
         if (!igemm_serves(g, dtype)) return TG_ERR_UNSUPPORTED;
-        if (igemm_rw_serves(g) && env_int("TG_IGEMM_RW", 1) != 0 &&
-            env_int("TG_IGEMM_CFG", -1) < 0) {
+        if (igemm_rw_serves(g) && tuned(tu.igemm_rw, 1) != 0 && tu.igemm_cfg < 0) {
             p.igemm_cfg = -1;
             igemm_rw_choose(g, &p.rw_nf, &p.rw_cs, &p.rw_ncw);
-            p.rw_nf = env_int("TG_RW_NF", p.rw_nf);
-            p.rw_cs = env_int("TG_RW_CS", p.rw_cs);
-            p.rw_ncw = env_int("TG_RW_NCW", p.rw_ncw);
+            p.rw_nf = tuned(tu.rw_nf, p.rw_nf);
+            p.rw_cs = tuned(tu.rw_cs, p.rw_cs);
+            p.rw_ncw = tuned(tu.rw_ncw, p.rw_ncw);
             if (!igemm_rw_valid(g, p.rw_nf, p.rw_cs, p.rw_ncw))  // override does not fit
                 igemm_rw_choose(g, &p.rw_nf, &p.rw_cs, &p.rw_ncw);
-            p.rw_grid = igemm_rw_grid(g, kCUs * env_int("TG_RW_WG_PER_CU", 1));
-            p.rw_nt = env_int("TG_NT", 1) != 0;
-            // TG_CU: wavefronts per 64-channel slice of the one-workgroup-per-CU
-            // kernel (0 disables it); TG_CU_PD: input blocks in flight per
+            p.rw_grid = igemm_rw_grid(g, kCUs * (tu.rw_wg_per_cu > 0 ? tu.rw_wg_per_cu : 1));
+            p.rw_nt = tuned(tu.nt, 1) != 0;
+            p.stream_waves = tu.stream > 0 ? tu.stream : 0;
+            p.xdma = tuned(tu.xdma, 0);
+            // cu: wavefronts per 64-channel slice of the one-workgroup-per-CU
+            // kernel (0 disables it); cu_pd: input blocks in flight per
             // wavefront (1..3). 3 and 3 (12 wavefronts for 256 channels, three
             // blocks ahead) measured best on MI355X for the 1x1 C_in=64 layer
             // with settled clocks (12.9 us mean over four runs against 13.5 us
             // two blocks ahead, and a tighter spread). The register-weights
             // kernel stays the fallback for BatchNorm vectors that are not
             // 16-byte aligned.
-            if (igemm_cu_serves(g) && env_int("TG_CU", 3) > 0) {
-                p.cu_waves = igemm_cu_waves(g, env_int("TG_CU", 3));
-                p.cu_pd = env_int("TG_CU_PD", 3);
+            if (igemm_cu_serves(g) && tuned(tu.cu, 3) > 0) {
+                p.cu_waves = igemm_cu_waves(g, tuned(tu.cu, 3));
+                p.cu_pd = tuned(tu.cu_pd, 3);
+                if (p.cu_pd < 1 || p.cu_pd > 3) return TG_ERR_INVALID_ARGUMENT;
             }
-        } else if (igemm_patch_serves(g) && env_int("TG_IGEMM_PATCH", 1) != 0 &&
-                   env_int("TG_IGEMM_CFG", -1) < 0) {
-            // TG_PATCH_CFG forces a tile (if it fits this shape's LDS need).
+        } else if (igemm_patch_serves(g) && tuned(tu.igemm_patch, 1) != 0 &&
+                   tu.igemm_cfg < 0) {
+            // patch_cfg forces a tile (if it fits this shape's LDS need).
             p.igemm_cfg = 0;
-            int forced = env_int("TG_PATCH_CFG", -1);
+            int forced = tu.patch_cfg;
             p.patch_cfg = igemm_patch_fits(g, forced) ? forced : igemm_patch_choose(g);
-        } else if (igemm_dma_serves(g) && env_int("TG_IGEMM_DMA", 1) != 0 &&
-                   env_int("TG_IGEMM_CFG", -1) < 0) {
+        } else if (igemm_dma_serves(g) && tuned(tu.igemm_dma, 1) != 0 && tu.igemm_cfg < 0) {
             p.igemm_cfg = 0;
-            p.dma_cfg = choose_igemm_dma_cfg(g);
+            p.dma_cfg = choose_igemm_dma_cfg(g, tu);
         } else {
-            p.igemm_cfg = choose_igemm_cfg(g);
+            p.igemm_cfg = choose_igemm_cfg(g, tu);
         }
     } else if (p.kernel == TG_KERNEL_TILED) {
         if (!tiled_serves(g, dtype, &p.tiled)) return TG_ERR_UNSUPPORTED;
-        // TG_STEM: workgroups per CU of the stem kernel (0 disables it);
-        // TG_STEM_ROWS: output rows per band.
-        if (stem_serves(g) && env_int("TG_STEM", 3) > 0) {
-            p.stem_wpc = env_int("TG_STEM", 3);
-            p.stem_rows = env_int("TG_STEM_ROWS", stem_rows(g));
+        // stem: workgroups per CU of the stem kernel (0 disables it);
+        // stem_rows: output rows per band.
+        if (stem_serves(g) && tuned(tu.stem, 3) > 0) {
+            p.stem_wpc = tuned(tu.stem, 3);
+            p.stem_rows = tuned(tu.stem_rows, stem_rows(g));
             if (!stem_rows_ok(g, p.stem_rows)) p.stem_rows = stem_rows(g);
         }
-        if (tiled_mfma_serves(g) && env_int("TG_TILED_MFMA", 1) != 0) {
-            p.tm_rows = env_int("TG_TM_ROWS", tiled_mfma_rows(g));
-            if (tiled_mfma_pipe_serves(g) && env_int("TG_TM_PIPE", 1) != 0) {
-                p.tm_rows = env_int("TG_TM_ROWS", 2);
-                p.tm_pipe_grid = kCUs * env_int("TG_TM_WG_PER_CU", 4);
+        if (tiled_mfma_serves(g) && tuned(tu.tiled_mfma, 1) != 0) {
+            p.tm_rows = tu.tm_rows > 0 ? tu.tm_rows : tiled_mfma_rows(g);
+            if (tiled_mfma_pipe_serves(g) && tuned(tu.tm_pipe, 1) != 0) {
+                p.tm_rows = tu.tm_rows > 0 ? tu.tm_rows : 2;
+                p.tm_pipe_grid = kCUs * (tu.tm_wg_per_cu > 0 ? tu.tm_wg_per_cu : 4);
             }
         }
     }
@@ -308,11 +407,6 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
 
     tg_conv_bn_silu_plan* h = new (std::nothrow) tg_conv_bn_silu_plan(p);
     if (!h) return TG_ERR_UNSUPPORTED;
-    if (env_flag("TG_LOG")) {
-        char buf[256];
-        tg_conv_bn_silu_describe(h, buf, sizeof(buf));
-        fprintf(stderr, "[tgconv] %s\n", buf);
-    }
     *out = h;
     return TG_OK;
 }
@@ -330,9 +424,9 @@ hipError_t launch_conv(const tg_conv_bn_silu_plan* plan, const ConvGeom& g, int 
             if (plan->cu_waves > 0 && aligned16(bn_scale) && aligned16(bn_bias))
                 e = launch_igemm_cu(g, plan->cu_waves, plan->cu_pd, plan->rw_nt, epi, x, w,
                                     bn_scale, bn_bias, conv_out, s);
-            else if (plan->igemm_cfg < 0 && env_int("TG_STREAM", 0) > 0 &&
+            else if (plan->igemm_cfg < 0 && plan->stream_waves > 0 &&
                      (epi == EPI_FUSED || epi == EPI_IDENTITY))
-                e = launch_igemm_stream(g, env_int("TG_STREAM", 16), plan->rw_nt, epi, x, w,
+                e = launch_igemm_stream(g, plan->stream_waves, plan->xdma, plan->rw_nt, epi, x, w,
                                         bn_scale, bn_bias, conv_out, s);
             else if (plan->patch_cfg >= 0)
                 e = launch_igemm_patch(g, plan->patch_cfg, epi, x, w, bn_scale, bn_bias,
@@ -392,7 +486,7 @@ extern "C" {
 tg_status tg_conv_bn_silu_create(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
                                  int C_out, int kh, int kw, int stride, int pad, tg_dtype dtype,
                                  tg_kernel kernel) {
-    return create_impl(out, N, H, W, C_in, C_out, kh, kw, stride, pad, dtype, kernel,
+    return create_impl(out, N, H, W, C_in, C_out, kh, kw, stride, pad, ival(dtype), ival(kernel),
                        TG_DISPATCH_MI355X);
 }
 
@@ -400,26 +494,44 @@ tg_status tg_conv_bn_silu_create_with_table(tg_conv_bn_silu_plan** out, int N, i
                                             int C_in, int C_out, int kh, int kw, int stride,
                                             int pad, tg_dtype dtype, tg_kernel kernel,
                                             tg_dispatch table) {
-    return create_impl(out, N, H, W, C_in, C_out, kh, kw, stride, pad, dtype, kernel, table);
+    return create_impl(out, N, H, W, C_in, C_out, kh, kw, stride, pad, ival(dtype), ival(kernel),
+                       ival(table));
 }
 
 tg_status tg_conv_bn_act_create(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
                                 int C_out, int kh, int kw, int stride, int pad, tg_dtype dtype,
                                 tg_kernel kernel, tg_activation act) {
+    return create_impl(out, N, H, W, C_in, C_out, kh, kw, stride, pad, ival(dtype), ival(kernel),
+                       TG_DISPATCH_MI355X, ival(act));
+}
+
+// y in the input dtype or fp8; anything else is TG_ERR_UNSUPPORTED.
+static tg_status create_out(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in, int C_out,
+                            int kh, int kw, int stride, int pad, int dtype, int kernel, int act,
+                            int y_dtype, const char* tuning) {
+    if (y_dtype != dtype && y_dtype != TG_F8_E4M3) {
+        if (out) *out = nullptr;
+        return TG_ERR_UNSUPPORTED;
+    }
     return create_impl(out, N, H, W, C_in, C_out, kh, kw, stride, pad, dtype, kernel,
-                       TG_DISPATCH_MI355X, act);
+                       TG_DISPATCH_MI355X, act, y_dtype == TG_F8_E4M3,
+                       tuning);
 }
 
 tg_status tg_conv_bn_act_create_out(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
                                     int C_out, int kh, int kw, int stride, int pad,
                                     tg_dtype dtype, tg_kernel kernel, tg_activation act,
                                     tg_dtype y_dtype) {
-    if (y_dtype != dtype && y_dtype != TG_F8_E4M3) {
-        if (out) *out = nullptr;
-        return TG_ERR_UNSUPPORTED;
-    }
-    return create_impl(out, N, H, W, C_in, C_out, kh, kw, stride, pad, dtype, kernel,
-                       TG_DISPATCH_MI355X, act, y_dtype == TG_F8_E4M3);
+    return create_out(out, N, H, W, C_in, C_out, kh, kw, stride, pad, ival(dtype), ival(kernel),
+                      ival(act), ival(y_dtype), nullptr);
+}
+
+tg_status tg_conv_bn_silu_create_tuned(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
+                                       int C_out, int kh, int kw, int stride, int pad,
+                                       tg_dtype dtype, tg_kernel kernel, tg_activation act,
+                                       tg_dtype y_dtype, const char* tuning) {
+    return create_out(out, N, H, W, C_in, C_out, kh, kw, stride, pad, ival(dtype), ival(kernel),
+                      ival(act), ival(y_dtype), tuning);
 }
 
 tg_status tg_conv_bn_silu_destroy(tg_conv_bn_silu_plan* plan) {
@@ -456,10 +568,7 @@ static tg_status run_impl(const tg_conv_bn_silu_plan* plan, const void* x, const
     ConvGeom gr = g;
     gr.res = residual;
     hipError_t e = launch_conv(plan, gr, kernel, epi, x, w, bn_scale, bn_bias, conv_out, s);
-    if (e != hipSuccess) {
-        if (env_flag("TG_LOG")) fprintf(stderr, "[tgconv] launch failed: %s\n", hipGetErrorString(e));
-        return TG_ERR_HIP;
-    }
+    if (e != hipSuccess) return TG_ERR_HIP;
     if (plan->unfused) {
         long long total = (long long)g.M * g.C_out;
         e = launch_bn_apply(f32, conv_out, bn_scale, bn_bias, t2, total, g.C_out, s);
@@ -519,7 +628,7 @@ tg_status tg_conv_bn_silu_train_run(const tg_conv_bn_silu_plan* plan, const void
 }
 
 static tg_status transpose_entry(const void* src, void* dst, long long B, long long R,
-                                 long long S, tg_dtype dtype, void* stream) {
+                                 long long S, int dtype, void* stream) {
     if (!src || !dst || src == dst || B < 1 || R < 1 || S < 1) return TG_ERR_INVALID_ARGUMENT;
     if (dtype != TG_F16 && dtype != TG_F32) return TG_ERR_UNSUPPORTED;
     if (B * R * S >= (1LL << 31)) return TG_ERR_UNSUPPORTED;
@@ -531,19 +640,19 @@ static tg_status transpose_entry(const void* src, void* dst, long long B, long l
 tg_status tg_nchw_to_nhwc(const void* src, void* dst, int N, int C, int H, int W,
                           tg_dtype dtype, void* stream) {
     if (N < 1 || C < 1 || H < 1 || W < 1) return TG_ERR_INVALID_ARGUMENT;
-    return transpose_entry(src, dst, N, C, (long long)H * W, dtype, stream);
+    return transpose_entry(src, dst, N, C, (long long)H * W, ival(dtype), stream);
 }
 
 tg_status tg_nhwc_to_nchw(const void* src, void* dst, int N, int C, int H, int W,
                           tg_dtype dtype, void* stream) {
     if (N < 1 || C < 1 || H < 1 || W < 1) return TG_ERR_INVALID_ARGUMENT;
-    return transpose_entry(src, dst, N, (long long)H * W, C, dtype, stream);
+    return transpose_entry(src, dst, N, (long long)H * W, C, ival(dtype), stream);
 }
 
 tg_status tg_filter_oihw_to_ohwi(const void* src, void* dst, int C_out, int C_in, int kh, int kw,
                                  tg_dtype dtype, void* stream) {
     if (C_out < 1 || C_in < 1 || kh < 1 || kw < 1) return TG_ERR_INVALID_ARGUMENT;
-    return transpose_entry(src, dst, C_out, C_in, (long long)kh * kw, dtype, stream);
+    return transpose_entry(src, dst, C_out, C_in, (long long)kh * kw, ival(dtype), stream);
 }
 
 tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan* plan, const void* x, const void* w,
@@ -594,11 +703,7 @@ tg_status tg_conv_bn_silu_run_packed(const tg_conv_bn_silu_plan* plan, const voi
     if (!aligned16(x) || !aligned16(w_packed) || !aligned16(y)) return TG_ERR_ALIGNMENT;
     hipError_t e = launch_igemm_patch(plan->g, plan->patch_cfg, plan->epi, x, w_packed,
                                       bn_scale, bn_bias, y, (hipStream_t)stream, true);
-    if (e != hipSuccess) {
-        if (env_flag("TG_LOG")) fprintf(stderr, "[tgconv] launch failed: %s\n", hipGetErrorString(e));
-        return TG_ERR_HIP;
-    }
-    return TG_OK;
+    return e == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 
 tg_status tg_bn_fold(const float* gamma, const float* beta, const float* mean, const float* var,
@@ -683,14 +788,15 @@ tg_status tg_dispatch_choose(int N, int H, int W, int C_in, int C_out, int kh, i
     ConvGeom g;
     tg_status st = make_geom(N, H, W, C_in, C_out, kh, kw, stride, pad, &g);
     if (st != TG_OK) return st;
-    if (dtype != TG_F16 && dtype != TG_F32) return TG_ERR_UNSUPPORTED;
-    if (table != TG_DISPATCH_MI355X && table != TG_DISPATCH_PAGES) return TG_ERR_UNSUPPORTED;
-    *chosen = dispatch(g, dtype, table);
+    const int dt = ival(dtype), tb = ival(table);
+    if (dt != TG_F16 && dt != TG_F32) return TG_ERR_UNSUPPORTED;
+    if (tb != TG_DISPATCH_MI355X && tb != TG_DISPATCH_PAGES) return TG_ERR_UNSUPPORTED;
+    *chosen = dispatch(g, (tg_dtype)dt, (tg_dispatch)tb);
     return TG_OK;
 }
 
-const char* tg_status_string(tg_status s) {
-    switch (s) {
+const char* tg_status_string(tg_status st) {
+    switch (ival(st)) {
         case TG_OK: return "ok";
         case TG_ERR_INVALID_ARGUMENT: return "invalid argument";
         case TG_ERR_UNSUPPORTED: return "unsupported";
@@ -702,7 +808,7 @@ const char* tg_status_string(tg_status s) {
 }
 
 const char* tg_kernel_name(tg_kernel k) {
-    int kv = (int)k;
+    int kv = ival(k);
     bool unf = (kv & TG_UNFUSED) != 0, spl = (kv & TG_SPLIT) != 0;
     if (unf && spl) return "unknown kernel";
     switch (kv & ~(TG_UNFUSED | TG_SPLIT)) {

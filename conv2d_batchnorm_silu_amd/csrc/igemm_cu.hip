@@ -246,13 +246,9 @@ hipError_t launch_cu_t(const ConvGeom& g, int grid, int nwaves, const void* x, c
     const CuLayout L = cu_layout(g.C_out, nwaves, PD);
     if (L.bytes > kCuMaxLdsBytes) return hipErrorInvalidValue;
     const int lds = L.bytes > kCuMinLdsBytes ? L.bytes : kCuMinLdsBytes;
-    static int attr_bytes = 0;  // largest dynamic LDS size enabled so far
-    if (lds > attr_bytes) {
-        hipError_t e = hipFuncSetAttribute((const void*)conv2d_bn_silu_igemm_cu<EPI, NT, PD, OUT8, RES>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        attr_bytes = lds;
-    }
+    hipError_t e = ensure_dynamic_lds(
+        (const void*)conv2d_bn_silu_igemm_cu<EPI, NT, PD, OUT8, RES>, (size_t)lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL((conv2d_bn_silu_igemm_cu<EPI, NT, PD, OUT8, RES>), dim3(grid), dim3(64 * nwaves), lds,
                        s, (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g.M, g.C_out, nwaves,
                        (const f16*)g.res);

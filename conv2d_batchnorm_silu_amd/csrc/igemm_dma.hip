@@ -307,13 +307,8 @@ static hipError_t dma_launch_one(const ConvGeom& g, int epi, const void* x, cons
 #define TG_K(E) k = conv2d_bn_silu_igemm_dma<BM, BN, WM, WN, RING, WK, E>
     TG_EPI_DISPATCH(epi, TG_K);
 #undef TG_K
-    static bool attr_set[kNumEpilogues] = {};
-    if (!attr_set[epi]) {
-        hipError_t e = hipFuncSetAttribute((const void*)k,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set[epi] = true;
-    }
+    hipError_t e = ensure_dynamic_lds((const void*)k, lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(tiles_m * tiles_n), dim3(64 * S::NW), lds, s, (const f16*)x,
                        (const f16*)w,
                        scale, bias, (f16*)y, g, tiles_m, tiles_n);

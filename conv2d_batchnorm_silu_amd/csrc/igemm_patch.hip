@@ -565,14 +565,8 @@ hipError_t patch_launch_one(const ConvGeom& g, int epi, const void* x, const voi
 #define TG_K(E) k = conv2d_bn_silu_igemm_patch<BM, BN, WM, WN, WK, RING, E>
     TG_EPI_DISPATCH(epi, TG_K);
 #undef TG_K
-    static size_t attr_bytes[kNumEpilogues] = {};
-    size_t& ab = attr_bytes[epi];
-    if (lds > ab) {
-        hipError_t e = hipFuncSetAttribute((const void*)k,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        ab = lds;
-    }
+    hipError_t e = ensure_dynamic_lds((const void*)k, lds);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k, dim3(g.N * tiles_per_img * tiles_n), dim3(64 * (S::NW + 1)), lds, s,
                        (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g, tiles_per_img,
                        tiles_n, patch_layout(g, c).pw, patch_layout(g, c).pstride,

@@ -452,7 +452,7 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_igemm_stream(
     }
 }
 
-hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, bool nt, int epi,
+hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, int xdma, bool nt, int epi,
                                const void* x, const void* w, const float* scale,
                                const float* bias, void* y, hipStream_t s) {
     const int NF = 4, CW = 64;
@@ -470,9 +470,8 @@ hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, bool nt, int
     int ks = g.K <= 32 ? 1 : 2;
     const bool xdma_ok = g.kh == 1 && g.kw == 1 && g.stride == 1 && g.pad == 0 && ks == 2 &&
                          g.C_in == 64 && g.C_out % CW == 0;
-    // TG_XDMA=d (1..4) selects the full-line staging path with prefetch depth d.
-    int pd = 0;
-    if (xdma_ok && getenv("TG_XDMA")) pd = atoi(getenv("TG_XDMA"));
+    // xdma = d (1..4) selects the full-line staging path with prefetch depth d.
+    int pd = xdma_ok ? xdma : 0;
     if (pd < 0 || pd > 4) pd = 0;
 #define TG_ST_LAUNCH(KSV, EPI, NTV)                                                              \
     do {                                                                                         \

@@ -324,14 +324,8 @@ hipError_t launch_stem(const ConvGeom& g, int wg_per_cu, int R, int epi, const v
     do {                                                                                      \
         auto k = conv2d_bn_silu_stem<NBV, EPI, LIV>;                                          \
         const size_t lds = 16 + (size_t)kStemBands * (LIV)*1024 + 4 * 32 * 32 * (NBV) * 2;     \
-        static size_t attr = 0;                                                               \
-        if (lds > attr) {                                                                     \
-            hipError_t e = hipFuncSetAttribute((const void*)k,                                \
-                                               hipFuncAttributeMaxDynamicSharedMemorySize,    \
-                                               (int)lds);                                     \
-            if (e != hipSuccess) return e;                                                    \
-            attr = lds;                                                                       \
-        }                                                                                     \
+        hipError_t e = ensure_dynamic_lds((const void*)k, lds);                               \
+        if (e != hipSuccess) return e;                                                        \
         hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(320), lds, s, (const f16*)x,         \
                            (const f16*)w, scale, bias, (f16*)y, g, R, bands);                  \
         return hipGetLastError();                                                             \

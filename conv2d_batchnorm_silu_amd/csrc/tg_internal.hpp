@@ -39,6 +39,12 @@ struct TiledCfg {
 // Largest band that fits; returns false when the shape cannot be served.
 bool tiled_plan(const ConvGeom& g, TiledCfg* out);
 
+// Raise `kernel`'s dynamic-LDS limit on the current device to at least
+// `bytes` (hipFuncSetAttribute), once per kernel, device and size. Safe when
+// several host threads launch concurrently: the record of limits already set
+// is guarded by a mutex.
+hipError_t ensure_dynamic_lds(const void* kernel, size_t bytes);
+
 hipError_t launch_scalar(const ConvGeom& g, bool f32, int epi, const void* x, const void* w,
                          const float* scale, const float* bias, void* y, hipStream_t s);
 hipError_t launch_tiled(const ConvGeom& g, const TiledCfg& c, int epi, const void* x,
@@ -54,7 +60,7 @@ int igemm_rw_grid(const ConvGeom& g, int slots);
 hipError_t launch_igemm_rw(const ConvGeom& g, int grid, int nf, int cs, int ncw, bool nt,
                            int epi, const void* x, const void* w, const float* scale,
                            const float* bias, void* y, hipStream_t s);
-hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, bool nt, int epi,
+hipError_t launch_igemm_stream(const ConvGeom& g, int waves_per_cu, int xdma, bool nt, int epi,
                                const void* x, const void* w, const float* scale,
                                const float* bias, void* y, hipStream_t s);
 

@@ -23,9 +23,10 @@
  * the epilogue are fp32; fp16 results are rounded to nearest even.
  *
  * Ownership: the caller owns every device buffer. A plan owns host memory
- * only; create/destroy never touch device memory. Entry points never abort
- * and never print (set TG_LOG=1 in the environment to log dispatch choices
- * to stderr). run() and bn_fold() are asynchronous on the given stream (a
+ * only; create/destroy never touch device memory. Entry points never abort,
+ * never print and never read the process environment (kernel-variant
+ * overrides are explicit: tg_conv_bn_silu_create_tuned). run() and
+ * bn_fold() are asynchronous on the given stream (a
  * hipStream_t passed as void*, NULL = the null stream) and do not
  * synchronise; launch failures are reported as TG_ERR_HIP.
  *
@@ -93,8 +94,7 @@ typedef enum { TG_DISPATCH_MI355X = 0, TG_DISPATCH_PAGES = 1 } tg_dispatch;
  * pad < 0 or a window larger than the padded input; TG_ERR_UNSUPPORTED when
  * any of x, w, y has 2^31 or more elements, when a forced kernel does not
  * serve the shape or dtype, or for an unknown dtype/kernel value. On error
- * *out is set to NULL. For tuning sweeps only, the environment variable
- * TG_IGEMM_CFG=<i> forces the i-th compiled implicit-GEMM tile variant. */
+ * *out is set to NULL. */
 tg_status tg_conv_bn_silu_create(tg_conv_bn_silu_plan **out, int N, int H, int W, int C_in,
                                  int C_out, int kh, int kw, int stride, int pad, tg_dtype dtype,
                                  tg_kernel kernel);
@@ -105,7 +105,10 @@ tg_status tg_conv_bn_silu_create_with_table(tg_conv_bn_silu_plan **out, int N, i
                                             int pad, tg_dtype dtype, tg_kernel kernel,
                                             tg_dispatch table);
 
-/* Run the planned operation on `stream`. x, w, y: device pointers in the
+/* Run the planned operation on `stream` -- conv, BatchNorm and SiLU in one
+ * kernel whose epilogue works on the output tile while it is in registers
+ * ("Fusing an Epilogue", section "The shape of it"), or the unfused / split
+ * sequence the plan's kernel flags select. x, w, y: device pointers in the
  * plan's dtype and the layouts above; bn_scale, bn_bias: device fp32
  * [C_out] (from tg_bn_fold). workspace/workspace_bytes: device scratch for the
  * unfused baseline (two intermediates t1 and t2 of y's size) and the split
@@ -227,6 +230,34 @@ tg_status tg_conv_bn_silu_run_packed(const tg_conv_bn_silu_plan *plan, const voi
                                      const void *w_packed, const float *bn_scale,
                                      const float *bn_bias, void *y, void *stream);
 
+/* Explicit kernel-variant overrides, for measurement sweeps and for tests
+ * that exercise a variant the dispatch table does not pick for the shape
+ * ("Fusing an Epilogue", section "Three kernels for one operation": the
+ * thresholds are measured, so every candidate must be runnable on demand).
+ * Same as tg_conv_bn_act_create_out, plus `tuning`: NULL or a string of
+ * comma-separated key=value pairs (decimal values below 2^20), resolved into
+ * the plan here; run() reads nothing else. Keys:
+ *   cu=<waves per 64-channel slice, 0 = off>, cu_pd=<1..3>   1x1 C_in=64
+ *       one-workgroup-per-CU kernel and its input prefetch depth;
+ *   igemm_rw=0|1, rw_nf, rw_cs, rw_ncw, rw_wg_per_cu, nt=0|1   the
+ *       register-weights 1x1 kernel, its split, grid and non-temporal stores;
+ *   stream=<waves per CU>, xdma=<1..4>   the streaming 1x1 kernel (opt-in)
+ *       and its full-line input staging depth;
+ *   igemm_patch=0|1, patch_cfg=<i>   the patch-staged implicit GEMM and a
+ *       forced tile (ignored when it does not fit the shape);
+ *   igemm_dma=0|1, dma_cfg=<i>, igemm_cfg=<i>   the direct-to-LDS and the
+ *       classic implicit GEMM and their tiles;
+ *   stem=<workgroups per CU, 0 = off>, stem_rows=<rows per band>   the RGB
+ *       stem kernel;
+ *   tiled_mfma=0|1, tm_pipe=0|1, tm_rows, tm_wg_per_cu   the band-staged MFMA
+ *       tiled kernel, its persistent form, band height and grid.
+ * Unknown keys, malformed text or out-of-range values: TG_ERR_INVALID_ARGUMENT.
+ * Other errors as for tg_conv_bn_act_create_out. */
+tg_status tg_conv_bn_silu_create_tuned(tg_conv_bn_silu_plan **out, int N, int H, int W,
+                                       int C_in, int C_out, int kh, int kw, int stride,
+                                       int pad, tg_dtype dtype, tg_kernel kernel,
+                                       tg_activation act, tg_dtype y_dtype, const char *tuning);
+
 /* Free a plan. NULL is a no-op. */
 tg_status tg_conv_bn_silu_destroy(tg_conv_bn_silu_plan *plan);
 
@@ -261,7 +292,9 @@ tg_status tg_nchw_to_nhwc(const void *src, void *dst, int N, int C, int H, int W
 tg_status tg_nhwc_to_nchw(const void *src, void *dst, int N, int C, int H, int W,
                           tg_dtype dtype, void *stream);
 
-/* Describe a plan: output extent, the kernel run() will launch (for aligned
+/* Describe a plan: output extent (P, Q as in the formula at the top), the
+ * kernel of the page's three that run() will launch ("Fusing an Epilogue",
+ * section "Three kernels for one operation"; for aligned
  * pointers; may include TG_UNFUSED or TG_SPLIT) and the workspace it needs. Any out
  * pointer may be NULL. TG_ERR_INVALID_ARGUMENT for a NULL plan. */
 tg_status tg_conv_bn_silu_query(const tg_conv_bn_silu_plan *plan, int *P, int *Q,

@@ -40,6 +40,7 @@ What each function follows:
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 import subprocess
@@ -57,17 +58,50 @@ _dp = ctypes.POINTER(ctypes.c_double)
 _llp = ctypes.POINTER(ctypes.c_longlong)
 
 
+_CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c99",
+           "-Wall", "-Werror"]
+
+
+def _compile(src: str, out: str, extra=()):
+    cmd = ["gcc"] + _CFLAGS + list(extra) + ["-o", out, src, "-lm", "-lpthread"]
+    subprocess.run(cmd, check=True)
+
+
 def build(force: bool = True) -> str:
     """Compile ``oracle.c`` into ``liboracle.so`` with gcc (no fast-math, no
     floating-point contraction)."""
     if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared",
-           "-std=c99", "-Wall", "-Werror", "-o", tmp, _SRC, "-lm", "-lpthread"]
-    subprocess.run(cmd, check=True)
+    _compile(_SRC, tmp)
     os.replace(tmp, _LIB)
     return _LIB
+
+
+def source() -> str:
+    """The text of oracle.c (for the tests that build altered copies)."""
+    with open(_SRC) as f:
+        return f.read()
+
+
+def _configure(lib):
+    i = ctypes.c_int
+    lib.oracle_out_extent.restype = ctypes.c_longlong
+    lib.oracle_out_extent.argtypes = [ctypes.c_longlong] * 4
+    lib.oracle_conv2d.restype = i
+    lib.oracle_conv2d.argtypes = [_dp, _dp] + [i] * 9 + [_dp, i]
+    lib.oracle_batchnorm.restype = None
+    lib.oracle_batchnorm.argtypes = [_dp, ctypes.c_longlong, i, _dp, _dp, _dp, _dp,
+                                     ctypes.c_double, _dp]
+    lib.oracle_silu.restype = None
+    lib.oracle_silu.argtypes = [_dp, ctypes.c_longlong, _dp]
+    lib.oracle_conv_bn_silu.restype = i
+    lib.oracle_conv_bn_silu.argtypes = ([_dp, _dp] + [i] * 9 + [_dp] * 4
+                                        + [ctypes.c_double, _dp, i])
+    lib.oracle_conv_bn_silu_at.restype = i
+    lib.oracle_conv_bn_silu_at.argtypes = ([_dp, _dp] + [i] * 9 + [_dp] * 4
+                                           + [ctypes.c_double, _llp, ctypes.c_longlong, _dp])
+    return lib
 
 
 def _load():
@@ -75,25 +109,30 @@ def _load():
     with _lock:
         if _lib is None:
             build(force=False)
-            lib = ctypes.CDLL(_LIB)
-            i = ctypes.c_int
-            lib.oracle_out_extent.restype = ctypes.c_longlong
-            lib.oracle_out_extent.argtypes = [ctypes.c_longlong] * 4
-            lib.oracle_conv2d.restype = i
-            lib.oracle_conv2d.argtypes = [_dp, _dp] + [i] * 9 + [_dp, i]
-            lib.oracle_batchnorm.restype = None
-            lib.oracle_batchnorm.argtypes = [_dp, ctypes.c_longlong, i, _dp, _dp, _dp, _dp,
-                                             ctypes.c_double, _dp]
-            lib.oracle_silu.restype = None
-            lib.oracle_silu.argtypes = [_dp, ctypes.c_longlong, _dp]
-            lib.oracle_conv_bn_silu.restype = i
-            lib.oracle_conv_bn_silu.argtypes = ([_dp, _dp] + [i] * 9 + [_dp] * 4
-                                                + [ctypes.c_double, _dp, i])
-            lib.oracle_conv_bn_silu_at.restype = i
-            lib.oracle_conv_bn_silu_at.argtypes = ([_dp, _dp] + [i] * 9 + [_dp] * 4
-                                                   + [ctypes.c_double, _llp, ctypes.c_longlong, _dp])
-            _lib = lib
+            _lib = _configure(ctypes.CDLL(_LIB))
     return _lib
+
+
+@contextlib.contextmanager
+def altered(text: str, workdir: str):
+    """Test hook: build ``text`` (an altered copy of oracle.c) in ``workdir``
+    and route every function of this module through it inside the block --
+    how the tests check that a planted mistake in the oracle fails a pin."""
+    global _lib
+    src = os.path.join(workdir, "oracle_altered.c")
+    so = os.path.join(workdir, "liboracle_altered_%d.so" % abs(hash(text)))
+    with open(src, "w") as f:
+        f.write(text)
+    _compile(src, so)
+    alt = _configure(ctypes.CDLL(so))
+    prev = _load()
+    with _lock:
+        _lib = alt
+    try:
+        yield
+    finally:
+        with _lock:
+            _lib = prev
 
 
 def _f64(a) -> np.ndarray:
@@ -105,7 +144,13 @@ def _ptr(a: np.ndarray):
 
 
 def default_threads() -> int:
-    return max(1, min(os.cpu_count() or 1, 64))
+    """Host threads for the oracle: OMP_NUM_THREADS when set (a machine's
+    share of its cores), else every core up to 64."""
+    try:
+        n = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        n = 0
+    return max(1, min(n if n > 0 else (os.cpu_count() or 1), 64))
 
 
 def out_extent(n_in: int, k: int, stride: int, pad: int) -> int:

@@ -8,9 +8,11 @@ Tighter bounds derived from the arithmetic are asserted as well: fp16 output
 rounding contributes at most 2^-11 relative, fp32 accumulation of fp16
 products and the hardware exp2/reciprocal add ~1e-6, so fp16 results must lie
 within 2e-3 * max(1, |oracle|) and fp32 results within 1e-5 * max(1, |oracle|).
+Every output element is compared, at the full workload sizes too.
 """
 from __future__ import annotations
 
+import collections
 import sys
 
 import numpy as np
@@ -66,44 +68,34 @@ def compare(got: np.ndarray, ref: np.ndarray, dtype: str, what: str):
     return worst
 
 
+# Oracle results of full workloads, kept for the other kernels and variants
+# a test module compares on the same inputs (a few hundred MB at most).
+_ORACLE_CACHE: "collections.OrderedDict" = collections.OrderedDict()
+_ORACLE_CACHE_MAX = 6
+
+
 def oracle_full(wl, d):
-    return oracle.conv_bn_silu(d["x"], d["w"], d["gamma"], d["beta"], d["mean"], d["var"],
-                               float(d["eps"]), wl.stride, wl.pad)
+    """The fp64 oracle on every output of ``wl`` (inputs ``d`` from
+    make_inputs(wl)); results are cached per workload."""
+    key = (wl, "silu")
+    hit = _ORACLE_CACHE.get(key)
+    if hit is not None:
+        _ORACLE_CACHE.move_to_end(key)
+        return hit
+    ref = oracle.conv_bn_silu(d["x"], d["w"], d["gamma"], d["beta"], d["mean"], d["var"],
+                              float(d["eps"]), wl.stride, wl.pad)
+    _ORACLE_CACHE[key] = ref
+    while len(_ORACLE_CACHE) > _ORACLE_CACHE_MAX:
+        _ORACLE_CACHE.popitem(last=False)
+    return ref
 
 
-def sample_indices(wl, count: int, seed: int) -> np.ndarray:
-    """Random flat output indices plus every corner pixel's channels and the
-    last output elements (image borders exercise the zero padding)."""
-    total = wl.N * wl.P * wl.Q * wl.C_out
-    rng = np.random.default_rng(seed)
-    idx = set(rng.integers(0, total, size=min(count, total)).tolist())
-    for n in (0, wl.N - 1):
-        for p in (0, wl.P - 1):
-            for q in (0, wl.Q - 1):
-                base = ((n * wl.P + p) * wl.Q + q) * wl.C_out
-                idx.update(range(base, base + wl.C_out))
-    idx.update(range(max(0, total - 64), total))
-    return np.array(sorted(idx), dtype=np.int64)
-
-
-def oracle_at(wl, d, idx):
-    return oracle.conv_bn_silu_at(d["x"], d["w"], d["gamma"], d["beta"], d["mean"], d["var"],
-                                  float(d["eps"]), wl.stride, wl.pad, idx)
-
-
-def check_workload(wl, kernel, d=None, t=None, full_limit=2_000_000, samples=6000):
-    """Run ``kernel`` on ``wl`` and compare: in full when the output is small,
-    else on sampled outputs; returns the GPU result (numpy)."""
+def check_workload(wl, kernel, d=None, t=None):
+    """Run ``kernel`` on ``wl`` and compare every output element with the
+    fp64 oracle; returns the GPU result (numpy)."""
     d = d if d is not None else make_inputs(wl)
     t = t if t is not None else to_device(d)
     plan, y = run_plan(wl, t, kernel)
     got = y.cpu().numpy()
-    assert not np.isnan(got.astype(np.float64)).any(), "NaN in output"
-    total = got.size
-    if total <= full_limit:
-        compare(got, oracle_full(wl, d), wl.dtype, "%s/%s full" % (wl.name, kernel))
-    else:
-        idx = sample_indices(wl, samples, seed=wl.seed + 17)
-        compare(got.ravel()[idx], oracle_at(wl, d, idx), wl.dtype,
-                "%s/%s sampled" % (wl.name, kernel))
+    compare(got, oracle_full(wl, d), wl.dtype, "%s/%s full" % (wl.name, kernel))
     return got

@@ -284,3 +284,66 @@ def test_strings(lib):
     assert B.kernel_name(1 | 0x200) == "split(scalar)"
     assert B.kernel_name(3 | 0x300) == "unknown kernel"
     assert B.kernel_name(77) == "unknown kernel"
+
+
+def _create_tuned(lib, shape, tuning, kernel=0, act=0, dtype=0, y_dtype=0):
+    h = ctypes.c_void_p()
+    st = lib.tg_conv_bn_silu_create_tuned(ctypes.byref(h), *shape, dtype, kernel, act, y_dtype,
+                                          tuning)
+    return st, h
+
+
+def _describe(lib, h):
+    buf = ctypes.create_string_buffer(512)
+    assert lib.tg_conv_bn_silu_describe(h, buf, 512) == OK
+    return buf.value.decode()
+
+
+HEAD = (32, 56, 56, 64, 256, 1, 1, 1, 0)
+
+
+def test_tuned_create_overrides_are_explicit(lib):
+    """Kernel-variant overrides travel in the tuning string and nowhere else:
+    NULL and "" give the default plan, known keys change it, and the plan
+    text shows the forced variant."""
+    st, h0 = _create(lib, *HEAD)
+    assert st == OK
+    default = _describe(lib, h0)
+    for t in (None, b""):
+        st, h = _create_tuned(lib, HEAD, t)
+        assert st == OK and _describe(lib, h) == default
+        lib.tg_conv_bn_silu_destroy(h)
+    st, h = _create_tuned(lib, HEAD, b"cu=2,cu_pd=1")
+    assert st == OK
+    d = _describe(lib, h)
+    assert "igemm_cu" in d and "waves=8" in d and "pd=1" in d, d
+    lib.tg_conv_bn_silu_destroy(h)
+    st, h = _create_tuned(lib, HEAD, b"cu=0")
+    assert st == OK and "igemm_rw" in _describe(lib, h)
+    lib.tg_conv_bn_silu_destroy(h)
+    stem = (64, 224, 224, 3, 16, 3, 3, 2, 1)
+    st, h = _create_tuned(lib, stem, b"stem=0,tm_pipe=0,tm_rows=4")
+    assert st == OK and _describe(lib, h).startswith("tiled_mfma R=4"), _describe(lib, h)
+    lib.tg_conv_bn_silu_destroy(h)
+    lib.tg_conv_bn_silu_destroy(h0)
+
+
+@pytest.mark.parametrize("bad", [b"bogus=1", b"cu", b"cu=", b"cu=x", b"cu=2,", b"cu=2;cu_pd=1",
+                                 b"cu=-1", b"cu=99999999", b"cu=2,,cu_pd=1", b"=3", b"cu_pd=4",
+                                 b"cu_pd=0", b" cu=2"])
+def test_tuned_create_rejects_bad_text(lib, bad):
+    st, h = _create_tuned(lib, HEAD, bad)
+    assert st == INVAL and not h.value
+
+
+def test_library_reads_no_environment(lib, monkeypatch):
+    """The names the library once read from the environment change nothing."""
+    st, h0 = _create(lib, *HEAD)
+    base = _describe(lib, h0)
+    for k, v in (("TG_CU", "0"), ("TG_CU_PD", "1"), ("TG_IGEMM_CFG", "0"), ("TG_PATCH_CFG", "1"),
+                 ("TG_STEM", "0"), ("TG_LOG", "1")):
+        monkeypatch.setenv(k, v)
+    st, h = _create(lib, *HEAD)
+    assert st == OK and _describe(lib, h) == base
+    lib.tg_conv_bn_silu_destroy(h)
+    lib.tg_conv_bn_silu_destroy(h0)

@@ -13,7 +13,7 @@ import oracle
 from conv2d_batchnorm_silu_amd import binding as B
 from conv2d_batchnorm_silu_amd.inputs import WORKLOADS, Workload, make_inputs
 
-from gpu_cases import compare, note, sample_indices
+from gpu_cases import compare, note
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -72,40 +72,38 @@ def test_act_shapes(act, kernel):
 # Kernel variants the dispatcher does not pick for these shapes, each through
 # its switch (same switches as test_variants_gpu).
 VARIANTS = [
-    ({"TG_CU": "0"}, WORKLOADS["conv1x1_c64_k256"].scaled(N=1, H=13, W=17), "igemm_rw"),
-    ({"TG_CU": "0", "TG_IGEMM_RW": "0", "TG_IGEMM_PATCH": "0"},
+    ({"cu": "0"}, WORKLOADS["conv1x1_c64_k256"].scaled(N=1, H=13, W=17), "igemm_rw"),
+    ({"cu": "0", "igemm_rw": "0", "igemm_patch": "0"},
      WORKLOADS["conv3x3_c128_k128"].scaled(N=1, H=17, W=15), "igemm_dma"),
-    ({"TG_CU": "0", "TG_IGEMM_RW": "0", "TG_IGEMM_PATCH": "0", "TG_IGEMM_DMA": "0"},
+    ({"cu": "0", "igemm_rw": "0", "igemm_patch": "0", "igemm_dma": "0"},
      WORKLOADS["conv3x3_c128_k128"].scaled(N=1, H=17, W=15), "igemm"),
-    ({"TG_STEM": "0"}, WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=40), "tiled_mfma_pipe"),
-    ({"TG_STEM": "0", "TG_TM_PIPE": "0"}, WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=36),
+    ({"stem": "0"}, WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=40), "tiled_mfma_pipe"),
+    ({"stem": "0", "tm_pipe": "0"}, WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=36),
      "tiled_mfma"),
-    ({"TG_STEM": "0", "TG_TILED_MFMA": "0"},
+    ({"stem": "0", "tiled_mfma": "0"},
      WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=36), "tiled"),
 ]
 
 
 @pytest.mark.parametrize("act", ACTS)
 @pytest.mark.parametrize("env,wl,prefix", VARIANTS, ids=[v[2] for v in VARIANTS])
-def test_act_variants(monkeypatch, act, env, wl, prefix):
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
+def test_act_variants(tune, act, env, wl, prefix):
+    tune(**env)
     plan = check_act(wl, act)
     assert plan.describe().startswith(prefix), plan.describe()
 
 
-@pytest.mark.parametrize("act", ["relu", "gelu"])
-@pytest.mark.parametrize("name", ["conv1x1_c64_k256", "conv3x3_c128_k128", "stem3x3s2_k24"])
-def test_act_full_size_sampled(name, act):
-    """Full-size workloads in the dispatched configuration, on sampled
-    outputs the oracle computes one by one."""
+@pytest.mark.parametrize("act", ["relu", "gelu", "none"])
+@pytest.mark.parametrize("name", ["conv1x1_c64_k256", "conv3x3_c128_k128", "stem3x3s2_k16",
+                                  "stem3x3s2_k24", "conv7x7_c64_k64"])
+def test_act_full_size(name, act):
+    """Full-size workloads in the dispatched configuration, every output
+    against the oracle's conv_bn_act."""
     wl = WORKLOADS[name]
     d, plan, y = run_act(wl, act)
-    idx = sample_indices(wl, 4000, seed=9)
-    ref = oracle.conv_bn_act_at(d["x"], d["w"], d["gamma"], d["beta"], d["mean"], d["var"],
-                                float(d["eps"]), wl.stride, wl.pad, act, idx)
-    got = y.cpu().numpy().ravel()[idx]
-    compare(got, ref, wl.dtype, "%s/%s sampled" % (name, act))
+    ref = oracle.conv_bn_act(d["x"], d["w"], d["gamma"], d["beta"], d["mean"], d["var"],
+                             float(d["eps"]), wl.stride, wl.pad, act)
+    compare(y.cpu().numpy(), ref, wl.dtype, "%s/%s full" % (name, act))
 
 
 def test_act_rejected_where_unsupported():

@@ -1,12 +1,12 @@
 """GPU parity of the fp8 (OCP E4M3) output cast in the epilogue
 (tg_conv_bn_act_create_out) in every kernel family, against the oracle's
-fp64 result. Bar per element: |gpu - oracle| <= one E4M3 spacing at the
-oracle's value, 2^(max(floor(log2|o|), -6) - 3): round-to-nearest gives at
-most half a spacing; the kernels round the fp32 epilogue result to fp16 first
-(their output tiles are fp16), and that double rounding can move a value
-across an fp8 rounding boundary by one spacing at most. Most elements must
-equal the oracle's own E4M3 rounding exactly (at least 99%). A decode of the
-bytes as fp8 in another layout (FNUZ) would fail both bars by a factor of 2.
+fp64 result. Bar per element: |gpu - oracle| <= (0.5 + 2^-7) E4M3 spacings
+at the oracle's value, spacing 2^(max(floor(log2|o|), -6) - 3):
+round-to-nearest gives at most half a spacing; the kernels round the fp32
+epilogue result to fp16 first (their output tiles are fp16), which adds at
+most 2^-8 of a spacing (derivation at FP8_BAR). Most elements must equal the
+oracle's own E4M3 rounding exactly (at least 99%). A decode of the bytes as
+fp8 in another layout (FNUZ) would fail both bars by a factor of 2.
 """
 from __future__ import annotations
 
@@ -36,6 +36,14 @@ def run_fp8(wl, act="silu", kernel="auto"):
     return d, plan, y.float().cpu().numpy().astype(np.float64)
 
 
+# Half an E4M3 spacing for the final rounding, plus the fp16 rounding before
+# it (fp16 keeps 7 more mantissa bits than E4M3: at most 2^-8 of a spacing,
+# also when that rounding lands on an E4M3 midpoint and the tie goes to even)
+# and the fp32 arithmetic (about 1e-6 relative, under 2^-16 of a spacing):
+# 0.5 + 2^-8 + 2^-16 < 0.5 + 2^-7.
+FP8_BAR = 0.5 + 2.0 ** -7
+
+
 def check_fp8(wl, got, ref, what):
     assert not np.isnan(got).any(), what
     a = np.abs(ref)
@@ -45,7 +53,7 @@ def check_fp8(wl, got, ref, what):
     worst = float((err / spacing).max())
     exact = float((got == oracle.round_fp8_e4m3(ref)).mean())
     note("%s: max error %.3g spacings, %.4f equal to the oracle's rounding" % (what, worst, exact))
-    assert worst <= 1.0 + 1e-9, what
+    assert worst <= FP8_BAR, what
     assert exact >= 0.99, what
 
 
@@ -78,23 +86,22 @@ def test_fp8_shapes(kernel, act):
 
 
 VARIANTS = [
-    ({"TG_CU": "0"}, WORKLOADS["conv1x1_c64_k256"].scaled(N=1, H=13, W=17), "igemm_rw"),
-    ({"TG_CU": "0", "TG_IGEMM_RW": "0", "TG_IGEMM_PATCH": "0"},
+    ({"cu": "0"}, WORKLOADS["conv1x1_c64_k256"].scaled(N=1, H=13, W=17), "igemm_rw"),
+    ({"cu": "0", "igemm_rw": "0", "igemm_patch": "0"},
      WORKLOADS["conv3x3_c128_k128"].scaled(N=1, H=17, W=15), "igemm_dma"),
-    ({"TG_CU": "0", "TG_IGEMM_RW": "0", "TG_IGEMM_PATCH": "0", "TG_IGEMM_DMA": "0"},
+    ({"cu": "0", "igemm_rw": "0", "igemm_patch": "0", "igemm_dma": "0"},
      WORKLOADS["conv3x3_c128_k128"].scaled(N=1, H=17, W=15), "igemm"),
-    ({"TG_STEM": "0"}, WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=40), "tiled_mfma_pipe"),
-    ({"TG_STEM": "0", "TG_TM_PIPE": "0"}, WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=40),
+    ({"stem": "0"}, WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=40), "tiled_mfma_pipe"),
+    ({"stem": "0", "tm_pipe": "0"}, WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=40),
      "tiled_mfma"),
-    ({"TG_STEM": "0", "TG_TILED_MFMA": "0"},
+    ({"stem": "0", "tiled_mfma": "0"},
      WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=36), "tiled"),
 ]
 
 
 @pytest.mark.parametrize("env,wl,prefix", VARIANTS, ids=[v[2] for v in VARIANTS])
-def test_fp8_variants(monkeypatch, env, wl, prefix):
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
+def test_fp8_variants(tune, env, wl, prefix):
+    tune(**env)
     d, plan, got = run_fp8(wl)
     assert plan.describe().startswith(prefix), plan.describe()
     ref = oracle.conv_bn_silu(d["x"], d["w"], d["gamma"], d["beta"], d["mean"], d["var"],
@@ -102,15 +109,15 @@ def test_fp8_variants(monkeypatch, env, wl, prefix):
     check_fp8(wl, got, ref, "%s/%s" % (wl.name, prefix))
 
 
-@pytest.mark.parametrize("name", ["conv1x1_c64_k256", "stem3x3s2_k16"])
-def test_fp8_full_size_sampled(name):
+@pytest.mark.parametrize("name", ["conv1x1_c64_k256", "conv3x3_c128_k128", "stem3x3s2_k16",
+                                  "stem3x3s2_k24", "conv7x7_c64_k64"])
+def test_fp8_full_size(name):
+    """Every output of the full workload in the dispatched configuration."""
     wl = WORKLOADS[name]
     d, plan, got = run_fp8(wl)
-    from gpu_cases import sample_indices
-    idx = sample_indices(wl, 4000, seed=11)
-    ref = oracle.conv_bn_silu_at(d["x"], d["w"], d["gamma"], d["beta"], d["mean"], d["var"],
-                                 float(d["eps"]), wl.stride, wl.pad, idx)
-    check_fp8(wl, got.ravel()[idx], ref, "%s sampled" % name)
+    ref = oracle.conv_bn_silu(d["x"], d["w"], d["gamma"], d["beta"], d["mean"], d["var"],
+                              float(d["eps"]), wl.stride, wl.pad)
+    check_fp8(wl, got, ref, "%s full" % name)
 
 
 def test_fp8_rejected_where_unsupported():

@@ -1,7 +1,7 @@
 """GPU parity: every kernel behind the C ABI against the fp64 oracle.
 
-Covers the six workloads at full size (full comparison where the oracle is
-quick, sampled outputs otherwise), a random sweep of small shapes that span
+Covers the six workloads at full size (every output element against the
+oracle), a random sweep of small shapes that span
 several tiles with ragged tails, the degenerate and edge shapes, the
 BatchNorm fold, fused vs unfused agreement, guard canaries around y, the
 misaligned-pointer fallback and a non-default stream.

@@ -79,23 +79,22 @@ def test_residual_shapes(kernel, act):
 
 
 VARIANTS = [
-    ({"TG_CU": "0"}, WORKLOADS["conv1x1_c64_k256"].scaled(N=1, H=13, W=17), "igemm_rw"),
-    ({"TG_CU": "0", "TG_IGEMM_RW": "0", "TG_IGEMM_PATCH": "0"},
+    ({"cu": "0"}, WORKLOADS["conv1x1_c64_k256"].scaled(N=1, H=13, W=17), "igemm_rw"),
+    ({"cu": "0", "igemm_rw": "0", "igemm_patch": "0"},
      WORKLOADS["conv3x3_c128_k128"].scaled(N=1, H=17, W=15), "igemm_dma"),
-    ({"TG_CU": "0", "TG_IGEMM_RW": "0", "TG_IGEMM_PATCH": "0", "TG_IGEMM_DMA": "0"},
+    ({"cu": "0", "igemm_rw": "0", "igemm_patch": "0", "igemm_dma": "0"},
      WORKLOADS["conv3x3_c128_k128"].scaled(N=1, H=17, W=15), "igemm"),
-    ({"TG_STEM": "0"}, WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=40), "tiled_mfma_pipe"),
-    ({"TG_STEM": "0", "TG_TM_PIPE": "0"}, WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=40),
+    ({"stem": "0"}, WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=40), "tiled_mfma_pipe"),
+    ({"stem": "0", "tm_pipe": "0"}, WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=40),
      "tiled_mfma"),
-    ({"TG_STEM": "0", "TG_TILED_MFMA": "0"},
+    ({"stem": "0", "tiled_mfma": "0"},
      WORKLOADS["stem3x3s2_k16"].scaled(N=2, H=40, W=36), "tiled"),
 ]
 
 
 @pytest.mark.parametrize("env,wl,prefix", VARIANTS, ids=[v[2] for v in VARIANTS])
-def test_residual_variants(monkeypatch, env, wl, prefix):
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
+def test_residual_variants(tune, env, wl, prefix):
+    tune(**env)
     d, r, plan, got = run_res(wl)
     assert plan.describe().startswith(prefix), plan.describe()
     check_res(wl, d, r, got, "silu", "%s/%s" % (wl.name, prefix))

@@ -1,22 +1,22 @@
 """GPU parity of every kernel variant that the dispatcher does not pick by
-default for some shape, each selected through its environment switch (read
-when a plan is created) and checked against the fp64 oracle:
+default for some shape, each selected through its tuning key
+(tg_conv_bn_silu_create_tuned) and checked against the fp64 oracle:
 
-  * the one-workgroup-per-CU 1x1 kernel (TG_CU = wavefronts per 64-channel
-    slice, TG_CU_PD = input prefetch depth), over C_out = 64..256, ragged
+  * the one-workgroup-per-CU 1x1 kernel (cu = wavefronts per 64-channel
+    slice, cu_pd = input prefetch depth), over C_out = 64..256, ragged
     pixel tails, fewer blocks than compute units and the full headline layer;
   * the streaming 1x1 kernel with and without full-line input staging
-    (TG_STREAM, TG_XDMA = prefetch depth);
+    (stream, xdma = prefetch depth);
   * the register-weights kernel's non-default splits and plain stores;
   * the stem kernel (3-channel 3x3 stride-2 layers) over channel counts,
-    image sizes, pixel tails and wave counts (TG_STEM), and with it switched
+    image sizes, pixel tails and wave counts (stem), and with it switched
     off the band-staged MFMA kernel with and without its persistent
-    pipeline (TG_TM_PIPE) and the VALU tiled kernel (TG_TILED_MFMA=0);
+    pipeline (tm_pipe) and the VALU tiled kernel (tiled_mfma=0);
   * the patch-staged implicit GEMM for stride-1 layers with C_in % 64 == 0
-    in every tile configuration (TG_PATCH_CFG), including partial channel
+    in every tile configuration (patch_cfg), including partial channel
     tiles, ragged pixel tails and channel counts it declines;
   * the direct-to-LDS implicit GEMM in every tile configuration
-    (TG_IGEMM_PATCH=0, TG_DMA_CFG) and the classic one (TG_IGEMM_DMA=0).
+    (igemm_patch=0, dma_cfg) and the classic one (igemm_dma=0).
 """
 import pytest
 
@@ -59,9 +59,9 @@ CU_CFGS = [("2", "1"), ("2", "2"), ("2", "3"), ("3", "2"), ("3", "3"), ("4", "1"
 
 @pytest.mark.parametrize("per_group,pd", CU_CFGS, ids=["r%s_pd%s" % c for c in CU_CFGS])
 @pytest.mark.parametrize("wl", ONE_BY_ONE, ids=[w.name for w in ONE_BY_ONE])
-def test_cu_kernel(monkeypatch, wl, per_group, pd):
-    monkeypatch.setenv("TG_CU", per_group)
-    monkeypatch.setenv("TG_CU_PD", pd)
+def test_cu_kernel(tune, wl, per_group, pd):
+    tune(cu=per_group)
+    tune(cu_pd=pd)
     assert "igemm_cu" in _plan(wl).describe()
     check_workload(wl, "igemm")
     check_workload(wl, "unfused")
@@ -69,16 +69,16 @@ def test_cu_kernel(monkeypatch, wl, per_group, pd):
 
 @pytest.mark.parametrize("per_group,pd", [("2", "2"), ("3", "2"), ("3", "3"), ("4", "1"),
                                           ("4", "2")])
-def test_cu_kernel_headline(monkeypatch, per_group, pd):
-    monkeypatch.setenv("TG_CU", per_group)
-    monkeypatch.setenv("TG_CU_PD", pd)
+def test_cu_kernel_headline(tune, per_group, pd):
+    tune(cu=per_group)
+    tune(cu_pd=pd)
     wl = WORKLOADS["conv1x1_c64_k256"]
     assert "igemm_cu" in _plan(wl, "auto").describe()
     check_workload(wl, "auto")
 
 
-def test_cu_kernel_not_for_other_shapes(monkeypatch):
-    monkeypatch.setenv("TG_CU", "2")
+def test_cu_kernel_not_for_other_shapes(tune):
+    tune(cu="2")
     for wl in (Workload("c32", 48, 1, 9, 9, 32, 256, 1, 1, 1, 0, "f16"),
                Workload("k96", 49, 1, 9, 9, 64, 96, 1, 1, 1, 0, "f16"),
                Workload("s2", 50, 1, 9, 9, 64, 256, 1, 1, 2, 0, "f16")):
@@ -88,30 +88,28 @@ def test_cu_kernel_not_for_other_shapes(monkeypatch):
 
 
 @pytest.mark.parametrize("env", [
-    {"TG_STREAM": "8"},
-    {"TG_STREAM": "8", "TG_XDMA": "1"},
-    {"TG_STREAM": "8", "TG_XDMA": "2"},
-    {"TG_STREAM": "12", "TG_XDMA": "4"},
-    {"TG_STREAM": "8", "TG_NT": "0"},
-], ids=lambda e: "_".join("%s%s" % (k[3:].lower(), v) for k, v in e.items()))
-def test_stream_kernel(monkeypatch, env):
-    monkeypatch.setenv("TG_CU", "0")
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
+    {"stream": "8"},
+    {"stream": "8", "xdma": "1"},
+    {"stream": "8", "xdma": "2"},
+    {"stream": "12", "xdma": "4"},
+    {"stream": "8", "nt": "0"},
+], ids=lambda e: "_".join("%s%s" % (k, v) for k, v in e.items()))
+def test_stream_kernel(tune, env):
+    tune(cu="0")
+    tune(**env)
     for wl in ONE_BY_ONE[:4] + [Workload("c32_k96", 51, 2, 7, 9, 32, 96, 1, 1, 1, 0, "f16")]:
         check_workload(wl, "igemm")
 
 
 @pytest.mark.parametrize("env", [
-    {"TG_RW_NF": "8", "TG_RW_CS": "2", "TG_RW_NCW": "4"},
-    {"TG_RW_NF": "4", "TG_RW_CS": "1", "TG_RW_NCW": "4"},
-    {"TG_NT": "0"},
-    {"TG_RW_WG_PER_CU": "2"},
-], ids=lambda e: "_".join("%s%s" % (k[3:].lower(), v) for k, v in e.items()))
-def test_register_weights_kernel(monkeypatch, env):
-    monkeypatch.setenv("TG_CU", "0")
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
+    {"rw_nf": "8", "rw_cs": "2", "rw_ncw": "4"},
+    {"rw_nf": "4", "rw_cs": "1", "rw_ncw": "4"},
+    {"nt": "0"},
+    {"rw_wg_per_cu": "2"},
+], ids=lambda e: "_".join("%s%s" % (k, v) for k, v in e.items()))
+def test_register_weights_kernel(tune, env):
+    tune(cu="0")
+    tune(**env)
     for wl in ONE_BY_ONE[:4] + [Workload("c8_2x2", 52, 1, 9, 11, 8, 40, 2, 2, 1, 0, "f16")]:
         assert "igemm_rw" in _plan(wl).describe()
         check_workload(wl, "igemm")
@@ -138,13 +136,12 @@ def test_cu_kernel_falls_back_for_unaligned_batchnorm_vectors():
     compare(y.cpu().numpy(), oracle_full(wl, d), "f16", "cu fallback, unaligned scale/bias")
 
 
-@pytest.mark.parametrize("env", [{"TG_TM_PIPE": "0"}, {"TG_TM_PIPE": "0", "TG_TM_ROWS": "4"},
-                                 {"TG_TM_ROWS": "4"}, {"TG_TILED_MFMA": "0"}],
+@pytest.mark.parametrize("env", [{"tm_pipe": "0"}, {"tm_pipe": "0", "tm_rows": "4"},
+                                 {"tm_rows": "4"}, {"tiled_mfma": "0"}],
                          ids=["nopipe", "nopipe_r4", "pipe_r4", "valu"])
-def test_tiled_variants(monkeypatch, env):
-    monkeypatch.setenv("TG_STEM", "0")
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
+def test_tiled_variants(tune, env):
+    tune(stem="0")
+    tune(**env)
     for wl in (WORKLOADS["stem3x3s2_k16"].scaled(N=2), WORKLOADS["stem3x3s2_k24"].scaled(N=1),
                Workload("stem_odd", 53, 1, 37, 29, 3, 24, 3, 3, 2, 1, "f16")):
         check_workload(wl, "tiled")
@@ -164,12 +161,12 @@ STEM_SHAPES = [
 
 
 @pytest.mark.parametrize("wpc,rows", [("3", ""), ("4", "1"), ("2", "2"), ("1", "")])
-def test_stem_kernel(monkeypatch, wpc, rows):
+def test_stem_kernel(tune, wpc, rows):
     """Workgroups per CU and band heights: with one-row bands the full-size
     workloads give each workgroup many bands, so its three band buffers are
     refilled while its compute waves work."""
-    monkeypatch.setenv("TG_STEM", wpc)
-    monkeypatch.setenv("TG_STEM_ROWS", rows)
+    tune(stem=wpc)
+    tune(stem_rows=rows)
     for wl in STEM_SHAPES:
         d = _plan(wl, "tiled").describe()
         note("%s -> %s" % (wl.name, d))
@@ -195,10 +192,10 @@ PATCH_SHAPES = [
 
 
 @pytest.mark.parametrize("cfg", [str(i) for i in range(10)])
-def test_patch_kernel(monkeypatch, cfg):
-    monkeypatch.setenv("TG_CU", "0")
-    monkeypatch.setenv("TG_IGEMM_RW", "0")
-    monkeypatch.setenv("TG_PATCH_CFG", cfg)
+def test_patch_kernel(tune, cfg):
+    tune(cu="0")
+    tune(igemm_rw="0")
+    tune(patch_cfg=cfg)
     ran = 0
     for wl in PATCH_SHAPES:
         d = _plan(wl).describe()
@@ -210,23 +207,22 @@ def test_patch_kernel(monkeypatch, cfg):
 
 
 @pytest.mark.parametrize("cfg", [str(i) for i in range(11)])
-def test_dma_kernel(monkeypatch, cfg):
-    monkeypatch.setenv("TG_CU", "0")
-    monkeypatch.setenv("TG_IGEMM_RW", "0")
-    monkeypatch.setenv("TG_IGEMM_PATCH", "0")
-    monkeypatch.setenv("TG_DMA_CFG", cfg)
+def test_dma_kernel(tune, cfg):
+    tune(cu="0")
+    tune(igemm_rw="0")
+    tune(igemm_patch="0")
+    tune(dma_cfg=cfg)
     for wl in PATCH_SHAPES[:4] + [Workload("s2_c64", 59, 1, 15, 13, 64, 80, 3, 3, 2, 1, "f16")]:
         assert "igemm_dma" in _plan(wl).describe()
         check_workload(wl, "igemm")
 
 
-@pytest.mark.parametrize("env", [{"TG_IGEMM_RW": "0", "TG_IGEMM_PATCH": "0"},
-                                 {"TG_IGEMM_RW": "0", "TG_IGEMM_PATCH": "0", "TG_IGEMM_DMA": "0"}],
+@pytest.mark.parametrize("env", [{"igemm_rw": "0", "igemm_patch": "0"},
+                                 {"igemm_rw": "0", "igemm_patch": "0", "igemm_dma": "0"}],
                          ids=["dma", "classic"])
-def test_igemm_variants(monkeypatch, env):
-    monkeypatch.setenv("TG_CU", "0")
-    for k, v in env.items():
-        monkeypatch.setenv(k, v)
+def test_igemm_variants(tune, env):
+    tune(cu="0")
+    tune(**env)
     for wl in (WORKLOADS["conv3x3_c128_k128"].scaled(N=1, H=17, W=15),
                WORKLOADS["conv7x7_c64_k64"].scaled(N=1, H=13, W=11),
                ONE_BY_ONE[0], ONE_BY_ONE[2]):
