@@ -68,6 +68,7 @@ struct tg_conv_bn_silu_plan {
     int xdma;        // ... staging x through LDS with this prefetch depth (0: off)
     int cu_waves;    // > 0: one-workgroup-per-CU variant with this many wavefronts
     int cu_pd;       // ... and this input prefetch depth
+    bool band;       // band implicit GEMM (all output channels of a pixel band per workgroup)
     int patch_cfg;   // >= 0: patch-staged implicit GEMM with this tile
     int stem_wpc;    // > 0: stem kernel with this many workgroups per CU
     int stem_rows;   // ... and bands of this many output rows
@@ -81,11 +82,14 @@ namespace {
 // and of this count only, so plans are reproducible on any host.
 const int kCUs = 256;
 
-// Measured on MI355X (gfx950): sustained fp16 MFMA rate per SIMD, in FLOP per
-// clock, and the rates of the memory paths the cost model uses.
+// Rates the cost model uses, per clock at 2.4 GHz. The microbenchmarks in
+// peaks.hip (profiles/peaks_mi355x.md) measure on MI355X: 16x16x32 f16 MFMA
+// 922 (one wave per SIMD) to 961 (two) FLOP per clock per SIMD, i.e.
+// 2.27-2.36 PFLOP/s, of which the model assumes 94%; conflict-free
+// ds_read_b128 146 (4 waves) to 250 (8 waves) bytes per clock per CU.
 const double kClock = 2.4e9;
-const double kMfmaFlopPerClkSimd = 871.0;  // 16x16x32 f16, 2.14 PFLOP/s on the whole chip
-const double kLdsBytesPerClkCu = 213.0;     // ds_read_b128, conflict-free
+const double kMfmaFlopPerClkSimd = 871.0;  // 2.14 PFLOP/s on the whole chip
+const double kLdsBytesPerClkCu = 213.0;     // ds_read_b128 at 6-8 waves per CU
 const double kHbmBytesPerSec = 5.0e12;      // mixed read/write streaming
 const double kL2FillBytesPerClkCu = 64.0;
 
@@ -97,6 +101,7 @@ struct Tuning {
     int rw_wg_per_cu = -1, nt = -1, stream = -1, xdma = -1, igemm_patch = -1;
     int patch_cfg = -1, igemm_dma = -1, dma_cfg = -1, igemm_cfg = -1, stem = -1;
     int stem_rows = -1, tiled_mfma = -1, tm_rows = -1, tm_pipe = -1, tm_wg_per_cu = -1;
+    int band = -1;
 };
 
 struct TuningKey {
@@ -112,7 +117,7 @@ const TuningKey kTuningKeys[] = {
     {"dma_cfg", &Tuning::dma_cfg}, {"igemm_cfg", &Tuning::igemm_cfg}, {"stem", &Tuning::stem},
     {"stem_rows", &Tuning::stem_rows}, {"tiled_mfma", &Tuning::tiled_mfma},
     {"tm_rows", &Tuning::tm_rows}, {"tm_pipe", &Tuning::tm_pipe},
-    {"tm_wg_per_cu", &Tuning::tm_wg_per_cu},
+    {"tm_wg_per_cu", &Tuning::tm_wg_per_cu}, {"band", &Tuning::band},
 };
 
 // "key=value[,key=value...]" with known keys and values in [0, 2^20); NULL or
@@ -373,6 +378,12 @@ tg_status create_impl(tg_conv_bn_silu_plan** out, int N, int H, int W, int C_in,
                 p.cu_pd = tuned(tu.cu_pd, 3);
                 if (p.cu_pd < 1 || p.cu_pd > 3) return TG_ERR_INVALID_ARGUMENT;
             }
+        } else if (igemm_band_serves(g) && tuned(tu.band, 0) != 0 && tu.igemm_cfg < 0 &&
+                   // Opt-in: on the 3x3 and 7x7 layers it runs level with
+                   // (3x3) or 8% behind (7x7) the patch-staged kernel below.
+                   tu.patch_cfg < 0 && tu.dma_cfg < 0) {
+            p.igemm_cfg = 0;
+            p.band = true;
         } else if (igemm_patch_serves(g) && tuned(tu.igemm_patch, 1) != 0 &&
                    tu.igemm_cfg < 0) {
             // patch_cfg forces a tile (if it fits this shape's LDS need).
@@ -428,6 +439,8 @@ hipError_t launch_conv(const tg_conv_bn_silu_plan* plan, const ConvGeom& g, int 
                      (epi == EPI_FUSED || epi == EPI_IDENTITY))
                 e = launch_igemm_stream(g, plan->stream_waves, plan->xdma, plan->rw_nt, epi, x, w,
                                         bn_scale, bn_bias, conv_out, s);
+            else if (plan->band)
+                e = launch_igemm_band(g, epi, x, w, bn_scale, bn_bias, conv_out, s);
             else if (plan->patch_cfg >= 0)
                 e = launch_igemm_patch(g, plan->patch_cfg, epi, x, w, bn_scale, bn_bias,
                                        conv_out, s);
@@ -739,6 +752,11 @@ tg_status tg_conv_bn_silu_describe(const tg_conv_bn_silu_plan* plan, char* buf, 
     } else if (plan->kernel == TG_KERNEL_IGEMM && plan->igemm_cfg < 0) {
         snprintf(k, sizeof(k), "igemm_rw (weights in VGPRs) nf=%d cs=%d ncw=%d grid=%d%s",
                  plan->rw_nf, plan->rw_cs, plan->rw_ncw, plan->rw_grid, plan->rw_nt ? " nt" : "");
+    } else if (plan->kernel == TG_KERNEL_IGEMM && plan->band) {
+        int tpx, tiles, lds;
+        igemm_band_describe(g, &tpx, &tiles, &lds);
+        snprintf(k, sizeof(k), "igemm_band tile=%dpx x %dch waves=2x2 grid=%d lds=%d",
+                 tpx, g.C_out, tiles, lds);
     } else if (plan->kernel == TG_KERNEL_IGEMM && plan->patch_cfg >= 0) {
         int BM, BN, WM, WN, WK;
         int ring;

@@ -89,6 +89,12 @@ void igemm_patch_describe(int cfg, int* BM, int* BN, int* WM, int* WN, int* WK, 
 hipError_t launch_igemm_patch(const ConvGeom& g, int cfg, int epi, const void* x,
                               const void* w, const float* scale, const float* bias, void* y,
                               hipStream_t s, bool packed = false);
+// Band implicit GEMM (igemm_band.hip): stride 1, C_in % 64 == 0, C_out 64
+// or 128, the tile's input rows fit LDS next to the filter ring.
+bool igemm_band_serves(const ConvGeom& g);
+void igemm_band_describe(const ConvGeom& g, int* tile_px, int* tiles, int* lds);
+hipError_t launch_igemm_band(const ConvGeom& g, int epi, const void* x, const void* w,
+                             const float* scale, const float* bias, void* y, hipStream_t s);
 // Bytes of tile cfg's packed filter (0: none fits 32-bit offsets), and the
 // load-time pack kernel that writes it from the OHWI filter.
 size_t igemm_patch_packed_bytes(const ConvGeom& g, int cfg);

@@ -243,8 +243,12 @@ tg_status tg_conv_bn_silu_run_packed(const tg_conv_bn_silu_plan *plan, const voi
  *       register-weights 1x1 kernel, its split, grid and non-temporal stores;
  *   stream=<waves per CU>, xdma=<1..4>   the streaming 1x1 kernel (opt-in)
  *       and its full-line input staging depth;
+ *   band=0|1   the band implicit GEMM (opt-in; stride 1, C_in % 64 == 0,
+ *       C_out 64 or 128: all output channels of a band of pixels per
+ *       workgroup; it takes no packed filter);
  *   igemm_patch=0|1, patch_cfg=<i>   the patch-staged implicit GEMM and a
- *       forced tile (ignored when it does not fit the shape);
+ *       forced tile (ignored when it does not fit the shape; a forced
+ *       patch or direct-to-LDS tile also turns the band kernel off);
  *   igemm_dma=0|1, dma_cfg=<i>, igemm_cfg=<i>   the direct-to-LDS and the
  *       classic implicit GEMM and their tiles;
  *   stem=<workgroups per CU, 0 = off>, stem_rows=<rows per band>   the RGB

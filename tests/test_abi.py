@@ -325,6 +325,17 @@ def test_tuned_create_overrides_are_explicit(lib):
     st, h = _create_tuned(lib, stem, b"stem=0,tm_pipe=0,tm_rows=4")
     assert st == OK and _describe(lib, h).startswith("tiled_mfma R=4"), _describe(lib, h)
     lib.tg_conv_bn_silu_destroy(h)
+    # The band implicit GEMM is opt-in; it takes no packed filter.
+    c2 = (32, 28, 28, 128, 128, 3, 3, 1, 1)
+    st, h = _create(lib, *c2)
+    assert st == OK and _describe(lib, h).startswith("igemm_patch"), _describe(lib, h)
+    lib.tg_conv_bn_silu_destroy(h)
+    st, h = _create_tuned(lib, c2, b"band=1")
+    d = _describe(lib, h)
+    assert st == OK and d.startswith("igemm_band tile=112px x 128ch") and "grid=224" in d, d
+    sz = ctypes.c_size_t(7)
+    assert lib.tg_conv_bn_silu_packed_filter_bytes(h, ctypes.byref(sz)) == UNSUP and sz.value == 0
+    lib.tg_conv_bn_silu_destroy(h)
     lib.tg_conv_bn_silu_destroy(h0)
 
 

@@ -227,3 +227,44 @@ def test_igemm_variants(tune, env):
                WORKLOADS["conv7x7_c64_k64"].scaled(N=1, H=13, W=11),
                ONE_BY_ONE[0], ONE_BY_ONE[2]):
         check_workload(wl, "igemm")
+
+
+BAND_SHAPES = [
+    WORKLOADS["conv3x3_c128_k128"].scaled(N=2),
+    WORKLOADS["conv7x7_c64_k64"].scaled(N=1),
+    WORKLOADS["conv3x3_c128_k128"].scaled(N=1, H=17, W=15),
+    WORKLOADS["conv7x7_c64_k64"].scaled(N=2, H=13, W=11),
+    Workload("b5x5_c64_k128", 70, 2, 9, 10, 64, 128, 5, 5, 1, 2, "f16"),
+    Workload("b3x3_c64_k128_wide", 71, 1, 6, 70, 64, 128, 3, 3, 1, 1, "f16"),
+    Workload("b3x3_c192_k64", 72, 2, 8, 8, 192, 64, 3, 3, 1, 1, "f16"),
+    Workload("b1x1_c128_k64", 73, 3, 7, 9, 128, 64, 1, 1, 1, 0, "f16"),
+    Workload("b3x3_nopad_c64_k64", 74, 3, 9, 30, 64, 64, 3, 3, 1, 0, "f16"),
+    Workload("b1px_c128_k128", 75, 1, 1, 1, 128, 128, 3, 3, 1, 1, "f16"),
+    Workload("b3x3_c192_k128_tail", 76, 2, 11, 13, 192, 128, 3, 3, 1, 1, "f16",
+             ("uniform", -2.0, 2.0)),
+]
+
+
+@pytest.mark.parametrize("wl", BAND_SHAPES, ids=[w.name for w in BAND_SHAPES])
+def test_band_kernel(tune, wl):
+    """The band implicit GEMM (opt-in, band=1; stride-1 layers with C_in % 64
+    == 0 and C_out 64 or 128): every output against the oracle, fused and as
+    the first kernel of the unfused and split forms, including odd K-step
+    counts (the zero-filter step past the last chunk) and one-pixel images."""
+    tune(band=1)
+    d = _plan(wl, "auto").describe()
+    note("%s -> %s" % (wl.name, d))
+    assert d.startswith("igemm_band"), d
+    check_workload(wl, "auto")
+    check_workload(wl, "unfused")
+    check_workload(wl, "split")
+
+
+def test_band_declines_other_shapes(tune):
+    tune(band=1)
+    for wl in (Workload("s2", 77, 1, 12, 12, 64, 128, 3, 3, 2, 1, "f16"),
+               Workload("k96", 78, 1, 12, 12, 64, 96, 3, 3, 1, 1, "f16"),
+               Workload("c32", 79, 1, 12, 12, 32, 64, 3, 3, 1, 1, "f16")):
+        d = _plan(wl, "auto").describe()
+        note("%s -> %s" % (wl.name, d))
+        assert not d.startswith("igemm_band"), d
