@@ -474,22 +474,83 @@ hipError_t launch_conv(const tg_conv_bn_silu_plan* plan, const ConvGeom& g, int 
     return e;
 }
 
-// Training-mode workspace: [t1, y-sized][scale fp32 [C]][bias fp32 [C]]
-// [row-block partials, fp64], each piece 256-byte aligned.
+// Training mode keeps t1 in y (the BatchNorm+SiLU pass then works on y in
+// place). Workspace: [scale fp32 [C]][bias fp32 [C]][statistics partials:
+// fp64 row-block sums, or the 1x1 kernel's per-workgroup triples], each
+// piece 256-byte aligned.
 struct TrainWs {
-    size_t t1, scale, bias, partial, total;
+    size_t scale, bias, partial, total;
 };
-TrainWs train_ws(const tg_conv_bn_silu_plan* plan) {
-    const ConvGeom& g = plan->g;
-    const size_t ysz = (size_t)g.M * g.C_out * (plan->dtype == TG_F32 ? 4 : 2);
+TrainWs train_ws(const ConvGeom& g) {
     const size_t vec = round256((size_t)g.C_out * 4);
+    size_t part = bn_train_partial_bytes(g.M, g.C_out);
+    if (igemm_cu_serves(g)) {
+        const size_t chan = bn_train_chan_bytes(igemm_cu_stats_grid(g), g.C_out);
+        if (chan > part) part = chan;
+    }
     TrainWs t;
-    t.t1 = 0;
-    t.scale = round256(ysz);
-    t.bias = t.scale + vec;
-    t.partial = t.bias + vec;
-    t.total = t.partial + round256(bn_train_partial_bytes(g.M, g.C_out));
+    t.scale = 0;
+    t.bias = vec;
+    t.partial = 2 * vec;
+    t.total = t.partial + round256(part);
     return t;
+}
+TrainWs train_ws(const tg_conv_bn_silu_plan* plan) { return train_ws(plan->g); }
+
+// Argument checks shared by the training entry points.
+tg_status train_check(const tg_conv_bn_silu_plan* plan, const void* x, const void* w,
+                      const float* gamma, const float* beta, float eps, float momentum,
+                      const float* running_mean, const float* running_var, const void* y) {
+    if (!plan || !x || !w || !gamma || !beta || !y) return TG_ERR_INVALID_ARGUMENT;
+    if ((running_mean == nullptr) != (running_var == nullptr)) return TG_ERR_INVALID_ARGUMENT;
+    if (!(eps >= 0.0f) || !(momentum >= 0.0f && momentum <= 1.0f)) return TG_ERR_INVALID_ARGUMENT;
+    if (plan->g.M < 2) return TG_ERR_INVALID_ARGUMENT;  // batch statistics need two values per channel
+    if (plan->epi != EPI_FUSED || plan->g.out8) return TG_ERR_UNSUPPORTED;  // SiLU, y in dtype
+    return TG_OK;
+}
+
+// The training passes on stream s, with scale, bias and the statistics
+// partials at ws (train_ws layout, device memory the caller provides).
+tg_status train_core(const tg_conv_bn_silu_plan* plan, const void* x, const void* w,
+                     const float* gamma, const float* beta, float eps, float momentum,
+                     float* running_mean, float* running_var, float* batch_mean,
+                     float* batch_var, void* y, char* ws, hipStream_t s) {
+    const ConvGeom& g = plan->g;
+    const TrainWs L = train_ws(g);
+    const bool f32 = plan->dtype == TG_F32;
+    int kernel = plan->kernel;
+    if (kernel != TG_KERNEL_SCALAR &&
+        !(aligned16(x) && aligned16(w) && aligned16(y) && aligned16(ws))) {
+        if (plan->forced) return TG_ERR_ALIGNMENT;
+        kernel = TG_KERNEL_SCALAR;
+    }
+    float* scale = (float*)(ws + L.scale);
+    float* bias = (float*)(ws + L.bias);
+    double* partial = (double*)(ws + L.partial);
+    hipError_t e;
+    if (kernel == TG_KERNEL_IGEMM && plan->cu_waves > 0 && !plan->unfused && !plan->split && !f32) {
+        // The 1x1 kernel: t1 -> y with the statistics in its epilogue (at
+        // most 12 waves: the statistics take registers).
+        const int ng = g.C_out / 64;
+        int nw = plan->cu_waves;
+        if (nw > 12) nw = 12 / ng * ng;
+        e = launch_igemm_cu_stats(g, nw, plan->cu_pd, x, w, y, partial, s);
+        if (e != hipSuccess) return TG_ERR_HIP;
+        e = launch_bn_train_finalize_chan(partial, igemm_cu_stats_grid(g), g.M, g.C_out, gamma,
+                                          beta, eps, momentum, running_mean, running_var,
+                                          batch_mean, batch_var, scale, bias, s);
+    } else {
+        // 1. conv -> t1 in y (identity epilogue: scale/bias are not read)
+        e = launch_conv(plan, g, kernel, EPI_IDENTITY, x, w, scale, bias, y, s);
+        if (e != hipSuccess) return TG_ERR_HIP;
+        // 2-3. batch statistics -> scale, bias, running estimates
+        e = launch_bn_train_stats(f32, y, g.M, g.C_out, gamma, beta, eps, momentum, running_mean,
+                                  running_var, batch_mean, batch_var, partial, scale, bias, s);
+    }
+    if (e != hipSuccess) return TG_ERR_HIP;
+    // 4. BatchNorm + SiLU on y in place
+    e = launch_bn_silu_apply(f32, y, scale, bias, y, (long long)g.M * g.C_out, g.C_out, s);
+    return e == hipSuccess ? TG_OK : TG_ERR_HIP;
 }
 
 }  // namespace
@@ -607,37 +668,11 @@ tg_status tg_conv_bn_silu_train_run(const tg_conv_bn_silu_plan* plan, const void
                                     float momentum, float* running_mean, float* running_var,
                                     float* batch_mean, float* batch_var, void* y, void* workspace,
                                     size_t workspace_bytes, void* stream) {
-    if (!plan || !x || !w || !gamma || !beta || !y) return TG_ERR_INVALID_ARGUMENT;
-    if ((running_mean == nullptr) != (running_var == nullptr)) return TG_ERR_INVALID_ARGUMENT;
-    if (!(eps >= 0.0f) || !(momentum >= 0.0f && momentum <= 1.0f)) return TG_ERR_INVALID_ARGUMENT;
-    const ConvGeom& g = plan->g;
-    if (g.M < 2) return TG_ERR_INVALID_ARGUMENT;  // batch statistics need two values per channel
-    if (plan->epi != EPI_FUSED || plan->g.out8) return TG_ERR_UNSUPPORTED;  // SiLU, y in dtype
-    const TrainWs L = train_ws(plan);
-    if (!workspace || workspace_bytes < L.total) return TG_ERR_WORKSPACE;
-    hipStream_t s = (hipStream_t)stream;
-    const bool f32 = plan->dtype == TG_F32;
-    int kernel = plan->kernel;
-    if (kernel != TG_KERNEL_SCALAR &&
-        !(aligned16(x) && aligned16(w) && aligned16(y) && aligned16(workspace))) {
-        if (plan->forced) return TG_ERR_ALIGNMENT;
-        kernel = TG_KERNEL_SCALAR;
-    }
-    char* ws = (char*)workspace;
-    void* t1 = ws + L.t1;
-    float* scale = (float*)(ws + L.scale);
-    float* bias = (float*)(ws + L.bias);
-    double* partial = (double*)(ws + L.partial);
-    // 1. conv -> t1 (identity epilogue: scale/bias are not read)
-    hipError_t e = launch_conv(plan, g, kernel, EPI_IDENTITY, x, w, scale, bias, t1, s);
-    if (e != hipSuccess) return TG_ERR_HIP;
-    // 2-3. batch statistics -> scale, bias, running estimates
-    e = launch_bn_train_stats(f32, t1, g.M, g.C_out, gamma, beta, eps, momentum, running_mean,
-                              running_var, batch_mean, batch_var, partial, scale, bias, s);
-    if (e != hipSuccess) return TG_ERR_HIP;
-    // 4. BatchNorm + SiLU: t1 -> y
-    e = launch_bn_silu_apply(f32, t1, scale, bias, y, (long long)g.M * g.C_out, g.C_out, s);
-    return e == hipSuccess ? TG_OK : TG_ERR_HIP;
+    tg_status st = train_check(plan, x, w, gamma, beta, eps, momentum, running_mean, running_var, y);
+    if (st != TG_OK) return st;
+    if (!workspace || workspace_bytes < train_ws(plan).total) return TG_ERR_WORKSPACE;
+    return train_core(plan, x, w, gamma, beta, eps, momentum, running_mean, running_var,
+                      batch_mean, batch_var, y, (char*)workspace, (hipStream_t)stream);
 }
 
 static tg_status transpose_entry(const void* src, void* dst, long long B, long long R,

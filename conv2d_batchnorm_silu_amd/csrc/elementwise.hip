@@ -61,12 +61,13 @@ __global__ __launch_bounds__(256) void bn_apply_f16x8(const half8_t* __restrict_
 // and the channel index is one 32-bit remainder per lane (element counts are
 // below 2^31). MODE 0: BatchNorm only (t2 = t1*scale + bias, unfused
 // baseline); MODE 1: BatchNorm + SiLU (split form).
+// in and out may be the same buffer (training mode applies BatchNorm+SiLU to
+// y in place): each lane reads its element before it writes it.
 template <int MODE>
-__global__ __launch_bounds__(256) void bn_c8_f16x8(const half8_t* __restrict__ in,
+__global__ __launch_bounds__(256) void bn_c8_f16x8(const half8_t* in,
                                                    const float4_t* __restrict__ scale4,
                                                    const float4_t* __restrict__ bias4,
-                                                   half8_t* __restrict__ out, unsigned nvec,
-                                                   unsigned cv) {
+                                                   half8_t* out, unsigned nvec, unsigned cv) {
     const unsigned j = blockIdx.x * 256u + threadIdx.x;
     if (j >= nvec) return;
     const unsigned c4 = (j % cv) * 2u;
@@ -108,12 +109,12 @@ __global__ __launch_bounds__(256) void silu_apply_f16x8(const half8_t* __restric
 // Fusion", the passage on when fusion does not pay): the conv kernel writes t1, then
 // this kernel applies the same fp32 epilogue as the fused kernels,
 // y = silu(t1 * scale[c] + bias[c]), reading t1 once and writing y once.
+// t1 and y may be the same buffer (training mode works in place).
 template <typename T>
-__global__ __launch_bounds__(256) void bn_silu_apply_scalar(const T* __restrict__ t1,
+__global__ __launch_bounds__(256) void bn_silu_apply_scalar(const T* t1,
                                                             const float* __restrict__ scale,
                                                             const float* __restrict__ bias,
-                                                            T* __restrict__ y, long long total,
-                                                            int C) {
+                                                            T* y, long long total, int C) {
     long long i = (long long)blockIdx.x * 256 + threadIdx.x;
     if (i >= total) return;
     int c = (int)(i % C);
@@ -122,11 +123,10 @@ __global__ __launch_bounds__(256) void bn_silu_apply_scalar(const T* __restrict_
     y[i] = from_f32<T>(epilogue<EPI_FUSED>(to_f32(t1[i]), s2, b2));
 }
 
-__global__ __launch_bounds__(256) void bn_silu_apply_f16x8(const half8_t* __restrict__ t1,
+__global__ __launch_bounds__(256) void bn_silu_apply_f16x8(const half8_t* t1,
                                                            const float* __restrict__ scale,
                                                            const float* __restrict__ bias,
-                                                           half8_t* __restrict__ y, long long nvec,
-                                                           int C) {
+                                                           half8_t* y, long long nvec, int C) {
     long long j = (long long)blockIdx.x * 256 + threadIdx.x;
     if (j >= nvec) return;
     half8_t v = t1[j];

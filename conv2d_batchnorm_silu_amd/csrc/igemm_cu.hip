@@ -26,6 +26,19 @@
 //     exact count that leaves the stores issued after it in flight.
 //   * Results go through a small wave-private LDS tile so that each store
 //     instruction writes whole 128-byte pieces of 8 pixel rows.
+//   * Training mode (STATS): the epilogue writes the conv output t1 and
+//     accumulates the per-channel batch statistics from the fp32
+//     accumulators on the way ("Kernel Fusion", cheatsheet page: a reduction
+//     next to elementwise work takes one or two passes), so t1 is written
+//     once and read once, by the BatchNorm+SiLU pass. Each lane sums
+//     d = acc - shift and d^2 over its pixels, with one shift per channel
+//     shared by the 16 lanes of a row (a value of the channel, so that the
+//     sum of squares does not cancel when the mean is far from 0); the
+//     row's sums become a (count, mean, sum of squared deviations) triple in
+//     fp64, and the waves of a slice combine theirs with the pairwise update
+//     of Chan, Golub and LeVeque (1979), all in a fixed order. Blocks are
+//     then assigned round-robin instead of pulled from the counter, so the
+//     result does not depend on scheduling.
 #include <stdlib.h>
 
 #include "tg_device.hpp"
@@ -38,6 +51,7 @@ constexpr int kCuMinLdsBytes = 81 * 1024;   // more than half of a CU's LDS
 constexpr int kCuMaxLdsBytes = 160 * 1024 - 64;  // 160 KB minus the static counters
 constexpr int kCuCW = 64;                  // channels per wavefront slice
 constexpr int kCuTrow = kCuCW + 8;         // padded tile row (halves)
+constexpr int kCuStatsThreads = 768;       // at most 12 waves with the statistics registers
 
 template <int N>
 __device__ __forceinline__ void cu_wait_vmcnt() {
@@ -99,11 +113,35 @@ __host__ __device__ inline CuLayout cu_layout(int C_out, int nwaves, int pd) {
     return L;
 }
 
-template <int EPI, bool NT, int PD, bool OUT8, bool RES>
-__global__ __launch_bounds__(1024) void conv2d_bn_silu_igemm_cu(
+// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), left in every
+// lane of the row: pairs, quads (quad permutes), then the other quad of the
+// half row (half mirror) and the other half (mirror). Each step adds two
+// values in either order, so all 16 lanes end with the same bits.
+__device__ __forceinline__ float cu_row_sum16(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)); // row_half_mirror
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)); // row_mirror
+    return v;
+}
+
+// (n, mean, M2) of the union of two disjoint sets; (0, 0, 0) is the empty set.
+__device__ __forceinline__ void cu_chan_merge(double& n, double& mean, double& m2, double nb,
+                                              double meanb, double m2b) {
+    const double nt = n + nb;
+    if (nt == 0.0) return;
+    const double d = meanb - mean;
+    const double f = nb / nt;
+    mean = mean + d * f;
+    m2 = m2 + m2b + d * d * n * f;
+    n = nt;
+}
+
+template <int EPI, bool NT, int PD, bool OUT8, bool RES, bool STATS>
+__global__ __launch_bounds__(STATS ? kCuStatsThreads : 1024) void conv2d_bn_silu_igemm_cu(
     const f16* __restrict__ x, const f16* __restrict__ w, const float* __restrict__ scale,
     const float* __restrict__ bias, f16* __restrict__ y, int M, int C_out, int nwaves,
-    const f16* __restrict__ res) {
+    const f16* __restrict__ res, double* __restrict__ stats) {
     constexpr int NF = 4, KS = 2;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     __shared__ int next_blk[4];
@@ -130,10 +168,11 @@ __global__ __launch_bounds__(1024) void conv2d_bn_silu_igemm_cu(
         const int piece = (lane & 7) ^ cu_wswz(row);
         cu_dma16(wrs, (unsigned)(row * 128 + piece * 16), lbase + L.w_off + h * 1024);
     }
-    // Scale and bias: up to 256 floats each, one instruction each.
-    if (wave == 0)
+    // Scale and bias: up to 256 floats each, one instruction each (none for
+    // the identity epilogue, which does not read them; they may be NULL).
+    if (EPI != EPI_IDENTITY && wave == 0)
         cu_dma16(cu_rsrc(scale, (unsigned)C_out * 4u), lane * 16u, lbase + L.s_off);
-    if (wave == (nwaves > 1 ? 1 : 0))
+    if (EPI != EPI_IDENTITY && wave == (nwaves > 1 ? 1 : 0))
         cu_dma16(cu_rsrc(bias, (unsigned)C_out * 4u), lane * 16u, lbase + L.b_off);
 
     // Input block b: pixels 16b..16b+15, 128 bytes each. Instruction h moves
@@ -186,12 +225,26 @@ __global__ __launch_bounds__(1024) void conv2d_bn_silu_igemm_cu(
     f16* tl = (f16*)(lds + L.t_off) + wave * 16 * kCuTrow;
     const int ocs = (lane % 8) * 8;  // channel within the slice, store phase
     const int orow = lane / 8;       // first tile row, store phase
+    // Statistics: lane (lr, lg) sees pixel lr of each of its blocks and
+    // channels c0 + 32*(f/2) + 8*lg + 4*(f%2) + e of accumulator f, element e.
+    float st_shift[NF][4], st_s1[NF][4], st_s2[NF][4];
+    int st_n = 0;
+    if (STATS) {
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) st_shift[f][e] = st_s1[f][e] = st_s2[f][e] = 0.0f;
+    }
     for (int it = 0;; ++it) {
         const int blk = q[0];
         if (blk >= b_end) break;
         int nb = 0;
-        if (lane == 0) nb = atomicAdd(&next_blk[grp], 1);
-        nb = __builtin_amdgcn_readfirstlane(nb);
+        if (STATS) {
+            nb = q[PD - 1] + R;  // round-robin: rank rnk takes b_begin + rnk + R*i
+        } else {
+            if (lane == 0) nb = atomicAdd(&next_blk[grp], 1);
+            nb = __builtin_amdgcn_readfirstlane(nb);
+        }
         // Exact wait for block blk's two loads. Each iteration issues two
         // loads (after its MFMAs) and two stores, so they are followed by
         // 2*(PD-1-it) + 4*it operations while it < PD and 4*PD-2 afterwards.
@@ -212,6 +265,40 @@ __global__ __launch_bounds__(1024) void conv2d_bn_silu_igemm_cu(
 #pragma unroll
             for (int f = 0; f < NF; ++f)
                 acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[f][s], xc[s], acc[f], 0, 0, 0);
+        if (STATS) {
+            // One shift per channel for the 16 lanes of a row: the value of
+            // the row's lane 0 in the first block (pixel 0 of a block is
+            // always inside the image), so the lanes' sums add directly.
+            // Pixels past M add nothing.
+            if (it == 0) {
+#pragma unroll
+                for (int f = 0; f < NF; ++f)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) st_shift[f][e] = __shfl(acc[f][e], lane & 48);
+            }
+            if (blk * 16 + 16 <= M) {  // whole block (wave-uniform)
+                ++st_n;
+#pragma unroll
+                for (int f = 0; f < NF; ++f)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float d = acc[f][e] - st_shift[f][e];
+                        st_s1[f][e] += d;
+                        st_s2[f][e] = __builtin_fmaf(d, d, st_s2[f][e]);
+                    }
+            } else {  // the last block of the image batch
+                const bool valid = blk * 16 + lr < M;
+                st_n += valid ? 1 : 0;
+#pragma unroll
+                for (int f = 0; f < NF; ++f)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float d = valid ? acc[f][e] - st_shift[f][e] : 0.0f;
+                        st_s1[f][e] += d;
+                        st_s2[f][e] = __builtin_fmaf(d, d, st_s2[f][e]);
+                    }
+            }
+        }
         fetch(nb, buf);  // the fragment reads above have completed (the MFMAs used them)
 #pragma unroll
         for (int d = 0; d + 1 < PD; ++d) q[d] = q[d + 1];
@@ -238,20 +325,77 @@ __global__ __launch_bounds__(1024) void conv2d_bn_silu_igemm_cu(
         }
         cu_wave_sync();
     }
+    if constexpr (STATS) {
+        // The 16 lanes of a row share their shifts: add their counts and
+        // sums across the row (every lane ends with the row's totals), then
+        // form the row's (count, mean, squared deviations) in fp64.
+        const float nrow = cu_row_sum16((float)st_n);  // at most 16 x blocks: exact
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                st_s1[f][e] = cu_row_sum16(st_s1[f][e]);
+                st_s2[f][e] = cu_row_sum16(st_s2[f][e]);
+            }
+        double sn[NF][4], smean[NF][4], sm2[NF][4];
+        const double n0 = (double)nrow;
+        const double inv_n = nrow > 0.0f ? 1.0 / n0 : 0.0;
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const double s1 = st_s1[f][e], s2 = st_s2[f][e];
+                sn[f][e] = n0;
+                smean[f][e] = nrow > 0.0f ? (double)st_shift[f][e] + s1 * inv_n : 0.0;
+                const double m2 = s2 - s1 * s1 * inv_n;
+                sm2[f][e] = m2 > 0.0 ? m2 : 0.0;
+            }
+        // The wave's triples (64 channels) go to its own input-buffer space
+        // once its last (zero-filled) prefetches have landed; then rank 0 of
+        // each slice merges the ranks in order and writes the workgroup's
+        // triples: stats[(blockIdx.x * C_out + c) * 3 + {0, 1, 2}].
+        cu_wait_vmcnt<0>();
+        double* wt = (double*)(lds + L.x_off + (unsigned)wave * PD * 2048u);
+        if (lr == 0) {
+#pragma unroll
+            for (int f = 0; f < NF; ++f)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int cl = 32 * (f >> 1) + 8 * lg + 4 * (f & 1) + e;
+                    wt[cl * 3 + 0] = sn[f][e];
+                    wt[cl * 3 + 1] = smean[f][e];
+                    wt[cl * 3 + 2] = sm2[f][e];
+                }
+        }
+        __syncthreads();
+        if (rnk == 0) {
+            double n = 0.0, mean = 0.0, m2 = 0.0;
+            for (int r = 0; r < R; ++r) {
+                const double* src =
+                    (const double*)(lds + L.x_off + (unsigned)(grp + r * ngroups) * PD * 2048u);
+                cu_chan_merge(n, mean, m2, src[lane * 3], src[lane * 3 + 1], src[lane * 3 + 2]);
+            }
+            double* dst = stats + ((size_t)blockIdx.x * C_out + c0 + lane) * 3;
+            dst[0] = n;
+            dst[1] = mean;
+            dst[2] = m2;
+        }
+    }
 }
 
-template <int EPI, bool NT, int PD, bool OUT8, bool RES>
+template <int EPI, bool NT, int PD, bool OUT8, bool RES, bool STATS = false>
 hipError_t launch_cu_t(const ConvGeom& g, int grid, int nwaves, const void* x, const void* w,
-                       const float* scale, const float* bias, void* y, hipStream_t s) {
+                       const float* scale, const float* bias, void* y, hipStream_t s,
+                       double* stats = nullptr) {
     const CuLayout L = cu_layout(g.C_out, nwaves, PD);
     if (L.bytes > kCuMaxLdsBytes) return hipErrorInvalidValue;
     const int lds = L.bytes > kCuMinLdsBytes ? L.bytes : kCuMinLdsBytes;
     hipError_t e = ensure_dynamic_lds(
-        (const void*)conv2d_bn_silu_igemm_cu<EPI, NT, PD, OUT8, RES>, (size_t)lds);
+        (const void*)conv2d_bn_silu_igemm_cu<EPI, NT, PD, OUT8, RES, STATS>, (size_t)lds);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((conv2d_bn_silu_igemm_cu<EPI, NT, PD, OUT8, RES>), dim3(grid), dim3(64 * nwaves), lds,
-                       s, (const f16*)x, (const f16*)w, scale, bias, (f16*)y, g.M, g.C_out, nwaves,
-                       (const f16*)g.res);
+    hipLaunchKernelGGL((conv2d_bn_silu_igemm_cu<EPI, NT, PD, OUT8, RES, STATS>), dim3(grid),
+                       dim3(64 * nwaves), lds, s, (const f16*)x, (const f16*)w, scale, bias,
+                       (f16*)y, g.M, g.C_out, nwaves, (const f16*)g.res, stats);
     return hipGetLastError();
 }
 
@@ -297,6 +441,28 @@ hipError_t launch_igemm_cu(const ConvGeom& g, int nwaves, int pd, bool nt, int e
     return hipErrorInvalidValue;
 #undef TG_CU_PD
 #undef TG_CU
+}
+
+int igemm_cu_stats_grid(const ConvGeom& g) {
+    const int nblocks = (g.M + 15) / 16;
+    return nblocks < 256 ? nblocks : 256;
+}
+
+hipError_t launch_igemm_cu_stats(const ConvGeom& g, int nwaves, int pd, const void* x,
+                                 const void* w, void* t1, double* stats, hipStream_t s) {
+    if (!igemm_cu_serves(g) || g.out8 || g.res || nwaves < 1 || nwaves > kCuStatsThreads / 64 ||
+        nwaves % (g.C_out / kCuCW) != 0)
+        return hipErrorInvalidValue;
+    const int grid = igemm_cu_stats_grid(g);
+    if (grid == 0) return hipSuccess;
+    if (pd <= 1)
+        return launch_cu_t<EPI_IDENTITY, false, 1, false, false, true>(g, grid, nwaves, x, w,
+                                                                      nullptr, nullptr, t1, s, stats);
+    if (pd == 2)
+        return launch_cu_t<EPI_IDENTITY, false, 2, false, false, true>(g, grid, nwaves, x, w,
+                                                                      nullptr, nullptr, t1, s, stats);
+    return launch_cu_t<EPI_IDENTITY, false, 3, false, false, true>(g, grid, nwaves, x, w, nullptr,
+                                                                  nullptr, t1, s, stats);
 }
 
 }  // namespace tg

@@ -7,8 +7,13 @@
 // passes, but a value that needs results computed by other blocks cannot be
 // fused across without a kernel boundary, since there is no grid-wide
 // barrier. So the path is:
+//   0. the 1x1 layer's kernel (igemm_cu.hip) forms the statistics in its own
+//      epilogue from the fp32 accumulators while it writes t1 into y, as
+//      (count, mean, sum of squared deviations) per workgroup, and
+//      bn_train_finalize_chan combines them (step 3); t1 is then written
+//      once and read once. The other kernels take steps 1-4:
 //   1. the conv kernel with an identity epilogue writes t1 (y's shape and
-//      dtype) -- the same kernels as the fused path (api.hip);
+//      dtype) into y -- the same kernels as the fused path (api.hip);
 //   2. bn_stats_partial: per block of rows, per channel, the sum and the sum
 //      of squares of (t1 - shift_c) in fp64, with shift_c = t1[0][c] (one
 //      value of the channel: it keeps the sum of squares from cancelling when
@@ -21,7 +26,7 @@
 //      scale and one bias (as tg_bn_fold does for running statistics), and
 //      moves the running estimates by `momentum` (unbiased variance);
 //   4. the split form's BatchNorm+SiLU streaming kernel (elementwise.hip)
-//      applies scale and bias and SiLU: t1 -> y.
+//      applies scale and bias and SiLU to y in place.
 // The batch-normalising transform is the one of Ioffe and Szegedy (2015):
 // normalise with the batch mean and the biased batch variance.
 #include "tg_device.hpp"
@@ -125,6 +130,27 @@ __global__ __launch_bounds__(kVecThreads) void bn_stats_partial_v8(const half8_t
     }
 }
 
+// Folds channel c's batch mean and biased variance with gamma, beta and eps
+// into one scale and one bias (as tg_bn_fold does for running statistics),
+// stores the batch values and moves the running estimates by `momentum`
+// (unbiased variance var*M/(M-1)).
+__device__ __forceinline__ void bn_train_outputs(int c, int M, double mean, double var,
+                                                 const float* gamma, const float* beta, float eps,
+                                                 float momentum, float* running_mean,
+                                                 float* running_var, float* batch_mean,
+                                                 float* batch_var, float* scale, float* bias) {
+    const double sc = (double)gamma[c] / sqrt(var + (double)eps);
+    scale[c] = (float)sc;
+    bias[c] = (float)((double)beta[c] - mean * sc);
+    if (batch_mean) batch_mean[c] = (float)mean;
+    if (batch_var) batch_var[c] = (float)var;
+    if (running_mean) {
+        const double m = momentum;
+        running_mean[c] = (float)((1.0 - m) * running_mean[c] + m * mean);
+        running_var[c] = (float)((1.0 - m) * running_var[c] + m * var * ((double)M / (M - 1)));
+    }
+}
+
 // One block of 1024 threads per 16 channels: thread t takes channel t % 16
 // and adds every 64th row block's partials from block t / 16 on (all its loads
 // in flight at once for up to 512 row blocks); the 64 sums of a channel are
@@ -176,20 +202,97 @@ __global__ __launch_bounds__(kFinChans * kFinPhases) void bn_train_finalize(
     const double md = s1 / M;                        // mean of (t1 - shift)
     double var = s2 / M - md * md;                   // biased batch variance
     if (var < 0.0) var = 0.0;                        // rounding of an exactly constant channel
-    const double mean = shift + md;
-    const double sc = (double)gamma[c] / sqrt(var + (double)eps);
-    scale[c] = (float)sc;
-    bias[c] = (float)((double)beta[c] - mean * sc);
-    if (batch_mean) batch_mean[c] = (float)mean;
-    if (batch_var) batch_var[c] = (float)var;
-    if (running_mean) {
-        const double m = momentum;
-        running_mean[c] = (float)((1.0 - m) * running_mean[c] + m * mean);
-        running_var[c] = (float)((1.0 - m) * running_var[c] + m * var * ((double)M / (M - 1)));
+    bn_train_outputs(c, M, shift + md, var, gamma, beta, eps, momentum, running_mean, running_var,
+                     batch_mean, batch_var, scale, bias);
+}
+
+// Triples from the 1x1 kernel's statistics epilogue: stats[(b*C + c)*3] =
+// (count n_b, mean m_b, sum of squared deviations q_b) of workgroup b; four
+// channels per workgroup, so the loads spread over C/4 compute units. Two
+// fixed-order passes (threads (ph, cl) take b = ph, ph + kFinPhases, ...;
+// phase 0 then adds the phases in order): the mean from sum(n_b*m_b)/M, then
+// the squared deviations as sum(q_b + n_b*(m_b - mean)^2), the exact
+// decomposition of the total about the mean. No term cancels and the result
+// does not depend on scheduling.
+constexpr int kChanChans = 4;   // channels per workgroup of the triple finalize
+constexpr int kChanHeld = 8;    // triples a thread keeps in registers between the passes
+__global__ __launch_bounds__(kChanChans * kFinPhases) void bn_train_finalize_chan(
+    const double* __restrict__ stats, int G, int M, int C, const float* __restrict__ gamma,
+    const float* __restrict__ beta, float eps, float momentum, float* __restrict__ running_mean,
+    float* __restrict__ running_var, float* __restrict__ batch_mean,
+    float* __restrict__ batch_var, float* __restrict__ scale, float* __restrict__ bias) {
+    __shared__ double red[kFinPhases][kChanChans];
+    __shared__ double mean_s[kChanChans];
+    const int cl = threadIdx.x % kChanChans, ph = threadIdx.x / kChanChans;
+    const int c = blockIdx.x * kChanChans + cl;
+    // Pass 1: sum(n_b*m_b) over this thread's triples b = ph + kFinPhases*i;
+    // the first kChanHeld stay in registers for pass 2.
+    double hn[kChanHeld], hm[kChanHeld], hq[kChanHeld];
+    double a = 0.0;
+#pragma unroll
+    for (int i = 0; i < kChanHeld; ++i) {
+        const int b = ph + i * kFinPhases;
+        hn[i] = hm[i] = hq[i] = 0.0;
+        if (c < C && b < G) {
+            const double* t = stats + ((size_t)b * C + c) * 3;
+            hn[i] = t[0];
+            hm[i] = t[1];
+            hq[i] = t[2];
+        }
     }
+#pragma unroll
+    for (int i = 0; i < kChanHeld; ++i) a += hn[i] * hm[i];
+    if (c < C)
+        for (int b = ph + kChanHeld * kFinPhases; b < G; b += kFinPhases) {
+            const double* t = stats + ((size_t)b * C + c) * 3;
+            a += t[0] * t[1];
+        }
+    red[ph][cl] = a;
+    __syncthreads();
+    if (ph == 0) {
+        double s = 0.0;
+        for (int k = 0; k < kFinPhases; ++k) s += red[k][cl];
+        mean_s[cl] = s / M;
+    }
+    __syncthreads();
+    const double mean = mean_s[cl];
+    // Pass 2: sum(q_b + n_b*(m_b - mean)^2).
+    a = 0.0;
+#pragma unroll
+    for (int i = 0; i < kChanHeld; ++i) {
+        const double d = hm[i] - mean;
+        a += hq[i] + hn[i] * d * d;
+    }
+    if (c < C)
+        for (int b = ph + kChanHeld * kFinPhases; b < G; b += kFinPhases) {
+            const double* t = stats + ((size_t)b * C + c) * 3;
+            const double d = t[1] - mean;
+            a += t[2] + t[0] * d * d;
+        }
+    __syncthreads();
+    red[ph][cl] = a;
+    __syncthreads();
+    if (ph != 0 || c >= C) return;
+    double q = 0.0;
+    for (int k = 0; k < kFinPhases; ++k) q += red[k][cl];
+    bn_train_outputs(c, M, mean, q / M, gamma, beta, eps, momentum, running_mean, running_var,
+                     batch_mean, batch_var, scale, bias);
 }
 
 }  // namespace
+
+size_t bn_train_chan_bytes(int G, int C) { return (size_t)G * C * 3 * sizeof(double); }
+
+hipError_t launch_bn_train_finalize_chan(const double* stats, int G, int M, int C,
+                                         const float* gamma, const float* beta, float eps,
+                                         float momentum, float* running_mean, float* running_var,
+                                         float* batch_mean, float* batch_var, float* scale,
+                                         float* bias, hipStream_t s) {
+    hipLaunchKernelGGL(bn_train_finalize_chan, dim3((C + kChanChans - 1) / kChanChans),
+                       dim3(kChanChans * kFinPhases), 0, s, stats, G, M, C, gamma, beta, eps,
+                       momentum, running_mean, running_var, batch_mean, batch_var, scale, bias);
+    return hipGetLastError();
+}
 
 void bn_train_grid(int M, int* R, int* GX) {
     // About 512 row blocks (two per compute unit), at least 64 rows each.

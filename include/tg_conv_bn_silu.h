@@ -132,16 +132,20 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan *plan, const void *x, c
  * (cheatsheet page, passages on reductions and on synchronization
  * boundaries) says cannot be fused without a kernel boundary, so the call
  * runs in passes on `stream`: the plan's conv kernel writes the conv output
- * t1 into the workspace, a reduction forms per-channel sums in fp64 (in a
- * fixed order: results are deterministic), a small kernel folds them into one
- * scale and one bias, and a streaming kernel applies BatchNorm and SiLU
- * (t1 -> y). gamma, beta: device fp32 [C_out]. running_mean/running_var:
+ * t1 into y; the 1x1 kernel forms the per-channel statistics in its own
+ * epilogue from the fp32 accumulators (count, mean and squared deviations
+ * per workgroup, fp64), the other kernels are followed by a reduction over
+ * t1 (fp64 sums); a small kernel combines the partials in a fixed order
+ * (results are deterministic) and folds them into one scale and one bias;
+ * a streaming kernel applies BatchNorm and SiLU to y in place. t1 is
+ * written once and read once. gamma, beta: device fp32 [C_out]. running_mean/running_var:
  * device fp32 [C_out] updated in place as r = (1-momentum)*r +
  * momentum*batch_value, with the unbiased variance var_k*M/(M-1); both NULL
  * for no update. batch_mean/batch_var: device fp32 [C_out] outputs (the
- * biased variance), each may be NULL. workspace: at least the size from
- * tg_conv_bn_silu_train_workspace, 16-byte aligned for the vector kernels,
- * not aliasing any other argument. Errors: TG_ERR_INVALID_ARGUMENT for a
+ * biased variance), each may be NULL. y must not alias x. workspace (the
+ * per-channel scale and bias and the statistics partials, a few MB at
+ * most): at least the size from tg_conv_bn_silu_train_workspace, 16-byte
+ * aligned for the vector kernels, not aliasing any other argument. Errors: TG_ERR_INVALID_ARGUMENT for a
  * NULL plan/x/w/gamma/beta/y, only one of running_mean/running_var given,
  * eps < 0, momentum outside [0, 1], or M < 2; TG_ERR_UNSUPPORTED for a plan
  * whose activation is not SiLU; TG_ERR_WORKSPACE;

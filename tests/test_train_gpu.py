@@ -9,9 +9,10 @@ each normalised value carries t1's rounding (2^-11 relative of |t1|) scaled by
 gamma/sigma, plus y's own rounding; with the seeded data (|t1|/sigma below
 about 6, gamma <= 1.5) that is below 5e-3 * max(1, |oracle|). The batch mean
 and (biased) variance and the updated running estimates are fp32 results of
-fp64 sums over rounded t1: within 1e-3 * max(1, |oracle|) for fp16 and 1e-5
-for fp32. The reduction adds its partial sums in a fixed order, so two calls
-give bit-identical results.
+fp64 sums over rounded t1 (over the fp32 accumulators for the 1x1 kernel,
+which forms them in its epilogue): within 1e-3 * max(1, |oracle|) for fp16
+and 1e-5 for fp32. The reductions combine their partials in a fixed order, so
+two calls give bit-identical results.
 """
 from __future__ import annotations
 
@@ -118,12 +119,53 @@ def test_train_constant_channel():
     assert float(_scaled(got, ref["y"]).max()) <= Y_TIGHT["f16"]
 
 
-def test_train_deterministic():
-    wl = WORKLOADS["conv3x3_c128_k128"].scaled(N=4)
+@pytest.mark.parametrize("name", ["conv3x3_c128_k128", "conv1x1_c64_k256"])
+def test_train_deterministic(name):
+    """Two calls give identical y and batch statistics: the row-block sums
+    (3x3) and the 1x1 kernel's in-epilogue triples are merged in a fixed
+    order whatever the scheduling."""
+    wl = WORKLOADS[name].scaled(N=4)
     d = make_inputs(wl)
     outs = [run_train(wl, d=d)[1] for _ in range(2)]
     for a, b in zip(outs[0][:3], outs[1][:3]):
         assert torch.equal(a, b)
+
+
+def test_train_statistics_large_offset():
+    """Inputs around 30 with a spread of 0.6 make every channel's conv output
+    mean some 50 standard deviations away from 0, where
+    sum(x^2) - sum(x)^2/M would cancel. The 1x1 kernel forms its statistics
+    from the fp32 accumulators (shifted, merged as count/mean/squared
+    deviations): they match the oracle's exact batch statistics. The other
+    kernels read the stored fp16 t1, whose rounding (2^-11 of |t1|, about a
+    twentieth of sigma here) moves the variance itself: their statistics match
+    those of the oracle's conv output rounded to fp16, up to the few stored
+    values that sit one fp16 step (0.03 here) from that rounding because the
+    fp32 sum ends on the other side of a rounding boundary: with 128 outputs
+    per channel those move the variance by a few 1e-4. y carries t1's
+    rounding too, so only the statistics are compared."""
+    for wl, exact in ((Workload("train_offset_1x1", 77, 4, 14, 14, 64, 128, 1, 1, 1, 0, "f16",
+                                ("uniform", 29.0, 31.0)), True),
+                      (Workload("train_offset_3x3", 78, 2, 10, 10, 64, 64, 3, 3, 1, 0, "f16",
+                                ("uniform", 29.0, 31.0)), False)):
+        d, (y, bm, bv, rm, rv), ref = run_train(wl)
+        assert not np.isnan(y.float().cpu().numpy()).any()
+        assert np.median(np.abs(ref["mean"]) / np.sqrt(ref["var"])) > 10.0
+        if exact:
+            mean, var = ref["mean"], ref["var"]
+        else:
+            t = oracle.conv2d(d["x"], d["w"], wl.stride, wl.pad)
+            flat = t.astype(np.float16).astype(np.float64).reshape(-1, wl.C_out)
+            mean = flat.mean(axis=0)
+            var = ((flat - mean) ** 2).mean(axis=0)
+        e_mean = float(np.abs(bm.cpu().numpy() - mean).max() / np.abs(mean).max())
+        e_var = float((np.abs(bv.cpu().numpy() - var) / var).max())
+        note("%s: mean error %.3g (relative to max |mean|), variance relative error %.3g" % (
+            wl.name, e_mean, e_var))
+        if exact:
+            assert e_mean <= 1e-6 and e_var <= 1e-5, (e_mean, e_var)
+        else:
+            assert e_mean <= 1e-5 and e_var <= 2e-3, (e_mean, e_var)
 
 
 def test_train_no_running_update_and_errors():
