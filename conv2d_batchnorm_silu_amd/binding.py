@@ -120,6 +120,8 @@ def library():
         f = ctypes.c_float
         lib.tg_conv_bn_silu_train_run.argtypes = [vp] * 5 + [f, f] + [vp] * 5 + [vp, sz, vp]
         lib.tg_conv_bn_silu_train_run.restype = i
+        lib.tg_conv_bn_silu_train_run_static.argtypes = [vp] * 5 + [f, f] + [vp] * 6
+        lib.tg_conv_bn_silu_train_run_static.restype = i
         lib.tg_conv_bn_silu_train_workspace.argtypes = [vp, ctypes.POINTER(sz)]
         lib.tg_conv_bn_silu_train_workspace.restype = i
         for name in ("tg_filter_oihw_to_ohwi", "tg_nchw_to_nhwc", "tg_nhwc_to_nchw"):
@@ -403,6 +405,41 @@ class ConvBnSilu:
             _stream_handle(stream))
         _check(st, "tg_conv_bn_silu_train_run")
         return out, bm, bv
+
+    def run_train_static(self, x, w, gamma, beta, eps=1e-5, momentum=0.1, running_mean=None,
+                         running_var=None, out=None, batch_mean=None, batch_var=None,
+                         stream=None):
+        """run_train through tg_conv_bn_silu_train_run_static: the library's
+        static device array serves as workspace, so with out, batch_mean and
+        batch_var given nothing is allocated on this path."""
+        import torch
+        N, H, W, C_in, C_out, kh, kw, _, _ = self.shape
+        td = _torch_dtype(self.dtype)
+        self._check_tensor(x, (N, H, W, C_in), td, "x")
+        self._check_tensor(w, (C_out, kh, kw, C_in), td, "w")
+        for t, name in ((gamma, "gamma"), (beta, "beta")):
+            self._check_tensor(t, (C_out,), torch.float32, name)
+        if (running_mean is None) != (running_var is None):
+            raise ValueError("give both running_mean and running_var, or neither")
+        for t, name in ((running_mean, "running_mean"), (running_var, "running_var")):
+            if t is not None:
+                self._check_tensor(t, (C_out,), torch.float32, name)
+        if out is None:
+            out = torch.empty(self.y_shape, dtype=td, device=x.device)
+        self._check_tensor(out, self.y_shape, td, "out")
+        if batch_mean is None:
+            batch_mean = torch.empty(C_out, dtype=torch.float32, device=x.device)
+        if batch_var is None:
+            batch_var = torch.empty(C_out, dtype=torch.float32, device=x.device)
+        self._check_tensor(batch_mean, (C_out,), torch.float32, "batch_mean")
+        self._check_tensor(batch_var, (C_out,), torch.float32, "batch_var")
+        ptr = lambda t: 0 if t is None else t.data_ptr()
+        st = self._lib.tg_conv_bn_silu_train_run_static(
+            self._h, x.data_ptr(), w.data_ptr(), gamma.data_ptr(), beta.data_ptr(), float(eps),
+            float(momentum), ptr(running_mean), ptr(running_var), batch_mean.data_ptr(),
+            batch_var.data_ptr(), out.data_ptr(), _stream_handle(stream))
+        _check(st, "tg_conv_bn_silu_train_run_static")
+        return out, batch_mean, batch_var
 
     def close(self):
         if getattr(self, "_h", None):

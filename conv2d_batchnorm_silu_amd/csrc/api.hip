@@ -474,6 +474,32 @@ hipError_t launch_conv(const tg_conv_bn_silu_plan* plan, const ConvGeom& g, int 
     return e;
 }
 
+// Device memory for tg_conv_bn_silu_train_run_static: one copy of this array
+// per GPU, at its own address on each. In host code `scratch` names a
+// host-side stand-in, never the device memory: kernels and copies take the
+// address from static_scratch().
+static __device__ __align__(256) unsigned char scratch[TG_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // per device; written once under g_scratch_mu
+
+// The array's device address on the current device, looked up (under the
+// lock) at the first call there.
+tg_status static_scratch(void** out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return TG_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return TG_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TG_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return TG_OK;
+}
+
 // Training mode keeps t1 in y (the BatchNorm+SiLU pass then works on y in
 // place). Workspace: [scale fp32 [C]][bias fp32 [C]][statistics partials:
 // fp64 row-block sums, or the 1x1 kernel's per-workgroup triples], each
@@ -661,6 +687,21 @@ tg_status tg_conv_bn_silu_train_workspace(const tg_conv_bn_silu_plan* plan, size
     if (!plan || !bytes) return TG_ERR_INVALID_ARGUMENT;
     *bytes = train_ws(plan).total;
     return TG_OK;
+}
+
+tg_status tg_conv_bn_silu_train_run_static(const tg_conv_bn_silu_plan* plan, const void* x,
+                                           const void* w, const float* gamma, const float* beta,
+                                           float eps, float momentum, float* running_mean,
+                                           float* running_var, float* batch_mean,
+                                           float* batch_var, void* y, void* stream) {
+    tg_status st = train_check(plan, x, w, gamma, beta, eps, momentum, running_mean, running_var, y);
+    if (st != TG_OK) return st;
+    if (train_ws(plan).total > (size_t)TG_STATIC_SCRATCH_BYTES) return TG_ERR_UNSUPPORTED;
+    void* ws = nullptr;
+    st = static_scratch(&ws);
+    if (st != TG_OK) return st;
+    return train_core(plan, x, w, gamma, beta, eps, momentum, running_mean, running_var,
+                      batch_mean, batch_var, y, (char*)ws, (hipStream_t)stream);
 }
 
 tg_status tg_conv_bn_silu_train_run(const tg_conv_bn_silu_plan* plan, const void* x, const void* w,

@@ -161,6 +161,28 @@ tg_status tg_conv_bn_silu_train_run(const tg_conv_bn_silu_plan *plan, const void
  * TG_ERR_INVALID_ARGUMENT for NULL arguments. */
 tg_status tg_conv_bn_silu_train_workspace(const tg_conv_bn_silu_plan *plan, size_t *bytes);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc:
+ * tg_conv_bn_silu_train_run with its workspace (scale, bias and statistics
+ * partials) in a static device array of TG_STATIC_SCRATCH_BYTES that the
+ * library holds on each GPU it runs on, until the process ends, instead of a
+ * caller's buffer. The call allocates nothing: at its first call on a device
+ * (the current device, which must be the stream's) it looks up the array's
+ * address there. Every byte of the array a call reads it has written earlier
+ * in the same call, so nothing needs clearing; calls that overlap on one GPU
+ * (two streams, two host threads) share the array and race -- serialise
+ * them. Errors: TG_ERR_UNSUPPORTED when the plan's training workspace
+ * (tg_conv_bn_silu_train_workspace) exceeds TG_STATIC_SCRATCH_BYTES, checked
+ * before anything touches the GPU; TG_ERR_HIP when the array's address
+ * cannot be taken or a launch fails; the other arguments and errors as for
+ * tg_conv_bn_silu_train_run. */
+#define TG_STATIC_SCRATCH_BYTES (4u << 20)
+tg_status tg_conv_bn_silu_train_run_static(const tg_conv_bn_silu_plan *plan, const void *x,
+                                           const void *w, const float *gamma, const float *beta,
+                                           float eps, float momentum, float *running_mean,
+                                           float *running_var, float *batch_mean,
+                                           float *batch_var, void *y, void *stream);
+
 /* Activation in the epilogue. The fused kernels apply, after the folded
  * BatchNorm v = acc*bn_scale[k] + bn_bias[k], one of: SiLU v*sigmoid(v)
  * (the default of every other create), ReLU max(v, 0), GELU in its exact

@@ -360,3 +360,21 @@ def test_library_reads_no_environment(lib, monkeypatch):
     assert st == OK and _describe(lib, h) == base
     lib.tg_conv_bn_silu_destroy(h)
     lib.tg_conv_bn_silu_destroy(h0)
+
+
+def test_static_train_entry_rejects_oversized_plan_on_host(lib):
+    """tg_conv_bn_silu_train_run_static checks the plan's training workspace
+    against the static array before touching the GPU: 1024 channels over 512
+    row blocks need 8 MiB of partials, above TG_STATIC_SCRATCH_BYTES (4 MiB);
+    argument errors come first, as for train_run."""
+    st, h = _create(lib, 64, 56, 56, 64, 1024, 1, 1, 1, 0)
+    assert st == OK
+    ws = ctypes.c_size_t()
+    assert lib.tg_conv_bn_silu_train_workspace(h, ctypes.byref(ws)) == OK
+    assert ws.value > 4 << 20
+    a = 1 << 20  # fake addresses: never dereferenced on these paths
+    f = lib.tg_conv_bn_silu_train_run_static
+    assert f(h, a, a, a, a, 1e-5, 0.1, None, None, None, None, a, None) == UNSUP
+    assert f(h, a, a, None, a, 1e-5, 0.1, None, None, None, None, a, None) == INVAL
+    assert f(None, a, a, a, a, 1e-5, 0.1, None, None, None, None, a, None) == INVAL
+    lib.tg_conv_bn_silu_destroy(h)
