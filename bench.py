@@ -385,6 +385,11 @@ def bench_workload(torch, wl, steps, warmup, with_unfused=True, plan_kind="auto"
            "us": round(ms * 1e3, 2), "tflops": round(tfl, 2), "gbs": round(gbs, 1),
            "bound": bound, "ai": round(ai, 1), "frac": round(frac, 4), "sets": sets.n,
            "parity": par}
+    # Counter-measured HBM bytes of this kernel (committed rocprofv3 runs of
+    # the same sources), next to the algorithmic bytes.
+    hbm = load_traffic(wl.name)
+    if hbm is not None:
+        row.update({"hbm_traffic": hbm, "hbm_traffic_excess": round(hbm / fb - 1.0, 4)})
     if with_unfused:
         up = B.ConvBnSilu(wl.N, wl.H, wl.W, wl.C_in, wl.C_out, wl.kh, wl.kw, wl.stride, wl.pad,
                           wl.dtype, "unfused")

@@ -132,7 +132,9 @@ __global__ __launch_bounds__(320) void conv2d_bn_silu_stem(
             }
         };
         // Band 0 alone first: at launch every workgroup's first band would
-        // otherwise share HBM with its second, and compute would start later.
+        // otherwise share HBM with its second, and compute would start later
+        // (requesting all three at once measured 6% slower on the 224x224
+        // stem).
         issue(0);
         stem_wait_vmcnt<0>();
         stem_barrier();  // band 0 ready

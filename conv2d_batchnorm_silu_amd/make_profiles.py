@@ -1,7 +1,7 @@
 """Regenerate the rocprofv3 summaries committed under profiles/ (GPU host only).
 
     python -m conv2d_batchnorm_silu_amd.make_profiles --raw gpurun_out/prof \
-        [--traces] [--split] [--counters] [--workloads W1,W2]
+        [--traces] [--split] [--counters] [--util] [--workloads W1,W2]
 
 * ``--traces``: one ``--kernel-trace --stats`` run of ``bench.py --only`` per
   workload -> ``profiles/kernel_trace_<workload>.txt`` (average duration of
@@ -11,9 +11,15 @@
   fp16 workload, with each kernel's registers and LDS from the trace ->
   ``profiles/fused_vs_split.md``.
 * ``--counters``: ``FETCH_SIZE`` and ``WRITE_SIZE`` (each in its own
-  ``--pmc`` run) of the headline's fused kernel and of a plain device copy of
-  known size (``copy_calibration.py``), which gives the scale of each counter
-  -> ``profiles/counters.json`` and ``profiles/hbm_traffic_<workload>.txt``.
+  ``--pmc`` run) of each workload's fused kernel and of a plain device copy
+  of known size (``copy_calibration.py``), which gives the scale of each
+  counter -> ``profiles/counters.json`` and
+  ``profiles/hbm_traffic_<workload>.txt``.
+* ``--util``: one ``--pmc`` run per workload with the matrix-core, LDS and
+  VALU activity counters of its fused kernel (MFMA busy cycles against the
+  GPU's active cycles times the SIMD count, MFMA FLOPs counted by the
+  hardware against the algorithmic FLOPs, LDS instructions and bank-conflict
+  cycles) -> ``profiles/util_<workload>.txt`` and ``counters.json``.
 
 Raw rocprofv3 output stays under ``--raw``. Every profiled program is run as
 ``rocprofv3 ... -- python3 <script>`` from /tmp with TMPDIR=/tmp; this
@@ -122,7 +128,26 @@ def write_trace(raw, wl):
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     log("wrote " + path)
+    TRACE_NS[wl.name] = t["avg_ns"]
     return fr
+
+
+TRACE_NS = {}  # workload -> timed-region average duration of its fused kernel (ns)
+
+
+def trace_ns(wl):
+    """The fused kernel's duration from this run's trace, else from the
+    kernel-trace summary under profiles/."""
+    if wl.name in TRACE_NS:
+        return TRACE_NS[wl.name]
+    try:
+        with open(os.path.join(PROFILES, "kernel_trace_%s.txt" % wl.name)) as f:
+            for line in f:
+                if line.startswith("# avg duration "):
+                    return float(line.split()[3]) * 1e3
+    except OSError:
+        pass
+    return None
 
 
 def compiler_resources():
@@ -224,6 +249,28 @@ def write_split(raw, names):
     log("wrote " + path)
 
 
+_COPY_KIB = {}  # counter -> KiB per dispatch of the calibration copy (one run each)
+
+
+def copy_kib(raw, counter):
+    if counter not in _COPY_KIB:
+        cout = run_profiled(raw, "pmc_%s_copy" % counter.lower(), ["--pmc", counter], [COPY], 60)
+        cpath = find_csv(cout, "_counter_collection.csv")
+        cv, cn = profiling.counter_per_dispatch(cpath, "copy", counter)
+        if cv is None:  # the copy kernel's name varies between torch builds
+            cv, cn = profiling.counter_per_dispatch(cpath, "", counter)
+        _COPY_KIB[counter] = cv
+    return _COPY_KIB[counter]
+
+
+def fused_symbol(path):
+    """The most dispatched conv2d_bn_silu kernel of a counter or trace CSV."""
+    with open(path) as f:
+        names = collections.Counter(r["Kernel_Name"] for r in csv.DictReader(f)
+                                    if "conv2d_bn_silu" in r["Kernel_Name"])
+    return names.most_common(1)[0][0]
+
+
 def write_counters(raw, wl, source_hash):
     prog = [BENCH, "--only", "--workload", wl.name, "--steps", "20", "--warmup", "2"]
     val = {}
@@ -231,16 +278,9 @@ def write_counters(raw, wl, source_hash):
         out = run_profiled(raw, "pmc_%s_%s" % (counter.lower(), wl.name), ["--pmc", counter],
                            prog, 60)
         path = find_csv(out, "_counter_collection.csv")
-        with open(path) as f:
-            names = collections.Counter(r["Kernel_Name"] for r in csv.DictReader(f)
-                                        if "conv2d_bn_silu" in r["Kernel_Name"])
-        sym = names.most_common(1)[0][0]
+        sym = fused_symbol(path)
         v, n = profiling.counter_per_dispatch(path, sym, counter)
-        cout = run_profiled(raw, "pmc_%s_copy" % counter.lower(), ["--pmc", counter], [COPY], 60)
-        cpath = find_csv(cout, "_counter_collection.csv")
-        cv, cn = profiling.counter_per_dispatch(cpath, "copy", counter)
-        if cv is None:  # the copy kernel's name varies between torch builds
-            cv, cn = profiling.counter_per_dispatch(cpath, "", counter)
+        cv = copy_kib(raw, counter)
         from conv2d_batchnorm_silu_amd.copy_calibration import COPY_BYTES
         scale = COPY_BYTES / (cv * 1024.0)
         val[counter] = dict(raw_kib=v, dispatches=n, copy_kib=cv, scale=scale, symbol=sym,
@@ -289,6 +329,91 @@ def write_counters(raw, wl, source_hash):
     with open(path, "w") as f:
         f.write("\n".join(lines) + "\n")
     log("wrote %s and %s" % (path, cpath))
+
+
+UTIL_COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_BUSY_CYCLES",
+                 "SQ_INSTS_LDS", "SQ_ACTIVE_INST_LDS", "SQ_LDS_BANK_CONFLICT",
+                 "SQ_INSTS_VALU", "SQ_ACTIVE_INST_VALU", "GRBM_GUI_ACTIVE")
+SIMDS = 1024  # 256 CUs x 4
+CLOCK_GHZ = 2.4
+MFMA_F16_PEAK_TFLOPS = 2516.6  # published dense fp16 MFMA peak
+
+
+def per_dispatch_max(path, sym, counter):
+    """Average over dispatches of the largest instance value (GRBM counters
+    repeat the GPU-wide value per instance)."""
+    per = collections.defaultdict(float)
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if sym in r["Kernel_Name"] and r["Counter_Name"] == counter:
+                per[r["Dispatch_Id"]] = max(per[r["Dispatch_Id"]], float(r["Counter_Value"]))
+    return (sum(per.values()) / len(per), len(per)) if per else (None, 0)
+
+
+def write_util(raw, wl, source_hash):
+    prog = [BENCH, "--only", "--workload", wl.name, "--steps", "20", "--warmup", "2"]
+    args = ["--pmc"] + list(UTIL_COUNTERS)
+    out = run_profiled(raw, "util_%s" % wl.name, args, prog, 60)
+    path = find_csv(out, "_counter_collection.csv")
+    sym = fused_symbol(path)
+    v = {}
+    for c in UTIL_COUNTERS:
+        if c.startswith("GRBM_"):
+            v[c], n = per_dispatch_max(path, sym, c)
+        else:
+            v[c], n = profiling.counter_per_dispatch(path, sym, c)
+    dur_ns = trace_ns(wl)
+    clk = dur_ns * CLOCK_GHZ if dur_ns else None  # kernel clocks at the peak engine clock
+    mfma_flop = v["SQ_INSTS_VALU_MFMA_MOPS_F16"] * 512
+    alg_flop = traffic.conv_flops(wl)
+    entry = {
+        "source_hash": source_hash, "kernel_symbol": sym, "dispatches": n, "raw": v,
+        "kernel_us": dur_ns / 1e3 if dur_ns else None,
+        "mfma_busy_frac": v["SQ_VALU_MFMA_BUSY_CYCLES"] / (SIMDS * clk) if clk else None,
+        "mfma_flop_frac_of_peak": (mfma_flop / dur_ns / 1e3 / MFMA_F16_PEAK_TFLOPS
+                                   if dur_ns else None),
+        "mfma_flop_counted": mfma_flop, "algorithmic_flop": alg_flop,
+        "mfma_flop_over_algorithmic": mfma_flop / alg_flop if alg_flop else None,
+        "lds_bank_conflict_frac": (v["SQ_LDS_BANK_CONFLICT"] / v["SQ_ACTIVE_INST_LDS"]
+                                   if v["SQ_ACTIVE_INST_LDS"] else None),
+        "valu_active_per_inst": (v["SQ_ACTIVE_INST_VALU"] / v["SQ_INSTS_VALU"]
+                                 if v["SQ_INSTS_VALU"] else None),
+    }
+    cpath = os.path.join(PROFILES, "counters.json")
+    try:
+        with open(cpath) as f:
+            allc = json.load(f)
+    except (OSError, ValueError):
+        allc = {}
+    allc.setdefault(wl.name, {})["util"] = entry
+    with open(cpath, "w") as f:
+        json.dump(allc, f, indent=1)
+    fmt = lambda x: "n/a" if x is None else "%.4g" % x
+    lines = ["# Matrix-core, LDS and VALU activity of the fused kernel, workload %s (N=%d %dx%d "
+             "C_in=%d -> C_out=%d, %dx%d, %s)" % (wl.name, wl.N, wl.H, wl.W, wl.C_in, wl.C_out,
+                                                   wl.kh, wl.kw, wl.dtype),
+             "# command (cd /tmp; TMPDIR=/tmp; one pass, 8 SQ counters and 1 GRBM counter):",
+             "#   " + cmd_text(args, prog),
+             "kernel %s (source hash %s), %d dispatches averaged" % (sym[:80], source_hash, n)]
+    for c in UTIL_COUNTERS:
+        lines.append("%-30s %.6g per dispatch" % (c, v[c]))
+    lines += [
+        "fused kernel duration (timed region of its kernel trace) %s us" % fmt(entry["kernel_us"]),
+        "MFMA busy: SQ_VALU_MFMA_BUSY_CYCLES (summed over the %d SIMDs) / (%d x duration x "
+        "%.1f GHz) = %s" % (SIMDS, SIMDS, CLOCK_GHZ, fmt(entry["mfma_busy_frac"])),
+        "MFMA rate: counted MFMA FLOPs / duration / %.1f TFLOP/s (dense fp16 peak) = %s" % (
+            MFMA_F16_PEAK_TFLOPS, fmt(entry["mfma_flop_frac_of_peak"])),
+        "MFMA FLOPs counted (SQ_INSTS_VALU_MFMA_MOPS_F16 x 512) = %.4g vs algorithmic %.4g "
+        "(ratio %s: padding and tail blocks the matrix cores still compute)" % (
+            mfma_flop, alg_flop, fmt(entry["mfma_flop_over_algorithmic"])),
+        "LDS: SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS = %s (bank-conflict stall cycles per "
+        "LDS-issue cycle)" % fmt(entry["lds_bank_conflict_frac"]),
+        "VALU active cycles per VALU instruction (SQ_ACTIVE_INST_VALU / SQ_INSTS_VALU) = %s" %
+        fmt(entry["valu_active_per_inst"])]
+    path_txt = os.path.join(PROFILES, "util_%s.txt" % wl.name)
+    with open(path_txt, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    log("wrote %s" % path_txt)
 
 
 def COPY_BYTES_MIB():
@@ -360,6 +485,7 @@ def main():
     ap.add_argument("--traces", action="store_true")
     ap.add_argument("--split", action="store_true")
     ap.add_argument("--counters", action="store_true")
+    ap.add_argument("--util", action="store_true")
     ap.add_argument("--workloads", default=None, help="comma-separated (default: all)")
     ap.add_argument("--dest", default=None, help="where the summaries go (default: profiles/)")
     ap.add_argument("--bench-json", default=None,
@@ -383,7 +509,11 @@ def main():
     if args.split:
         write_split(raw, names)
     if args.counters:
-        write_counters(raw, WORKLOADS[HEADLINE], bench.source_hash())
+        for n in names:
+            write_counters(raw, WORKLOADS[n], bench.source_hash())
+    if args.util:
+        for n in names:
+            write_util(raw, WORKLOADS[n], bench.source_hash())
     if args.bench_json:
         write_bench_table(args.bench_json)
 

@@ -88,6 +88,29 @@ def measure() -> dict:
     for nt in (0, 1):
         ms = _time(torch, lambda: lib.tgp_write(b.data_ptr(), nbytes, nt, grid, s), 10)
         res["hbm_write_%s_gbs" % ("nt" if nt else "plain")] = round(nbytes / ms / 1e6, 1)
+    # The same copy at the HBM-bound layers' sizes (bytes read + written =
+    # the layer's algorithmic bytes): the rate a streaming kernel of that
+    # size can reach,
+    # launch and ramp included (grid: 8 workgroups of 256 per CU, capped by
+    # the 16-byte elements).
+    # Successive calls take successive slices of the 1 GB buffers, as the
+    # bench rotates its input and output copies, so that each call reads
+    # and writes HBM rather than the last-level cache.
+    for name, moved in (("conv1x1_c64_k256", 64_260_096), ("stem3x3s2_k16", 44_958_688),
+                        ("stem3x3s2_k24", 57_804_240)):
+        half = moved // 2 // 256 * 256
+        g = min(CUS * 8, (half // 16 + 255) // 256)
+        nslices = nbytes // half
+        ctr = [0]
+
+        def rotating_copy():
+            k = ctr[0] % nslices
+            ctr[0] += 1
+            return lib.tgp_copy(a.data_ptr() + k * half, b.data_ptr() + k * half, half, g, s)
+
+        ms = _time(torch, rotating_copy, 4 * nslices)
+        res["copy_%s_us" % name] = round(ms * 1e3, 2)
+        res["copy_%s_gbs" % name] = round(2 * half / ms / 1e6, 1)
     del a, b
     iters = 4000
     for shape, name, flop_per_wave_iter in ((0, "16x16x32", 8 * 16384), (1, "32x32x16", 4 * 32768)):
