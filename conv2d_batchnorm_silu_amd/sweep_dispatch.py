@@ -14,6 +14,13 @@ Grid: k in {1, 3, 5, 7} (pad k//2), stride in {1, 2}, C_in in {3, 16, 64,
 Inputs are device-side random fp16 tensors (correctness is the tests' job).
 
     python -m conv2d_batchnorm_silu_amd.sweep_dispatch --out profiles/dispatch_sweep
+
+With --patch-tiles it times every tile configuration of the patch-staged
+implicit GEMM on the stride-1 shapes it serves instead (the data behind the
+tile cost model in csrc/igemm_patch.hip):
+
+    python -m conv2d_batchnorm_silu_amd.sweep_dispatch --patch-tiles --reps 20 \
+        --out profiles/patch_tile_sweep
 """
 import argparse
 import json
@@ -53,15 +60,103 @@ def time_plan(torch, plan, x, w, sc, bi, y, reps):
     return e0.elapsed_time(e1) * 1e3 / reps  # us
 
 
+def tile_shapes():
+    """Stride-1 shapes for the patch-staged kernel's tile sweep: k in {1, 3,
+    5}, C_in in {64, 128}, C_out in {8 .. 256} on 8 x 112 x 112 images, plus
+    the 3x3 and 7x7 benchmark layers."""
+    for k in (1, 3, 5):
+        for cin in (64, 128):
+            for cout in (8, 16, 24, 32, 48, 64, 128, 256):
+                yield dict(name="k%d_c%d_k%d" % (k, cin, cout), N=8, H=112, W=112, C_in=cin,
+                           C_out=cout, k=k, pad=k // 2)
+    from conv2d_batchnorm_silu_amd.inputs import WORKLOADS
+    for name in ("conv3x3_c128_k128", "conv7x7_c64_k64"):
+        wl = WORKLOADS[name]
+        yield dict(name=name, N=wl.N, H=wl.H, W=wl.W, C_in=wl.C_in, C_out=wl.C_out, k=wl.kh,
+                   pad=wl.pad)
+
+
+def patch_tiles(out, reps):
+    """Every tile configuration of the patch-staged implicit GEMM that fits
+    each shape of tile_shapes(), forced with the tuning key patch_cfg (the 1x1
+    kernels switched off with cu=0, igemm_rw=0), against the configuration
+    the plan chooses -> <out>.jsonl and <out>.md."""
+    import torch
+    from conv2d_batchnorm_silu_amd import binding as B
+    B.library()
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    base = {"cu": 0, "igemm_rw": 0}
+    rows = []
+    with open(out + ".jsonl", "w") as jf:
+        for s in tile_shapes():
+            gen.manual_seed(len(rows) + 1)
+            x = torch.randn(s["N"], s["H"], s["W"], s["C_in"], device=dev, generator=gen).half()
+            w = (torch.randn(s["C_out"], s["k"], s["k"], s["C_in"], device=dev, generator=gen) /
+                 (s["k"] * s["k"] * s["C_in"]) ** 0.5).half()
+            sc = torch.ones(s["C_out"], device=dev)
+            bi = torch.zeros(s["C_out"], device=dev)
+            y = torch.empty(s["N"], s["H"] + 2 * s["pad"] - s["k"] + 1,
+                            s["W"] + 2 * s["pad"] - s["k"] + 1, s["C_out"], device=dev).half()
+
+            def mk(extra):
+                return B.ConvBnSilu(s["N"], s["H"], s["W"], s["C_in"], s["C_out"], s["k"], s["k"],
+                                    1, s["pad"], "f16", "igemm", tuning=dict(base, **extra))
+            chosen = mk({}).describe()
+            if not chosen.startswith("igemm_patch"):
+                continue
+            us = {}
+            for cfg in range(10):
+                plan = mk({"patch_cfg": cfg})
+                if not plan.describe().startswith("igemm_patch cfg=%d " % cfg):
+                    continue  # this tile does not fit the shape
+                us[cfg] = round(time_plan(torch, plan, x, w, sc, bi, y, reps), 2)
+            row = dict(s, chosen=int(chosen.split("cfg=")[1].split()[0]), us=us)
+            rows.append(row)
+            jf.write(json.dumps(row) + "\n")
+            jf.flush()
+            print(json.dumps(row), flush=True)
+    lines = ["# Patch-staged implicit GEMM: every tile configuration per stride-1 shape "
+             "(one MI355X)",
+             "# command: python -m conv2d_batchnorm_silu_amd.sweep_dispatch --patch-tiles --out "
+             "%s --reps %d" % (out, reps),
+             "# us per launch (HIP events over %d back-to-back launches after 5 ms untimed); "
+             "'-' = the tile does not fit the shape" % reps,
+             "",
+             "shape | N H W | " + " | ".join("cfg %d" % c for c in range(10)) +
+             " | chosen | chosen / fastest",
+             "---|---|" + "---|" * 10 + "---|---"]
+    ratios = []
+    for r in rows:
+        best = min(r["us"].values())
+        ratio = r["us"][r["chosen"]] / best
+        ratios.append(ratio)
+        lines.append("%s | %d %d %d | %s | %d | %.3f" % (
+            r["name"], r["N"], r["H"], r["W"],
+            " | ".join(str(r["us"].get(c, "-")) for c in range(10)), r["chosen"], ratio))
+    if ratios:
+        lines += ["", "chosen = fastest on %d of %d shapes; within 10%% on %d; worst chosen / "
+                  "fastest %.3f" % (sum(1 for q in ratios if q == 1.0), len(ratios),
+                                    sum(1 for q in ratios if q <= 1.10), max(ratios))]
+    with open(out + ".md", "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("wrote %s.md" % out, file=sys.stderr)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--out", default="dispatch_sweep", help="output path prefix (.jsonl, .md)")
+    ap.add_argument("--patch-tiles", action="store_true",
+                    help="time every tile of the patch-staged kernel instead (patch_tiles())")
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--limit", type=int, default=0, help="only the first N shapes (0: all)")
     ap.add_argument("--from-jsonl", default=None,
                     help="re-render <out>.md from this JSON-lines file of an earlier sweep")
     ap.add_argument("--gpu", default=None, help="device name for the header (--from-jsonl)")
     args = ap.parse_args(argv)
+    if args.patch_tiles:
+        patch_tiles(args.out, args.reps)
+        return 0
     if args.from_jsonl:
         with open(args.from_jsonl) as f:
             rows = [json.loads(l) for l in f if l.strip()]
