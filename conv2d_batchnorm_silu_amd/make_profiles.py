@@ -249,18 +249,25 @@ def write_split(raw, names):
     log("wrote " + path)
 
 
-_COPY_KIB = {}  # counter -> KiB per dispatch of the calibration copy (one run each)
+_COPY_KIB = {}  # (counter, mode) -> KiB per dispatch of the calibration copy (one run each)
+CALIBRATIONS = (("", []), ("_dma", ["--dma"]), ("_rotate", ["--rotate"]))  # first: the one used
 
 
-def copy_kib(raw, counter):
-    if counter not in _COPY_KIB:
-        cout = run_profiled(raw, "pmc_%s_copy" % counter.lower(), ["--pmc", counter], [COPY], 60)
+def copy_kib(raw, counter, mode=""):
+    """The counter's value per dispatch for a copy of COPY_BYTES: torch's
+    copy of one buffer pair (mode ""), this library's copy that reads through
+    direct-to-LDS buffer loads ("_dma"), or torch's copy over four buffer
+    pairs ("_rotate")."""
+    key = (counter, mode)
+    if key not in _COPY_KIB:
+        name = "pmc_%s_copy%s" % (counter.lower(), mode)
+        cout = run_profiled(raw, name, ["--pmc", counter], [COPY] + dict(CALIBRATIONS)[mode], 60)
         cpath = find_csv(cout, "_counter_collection.csv")
         cv, cn = profiling.counter_per_dispatch(cpath, "copy", counter)
         if cv is None:  # the copy kernel's name varies between torch builds
             cv, cn = profiling.counter_per_dispatch(cpath, "", counter)
-        _COPY_KIB[counter] = cv
-    return _COPY_KIB[counter]
+        _COPY_KIB[key] = cv
+    return _COPY_KIB[key]
 
 
 def fused_symbol(path):
@@ -280,12 +287,20 @@ def write_counters(raw, wl, source_hash):
         path = find_csv(out, "_counter_collection.csv")
         sym = fused_symbol(path)
         v, n = profiling.counter_per_dispatch(path, sym, counter)
-        cv = copy_kib(raw, counter)
         from conv2d_batchnorm_silu_amd.copy_calibration import COPY_BYTES
-        scale = COPY_BYTES / (cv * 1024.0)
-        val[counter] = dict(raw_kib=v, dispatches=n, copy_kib=cv, scale=scale, symbol=sym,
-                            bytes=v * 1024.0 * scale)
+        scales = {m: COPY_BYTES / (copy_kib(raw, counter, m) * 1024.0) for m, _ in CALIBRATIONS}
+        val[counter] = dict(raw_kib=v, dispatches=n, copy_kib=copy_kib(raw, counter),
+                            symbol=sym, copy_scales=scales)
+    # Scales. The copies' absolute scales vary between runs and buffer
+    # reuse (recorded below), but in every copy FETCH_SIZE's scale is the
+    # same multiple of WRITE_SIZE's, and this kernel writes y exactly once:
+    # WRITE_SIZE is scaled to y's bytes, FETCH_SIZE by the copy's ratio.
     b = traffic.workload_bytes(wl)
+    wscale = b["y"] / (val["WRITE_SIZE"]["raw_kib"] * 1024.0)
+    ratio = val["FETCH_SIZE"]["copy_scales"][""] / val["WRITE_SIZE"]["copy_scales"][""]
+    for counter, sc in (("FETCH_SIZE", wscale * ratio), ("WRITE_SIZE", wscale)):
+        val[counter]["scale"] = sc
+        val[counter]["bytes"] = val[counter]["raw_kib"] * 1024.0 * sc
     alg = traffic.fused_bytes(wl)
     hbm = val["FETCH_SIZE"]["bytes"] + val["WRITE_SIZE"]["bytes"]
     sym = val["FETCH_SIZE"]["symbol"]
@@ -293,6 +308,8 @@ def write_counters(raw, wl, source_hash):
              "fetch_kib_raw": val["FETCH_SIZE"]["raw_kib"],
              "write_kib_raw": val["WRITE_SIZE"]["raw_kib"],
              "fetch_scale": val["FETCH_SIZE"]["scale"], "write_scale": val["WRITE_SIZE"]["scale"],
+             "copy_scales": {c: val[c]["copy_scales"] for c in ("FETCH_SIZE", "WRITE_SIZE")},
+             "fetch_over_write_scale_of_copy": ratio,
              "fetch_bytes": val["FETCH_SIZE"]["bytes"], "write_bytes": val["WRITE_SIZE"]["bytes"],
              "hbm_bytes_per_launch": int(round(hbm)), "algorithmic_bytes": alg,
              "excess_frac": hbm / alg - 1.0}
@@ -310,12 +327,22 @@ def write_counters(raw, wl, source_hash):
              "# commands (cd /tmp; TMPDIR=/tmp), each counter in its own run:"]
     for counter in ("FETCH_SIZE", "WRITE_SIZE"):
         lines.append("#   " + cmd_text(["--pmc", counter], prog))
-    lines += ["# calibration with a plain %d MiB device copy (reads and writes exactly %d bytes):"
-              % (COPY_BYTES_MIB(), COPY_BYTES_MIB() * 2**20),
-              "#   " + cmd_text(["--pmc", "FETCH_SIZE"], [COPY]) + "   (and WRITE_SIZE)",
-              "# copy: FETCH_SIZE %.1f KiB/dispatch (scale %.4f); WRITE_SIZE %.1f KiB/dispatch "
-              "(scale %.4f)" % (val["FETCH_SIZE"]["copy_kib"], val["FETCH_SIZE"]["scale"],
-                                val["WRITE_SIZE"]["copy_kib"], val["WRITE_SIZE"]["scale"]),
+    cs = lambda c, m: val[c]["copy_scales"][m]
+    lines += ["# calibration: a %d MiB device copy (reads and writes exactly %d bytes), each "
+              "counter in its own run, three ways: torch's copy of one buffer pair, this "
+              "library's copy reading through direct-to-LDS loads, torch's copy over four "
+              "buffer pairs:" % (COPY_BYTES_MIB(), COPY_BYTES_MIB() * 2**20),
+              "#   " + cmd_text(["--pmc", "FETCH_SIZE"], [COPY]) + "   (and WRITE_SIZE; "
+              "and with --dma, --rotate)",
+              "# copy scales FETCH / WRITE: one pair %.4f / %.4f, direct-to-LDS %.4f / %.4f, four "
+              "pairs %.4f / %.4f (the absolute scale moves with the run and with buffer reuse; "
+              "the ratio stays %.3f)" % (cs("FETCH_SIZE", ""), cs("WRITE_SIZE", ""),
+                                        cs("FETCH_SIZE", "_dma"), cs("WRITE_SIZE", "_dma"),
+                                        cs("FETCH_SIZE", "_rotate"), cs("WRITE_SIZE", "_rotate"),
+                                        ratio),
+              "# applied: WRITE_SIZE scaled to y's bytes (written exactly once; raw x 1024 / y = "
+              "%.4f), FETCH_SIZE by that scale times the copy ratio: %.4f / %.4f" % (
+                  1.0 / wscale, val["FETCH_SIZE"]["scale"], val["WRITE_SIZE"]["scale"]),
               "kernel %s (source hash %s), %d dispatches averaged" % (
                   sym[:80], source_hash, val["FETCH_SIZE"]["dispatches"]),
               "FETCH_SIZE raw %.1f KiB -> %.3f MB   (algorithmic reads x+w+BN = %.3f MB)" % (

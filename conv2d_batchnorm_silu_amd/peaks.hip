@@ -45,6 +45,36 @@ __global__ void pk_write(pk_u32x4* __restrict__ dst, long long n) {
     }
 }
 
+// Copy whose reads are direct-to-LDS buffer loads (the fused kernels' way of
+// reading x): each wave moves 1 KB per step, global -> LDS (lane l's 16
+// bytes land at the wave's slot + 16*l), then each lane stores the slot it
+// loaded. The lane reads only what its own load wrote, so the wave's own
+// vector-memory count orders the two. A calibration kernel for the HBM
+// byte counters of such reads.
+__global__ __launch_bounds__(256) void pk_copy_dma(const pk_u32x4* __restrict__ src,
+                                                   pk_u32x4* __restrict__ dst, long long n) {
+    __shared__ pk_u32x4 slot[256];
+    const unsigned long long a = (unsigned long long)src;
+    pk_u32x4 rs;
+    rs[0] = (unsigned)a;
+    rs[1] = (unsigned)(a >> 32) & 0xffffu;
+    rs[2] = (unsigned)(n * 16);
+    rs[3] = 0x00020000u;
+    const int wave = threadIdx.x >> 6;
+    const unsigned lds = __builtin_amdgcn_readfirstlane(
+        (unsigned)(uintptr_t)((__attribute__((address_space(3))) pk_u32x4*)slot) + wave * 1024u);
+    for (long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (long long)gridDim.x * blockDim.x) {
+        const unsigned voff = (unsigned)(i * 16);
+        asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds\n\ts_waitcnt vmcnt(0)"
+                     :
+                     : "v"(voff), "s"(rs), "{m0}"(lds)
+                     : "memory");
+        dst[i] = slot[threadIdx.x];
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+}
+
 // ---- MFMA ---------------------------------------------------------------
 // Each wave runs `iters` rounds of ACC independent MFMAs (no dependency
 // between consecutive instructions), so the matrix core is the only limit.
@@ -271,6 +301,14 @@ int tgp_valu(int op, int iters, int grid, int block, void* out, void* stream) {
 // the caller's (peaks.py documents what it uses).
 int tgp_copy(const void* src, void* dst, long long bytes, int grid, void* stream) {
     hipLaunchKernelGGL(pk_copy, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       (const pk_u32x4*)src, (pk_u32x4*)dst, bytes / 16);
+    return (int)hipGetLastError();
+}
+
+// bytes: a multiple of 16 below 4 GiB; grid x 256 lanes move 16 bytes each per step.
+int tgp_copy_dma(const void* src, void* dst, long long bytes, int grid, void* stream) {
+    if (bytes % 16 != 0 || bytes >= (1LL << 32)) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(pk_copy_dma, dim3(grid), dim3(256), 0, (hipStream_t)stream,
                        (const pk_u32x4*)src, (pk_u32x4*)dst, bytes / 16);
     return (int)hipGetLastError();
 }

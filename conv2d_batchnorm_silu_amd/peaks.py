@@ -44,6 +44,7 @@ def _lib():
     lib = ctypes.CDLL(LIB)
     vp, i, ll = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
     lib.tgp_copy.argtypes = [vp, vp, ll, i, vp]
+    lib.tgp_copy_dma.argtypes = [vp, vp, ll, i, vp]
     lib.tgp_read.argtypes = [vp, ll, vp, i, vp]
     lib.tgp_write.argtypes = [vp, ll, i, i, vp]
     lib.tgp_mfma.argtypes = [i, i, i, i, vp, vp]
@@ -83,6 +84,8 @@ def measure() -> dict:
     grid = CUS * 8
     ms = _time(torch, lambda: lib.tgp_copy(a.data_ptr(), b.data_ptr(), nbytes, grid, s), 10)
     res["hbm_copy_gbs"] = round(2 * nbytes / ms / 1e6, 1)
+    ms = _time(torch, lambda: lib.tgp_copy_dma(a.data_ptr(), b.data_ptr(), nbytes, grid, s), 10)
+    res["hbm_copy_dma_gbs"] = round(2 * nbytes / ms / 1e6, 1)
     ms = _time(torch, lambda: lib.tgp_read(a.data_ptr(), nbytes, out.data_ptr(), grid, s), 10)
     res["hbm_read_gbs"] = round(nbytes / ms / 1e6, 1)
     for nt in (0, 1):
