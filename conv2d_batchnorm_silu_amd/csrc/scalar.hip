@@ -18,8 +18,11 @@ template <typename T, int EPI>
 __global__ __launch_bounds__(256) void conv2d_bn_silu_scalar(
     const T* __restrict__ x, const T* __restrict__ w, const float* __restrict__ scale,
     const float* __restrict__ bias, T* __restrict__ y, ConvGeom g, int total) {
-    int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= total) return;
+    // 64-bit before the comparison: with total close to 2^31 the last
+    // block's lanes would overflow an int.
+    const long long lidx = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (lidx >= total) return;
+    const int idx = (int)lidx;
     int k = idx % g.C_out;
     int pix = idx / g.C_out;
     int q = pix % g.Q;
@@ -50,8 +53,8 @@ __global__ __launch_bounds__(256) void conv2d_bn_silu_scalar(
 
 hipError_t launch_scalar(const ConvGeom& g, bool f32, int epi, const void* x, const void* w,
                          const float* scale, const float* bias, void* y, hipStream_t s) {
-    int total = g.M * g.C_out;  // < 2^31, checked at plan time
-    dim3 grid((total + 255) / 256), block(256);
+    const int total = g.M * g.C_out;  // < 2^31, checked at plan time
+    dim3 grid((unsigned)(((long long)total + 255) / 256)), block(256);
 #define TG_S32(E)                                                                \
     hipLaunchKernelGGL((conv2d_bn_silu_scalar<float, E>), grid, block, 0, s,       \
                        (const float*)x, (const float*)w, scale, bias, (float*)y, g, total)
