@@ -336,29 +336,29 @@ __global__ __launch_bounds__(64 * (WM * WN * WK + 1), 1) void conv2d_bn_silu_ige
     // Chunk kc's filter data has landed once only the loads of the RING - 2
     // chunks issued after it are pending (chunks run RING - 1 ahead).
     auto wait_chunk = [&]() { pt_wait_vmcnt<(RING - 2) * S::LI>(); };
-    auto load = [&](int kc, int tr, int ts, int c, Frags& F) {
-        const unsigned st = ring_lds + (unsigned)((kc % RING) * S::WSTAGE);
-        const unsigned delta = (unsigned)((tr * PW + ts) * pstride + c * 128);
-#pragma unroll
-        for (int kk = 0; kk < KSW; ++kk) {
-            const int ks = WK == 2 ? kg : kk;
-#pragma unroll
-            for (int f = 0; f < S::FN; ++f)
-                F.a[kk][f] = pt_lds16(st + (unsigned)(bbase[f] ^ (WK == 2 ? 0 : ks * 64)));
-#pragma unroll
-            for (int f = 0; f < S::FM; ++f)
-                F.b[kk][f] = pt_lds16(patch_lds + (unsigned)(abase[f] + ks * 64) + delta);
-        }
+    // MFMA m of a step (m = (kk*FN + i)*FM + j: acc[i][j] += a[kk][i] x
+    // b[kk][j], the order of the plain triple loop) as inline assembly, so
+    // that it keeps its place in program order between the step's filter
+    // loads and LDS reads (also inline assembly). The compiler schedules a
+    // builtin MFMA freely and put all of a step's MFMAs in one run after the
+    // step's other instructions; the wave then issued those with the matrix
+    // core idle, and on both waves of a SIMD at once.
+    auto mfma = [&](const Frags& F, int m) {
+        const int kk = m / (S::FN * S::FM), i = (m / S::FM) % S::FN, j = m % S::FM;
+        asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                     : "+v"(acc[i][j])
+                     : "v"(F.a[kk][i]), "v"(F.b[kk][j]));
     };
-    auto mma = [&](const Frags& F) {
-#pragma unroll
-        for (int kk = 0; kk < KSW; ++kk)
-#pragma unroll
-            for (int i = 0; i < S::FN; ++i)
-#pragma unroll
-                for (int j = 0; j < S::FM; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(F.a[kk][i], F.b[kk][j],
-                                                                       acc[i][j], 0, 0, 0);
+    // Read r of a chunk's fragments (kk = r / (FN + FM): FN filter
+    // fragments from ring stage st, then FM pixel fragments at patch offset
+    // delta).
+    auto read = [&](Frags& F, int r, unsigned st, unsigned delta) {
+        const int kk = r / (S::FN + S::FM), q = r % (S::FN + S::FM);
+        const int ks = WK == 2 ? kg : kk;
+        if (q < S::FN)
+            F.a[kk][q] = pt_lds16(st + (unsigned)(bbase[q] ^ (WK == 2 ? 0 : ks * 64)));
+        else
+            F.b[kk][q - S::FN] = pt_lds16(patch_lds + (unsigned)(abase[q - S::FN] + ks * 64) + delta);
     };
     // (tap_r, tap_s, cc) of the chunk whose fragments are loaded next;
     // advanced with selects, not branches.
@@ -370,34 +370,48 @@ __global__ __launch_bounds__(64 * (WM * WN * WK + 1), 1) void conv2d_bn_silu_ige
         tap_s = ws ? 0 : (wc ? tap_s + 1 : tap_s);
         tap_r = ws ? tap_r + 1 : tap_r;
     };
+    constexpr int NM = KSW * S::FN * S::FM;    // MFMAs per step
+    constexpr int NL = KSW * (S::FN + S::FM);  // fragment reads per step
     Frags F0, F1;
     wait_chunk();
     wait_rows(0);
-    load(0, tap_r, tap_s, cc, F0);
+#pragma unroll
+    for (int r = 0; r < NL; ++r) read(F0, r, ring_lds, 0u);
     advance();
     frag_wait(F0);
     // One step: refill the ring, fetch chunk kc+1's fragments into `nxt`,
     // run chunk kc's MFMAs from `cur`, then wait for the fetch (it overlaps
     // the MFMAs). Stage (kc + RING - 1) % RING was last read for chunk
     // kc - 1, whose fragment reads completed at the end of step kc - 2.
+    // The step's other instructions sit between its MFMAs, one group after
+    // each: the filter loads after the first, the ring wait (and at a
+    // filter row's first chunk the patch-row wait) after the second, then
+    // one fragment read after each further MFMA. The matrix core works
+    // through the earlier MFMAs meanwhile.
+    // The last step reads fragments too (one MFMA sequence in the code, not
+    // two): at patch offset 0 and a ring stage that the trailing zero-filling
+    // filter loads may be writing, values no MFMA uses. The fragment
+    // registers are kept live past the loop's last LDS wait (below), so that
+    // no other value is given a register a late LDS write would overwrite.
     auto step = [&](int kc, Frags& cur, Frags& nxt) {
-        issue(kc + RING - 1);
-        wait_chunk();
-        // Never issue reads whose results are dead: the compiler would hand
-        // their registers to other values, which the late LDS data would
-        // then overwrite.
-        if (kc + 1 < nk) {
-            if (tap_s == 0 && cc == 0) wait_rows(tap_r);  // first chunk of a filter row
-            load(kc + 1, tap_r, tap_s, cc, nxt);
+        const bool more = kc + 1 < nk;
+        const bool row_wait = more && tap_s == 0 && cc == 0;  // first chunk of a filter row
+        const unsigned st = ring_lds + (unsigned)(((kc + 1) % RING) * S::WSTAGE);
+        const unsigned delta = more ? (unsigned)((tap_r * PW + tap_s) * pstride + cc * 128) : 0u;
+#pragma unroll
+        for (int m = 0; m < NM; ++m) {
+            mfma(cur, m);
+            if (m == 0) issue(kc + RING - 1);
+            if (m == 1) {
+                wait_chunk();
+                if (row_wait) wait_rows(tap_r);
+            }
+            if (m >= 2 && m - 2 < NL) read(nxt, m - 2, st, delta);
         }
+#pragma unroll
+        for (int r = NM - 2; r < NL; ++r) read(nxt, r > 0 ? r : 0, st, delta);
         advance();
-        // Raised priority while this wave's MFMAs issue: the other K-group's
-        // wave on the SIMD then issues its loads and LDS reads in the gaps
-        // rather than in step with this one (measured: 7x7 layer -2%).
-        __builtin_amdgcn_s_setprio(1);
-        mma(cur);
-        __builtin_amdgcn_s_setprio(0);
-        frag_wait(cur);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     };
     // Pairs of steps in straight-line code (the compiler's wait counts stay
     // exact across the back edge), then an odd last step.
@@ -408,8 +422,21 @@ __global__ __launch_bounds__(64 * (WM * WN * WK + 1), 1) void conv2d_bn_silu_ige
     }
     if (kc < nk) {  // odd last step: nothing left to fetch
         issue(kc + RING - 1);
-        mma(F0);
+#pragma unroll
+        for (int m = 0; m < NM; ++m) mfma(F0, m);
     }
+#pragma unroll
+    for (int kk = 0; kk < KSW; ++kk) {
+#pragma unroll
+        for (int f = 0; f < S::FN; ++f) asm volatile("" ::"v"(F0.a[kk][f]), "v"(F1.a[kk][f]));
+#pragma unroll
+        for (int f = 0; f < S::FM; ++f) asm volatile("" ::"v"(F0.b[kk][f]), "v"(F1.b[kk][f]));
+    }
+    // The accumulators are read below by LDS stores and VALU: the matrix
+    // core's last results must be written first (inline-assembly MFMAs get
+    // no hazard padding from the compiler; 32 wait states cover the
+    // 8-pass 16x16x32 MFMA with margin).
+    asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
     // The last steps' filter loads (past the last chunk, zero-filling) land
     // in the ring asynchronously: drain them before the ring's LDS is reused.
     pt_wait_vmcnt<0>();

@@ -172,6 +172,56 @@ __global__ __launch_bounds__(512) void pk_lds_stride(int iters, int stride, floa
     if ((float)s[0] == 12345.678f) out[0] = (float)s[1];
 }
 
+// LDS read patterns of the implicit-GEMM fragments. Each of 8 waves issues
+// 12 ds_read_b128 back to back per iteration, 4 KB apart (the same bank
+// alignment), then waits; lane l = 16 p + r (row r, piece p) reads at byte
+// offset:
+//   0  16 l                                   (linear: every bank once per 16 lanes)
+//   1  r * prm + 16 p                         (16 pixels of a patch, pixel stride prm)
+//   2  (r + (r >= 8 ? 6 : 0)) * prm + 16 p    (... wrapping to the next row after 8)
+//   3  64 r + 16 (p ^ ((r >> 1) & 3))         (64-byte filter rows, three swizzles)
+//   4  64 r + 16 (p ^ ((r >> 2) & 3))
+//   5  64 r + 16 (p ^ (((r >> 1) ^ (r >> 2)) & 3))
+//   6  128 r + 16 ((p + 4 prm) ^ ((r >> 1) & 7))      (128-byte filter rows,
+//   7  128 r + 16 ((p + 4 prm) ^ ((r & 7) ^ (r >> 3)))  half prm of the row)
+// Bytes per clock per CU against the linear pattern show the bank conflicts
+// of each layout.
+constexpr int kPatReads = 12, kPatStep = 4096, kPatLds = 96 * 1024;
+__global__ __launch_bounds__(512) void pk_lds_pattern(int iters, int mode, int prm, float* out) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char pk_dyn[];
+    for (int i = threadIdx.x; i < kPatLds / 16; i += blockDim.x)
+        ((pk_u32x4*)pk_dyn)[i] = (pk_u32x4){(unsigned)i, 3u, 5u, 7u};
+    __syncthreads();
+    const int lane = threadIdx.x & 63, r = lane & 15, p = lane >> 4;
+    int off;
+    switch (mode) {
+        case 0: off = 16 * lane; break;
+        case 1: off = r * prm + 16 * p; break;
+        case 2: off = (r + (r >= 8 ? 6 : 0)) * prm + 16 * p; break;
+        case 3: off = 64 * r + 16 * (p ^ ((r >> 1) & 3)); break;
+        case 4: off = 64 * r + 16 * (p ^ ((r >> 2) & 3)); break;
+        case 5: off = 64 * r + 16 * (p ^ (((r >> 1) ^ (r >> 2)) & 3)); break;
+        case 6: off = 128 * r + 16 * ((p + 4 * prm) ^ ((r >> 1) & 7)); break;
+        default: off = 128 * r + 16 * ((p + 4 * prm) ^ ((r & 7) ^ (r >> 3))); break;
+    }
+    const unsigned base = (unsigned)(uintptr_t)(
+        (__attribute__((address_space(3))) unsigned char*)pk_dyn) + (unsigned)off;
+    unsigned addr[kPatReads];
+#pragma unroll
+    for (int u = 0; u < kPatReads; ++u) addr[u] = base + (unsigned)(u * kPatStep);
+    pk_u32x4 acc = {0, 0, 0, 0};
+    for (int it = 0; it < iters; ++it) {
+        pk_u32x4 v[kPatReads];
+#pragma unroll
+        for (int u = 0; u < kPatReads; ++u)
+            asm volatile("ds_read_b128 %0, %1" : "=v"(v[u]) : "v"(addr[u]));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int u = 0; u < kPatReads; ++u) acc ^= v[u];
+    }
+    if ((acc[0] ^ acc[1] ^ acc[2] ^ acc[3]) == 0x9e3779b9u) out[0] = 1.f;
+}
+
 // The implicit-GEMM step shape: per wave a 4 x 7 grid of 16x16x32 MFMAs
 // (4 filter fragments held in registers, 7 pixel fragments) with the next
 // step's 7 pixel fragments read from LDS (16 rows of a 160-byte stride,
@@ -352,6 +402,22 @@ int tgp_lds_stride(int iters, int stride, int grid, int block, void* out, void* 
     if (e != hipSuccess) return (int)e;
     hipLaunchKernelGGL(pk_lds_stride, dim3(grid), dim3(block), lds, (hipStream_t)stream, iters,
                        stride, (float*)out);
+    return (int)hipGetLastError();
+}
+
+// One workgroup of 512 threads per CU (96 KB of LDS each); mode and prm as
+// in pk_lds_pattern: prm 16..512 in steps of 16 for modes 1-2, 0 or 1 for
+// modes 6-7 (every address stays inside the 96 KB).
+int tgp_lds_pattern(int iters, int mode, int prm, int grid, void* out, void* stream) {
+    if (mode < 0 || mode > 7) return (int)hipErrorInvalidValue;
+    if ((mode == 1 || mode == 2) && (prm < 16 || prm > 512 || prm % 16 != 0))
+        return (int)hipErrorInvalidValue;
+    if (mode >= 6 && prm != 0 && prm != 1) return (int)hipErrorInvalidValue;
+    hipError_t e = hipFuncSetAttribute((const void*)pk_lds_pattern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kPatLds);
+    if (e != hipSuccess) return (int)e;
+    hipLaunchKernelGGL(pk_lds_pattern, dim3(grid), dim3(512), kPatLds, (hipStream_t)stream, iters,
+                       mode, prm, (float*)out);
     return (int)hipGetLastError();
 }
 

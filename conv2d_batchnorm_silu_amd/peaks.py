@@ -52,6 +52,7 @@ def _lib():
     lib.tgp_lds_stride.argtypes = [i, i, i, i, vp, vp]
     lib.tgp_valu.argtypes = [i, i, i, i, vp, vp]
     lib.tgp_mfma_lds.argtypes = [i, i, i, vp, vp, vp]
+    lib.tgp_lds_pattern.argtypes = [i, i, i, i, vp, vp]
     return lib
 
 
@@ -156,6 +157,21 @@ def measure() -> dict:
                                                      out.data_ptr(), s), 5)
         nb = CUS * 4 * lds_iters * 8 * 1024
         res["lds_frag_stride%d_bytes_per_clk_cu" % stride] = round(
+            nb / ms / 1e9 * 1e12 / (CUS * CLOCK_GHZ * 1e9), 1)
+    # Fragment layouts (peaks.hip, pk_lds_pattern): 8 waves per CU, 12 reads
+    # in flight per wave; bytes per clock per CU.
+    pat_iters = 4000
+    patterns = [("linear", 0, 0)]
+    for stride in (144, 160, 176, 272, 288):
+        patterns.append(("patch_stride%d" % stride, 1, stride))
+        patterns.append(("patch_stride%d_wrap" % stride, 2, stride))
+    patterns += [("ring64_swz_r1", 3, 0), ("ring64_swz_r2", 4, 0), ("ring64_swz_r1r2", 5, 0),
+                 ("ring128_swz_r1_lo", 6, 0), ("ring128_swz_r1_hi", 6, 1),
+                 ("ring128_swz_r7r3_lo", 7, 0), ("ring128_swz_r7r3_hi", 7, 1)]
+    for name, mode, prm in patterns:
+        ms = _time(torch, lambda: lib.tgp_lds_pattern(pat_iters, mode, prm, CUS, out.data_ptr(), s), 5)
+        nb = CUS * 8 * pat_iters * 12 * 1024
+        res["lds_pattern_%s_bytes_per_clk_cu" % name] = round(
             nb / ms / 1e9 * 1e12 / (CUS * CLOCK_GHZ * 1e9), 1)
     return res
 
