@@ -53,6 +53,7 @@ def _lib():
     lib.tgp_valu.argtypes = [i, i, i, i, vp, vp]
     lib.tgp_mfma_lds.argtypes = [i, i, i, vp, vp, vp]
     lib.tgp_lds_pattern.argtypes = [i, i, i, i, vp, vp]
+    lib.tgp_vmem_batch.argtypes = [i, i, vp, ctypes.c_ulonglong, i, i, i, vp, vp]
     return lib
 
 
@@ -158,6 +159,20 @@ def measure() -> dict:
         nb = CUS * 4 * lds_iters * 8 * 1024
         res["lds_frag_stride%d_bytes_per_clk_cu" % stride] = round(
             nb / ms / 1e9 * 1e12 / (CUS * CLOCK_GHZ * 1e9), 1)
+    # One wave's batch of n 1 KB loads, then a wait: ns per batch, from an
+    # L2-resident 1 MB window and from a 1 GB window (HBM), one wave per CU
+    # and eight.
+    big = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(3)
+    vb_iters = 400
+    for window, wname in ((1 << 20, "l2"), (1 << 30, "hbm")):
+        for waves in (1, 8):
+            for mode, mname in ((0, "lds"), (1, "vgpr")):
+                for n in (1, 4, 16):
+                    ms = _time(torch, lambda: lib.tgp_vmem_batch(mode, n, big.data_ptr(), window, vb_iters,
+                                                                  CUS, waves, out.data_ptr(), s), 3)
+                    res["vmem_batch_%s_%s_%dw_n%d_ns" % (mname, wname, waves, n)] = round(
+                        ms * 1e6 / vb_iters, 1)
+    del big
     # Fragment layouts (peaks.hip, pk_lds_pattern): 8 waves per CU, 12 reads
     # in flight per wave; bytes per clock per CU.
     pat_iters = 4000
