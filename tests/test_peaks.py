@@ -10,5 +10,5 @@ def test_peaks_library_exports():
     path = peaks.LIB if os.path.exists(peaks.LIB) else peaks.build()
     lib = ctypes.CDLL(path)
     for name in ("tgp_copy", "tgp_copy_dma", "tgp_read", "tgp_write", "tgp_mfma", "tgp_mfma_lds", "tgp_valu",
-                 "tgp_lds", "tgp_lds_stride", "tgp_lds_pattern"):
+                 "tgp_lds", "tgp_lds_stride", "tgp_lds_pattern", "tgp_vmem_batch"):
         assert getattr(lib, name) is not None
