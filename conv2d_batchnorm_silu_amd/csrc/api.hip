@@ -500,10 +500,11 @@ tg_status static_scratch(void** out) {
     return TG_OK;
 }
 
-// Training mode keeps t1 in y (the BatchNorm+SiLU pass then works on y in
-// place). Workspace: [scale fp32 [C]][bias fp32 [C]][statistics partials:
-// fp64 row-block sums, or the 1x1 kernel's per-workgroup triples], each
-// piece 256-byte aligned.
+// Training mode: the 1x1 layer takes its statistics from a conv pass that
+// stores nothing and then runs the fused kernel; the other layers keep t1 in
+// y (the BatchNorm+SiLU pass then works on y in place). Workspace: [scale
+// fp32 [C]][bias fp32 [C]][statistics partials: fp64 row-block sums, or the
+// 1x1 kernel's per-workgroup triples], each piece 256-byte aligned.
 struct TrainWs {
     size_t scale, bias, partial, total;
 };
@@ -555,16 +556,24 @@ tg_status train_core(const tg_conv_bn_silu_plan* plan, const void* x, const void
     double* partial = (double*)(ws + L.partial);
     hipError_t e;
     if (kernel == TG_KERNEL_IGEMM && plan->cu_waves > 0 && !plan->unfused && !plan->split && !f32) {
-        // The 1x1 kernel: t1 -> y with the statistics in its epilogue (at
-        // most 12 waves: the statistics take registers).
+        // The 1x1 layer is bound by HBM, not by its arithmetic: its
+        // statistics come from a pass of the conv that reads x and stores
+        // nothing (at most 12 waves: the statistics take registers), and the
+        // fused kernel then computes the conv again with the batch
+        // statistics folded into scale and bias. That reads x twice instead
+        // of writing t1 and reading and writing it again, and y is the
+        // BatchNorm+SiLU of the fp32 accumulators, as in inference.
         const int ng = g.C_out / 64;
         int nw = plan->cu_waves;
         if (nw > 12) nw = 12 / ng * ng;
-        e = launch_igemm_cu_stats(g, nw, plan->cu_pd, x, w, y, partial, s);
+        e = launch_igemm_cu_stats(g, nw, plan->cu_pd, x, w, partial, s);
         if (e != hipSuccess) return TG_ERR_HIP;
         e = launch_bn_train_finalize_chan(partial, igemm_cu_stats_grid(g), g.M, g.C_out, gamma,
                                           beta, eps, momentum, running_mean, running_var,
                                           batch_mean, batch_var, scale, bias, s);
+        if (e != hipSuccess) return TG_ERR_HIP;
+        e = launch_conv(plan, g, kernel, plan->epi, x, w, scale, bias, y, s);
+        return e == hipSuccess ? TG_OK : TG_ERR_HIP;
     } else {
         // 1. conv -> t1 in y (identity epilogue: scale/bias are not read)
         e = launch_conv(plan, g, kernel, EPI_IDENTITY, x, w, scale, bias, y, s);

@@ -26,11 +26,13 @@
 //     exact count that leaves the stores issued after it in flight.
 //   * Results go through a small wave-private LDS tile so that each store
 //     instruction writes whole 128-byte pieces of 8 pixel rows.
-//   * Training mode (STATS): the epilogue writes the conv output t1 and
-//     accumulates the per-channel batch statistics from the fp32
-//     accumulators on the way ("Kernel Fusion", cheatsheet page: a reduction
-//     next to elementwise work takes one or two passes), so t1 is written
-//     once and read once, by the BatchNorm+SiLU pass. Each lane sums
+//   * Training mode (STATS): the kernel accumulates the per-channel batch
+//     statistics from the fp32 accumulators ("Kernel Fusion", cheatsheet
+//     page: a reduction next to elementwise work takes one or two passes)
+//     and stores nothing; the training call then runs the fused kernel with
+//     the folded batch statistics, which computes the conv again (the layer
+//     is bound by HBM, and reading x twice costs less than writing t1 and
+//     reading and writing it again). Each lane sums
 //     d = acc - shift and d^2 over its pixels, with one shift per channel
 //     shared by the 16 lanes of a row (a value of the channel, so that the
 //     sum of squares does not cancel when the mean is far from 0); the
@@ -137,6 +139,7 @@ __device__ __forceinline__ void cu_chan_merge(double& n, double& mean, double& m
     n = nt;
 }
 
+// STATS: the per-workgroup statistics into stats and nothing stored to y.
 template <int EPI, bool NT, int PD, bool OUT8, bool RES, bool STATS>
 __global__ __launch_bounds__(STATS ? kCuStatsThreads : 1024) void conv2d_bn_silu_igemm_cu(
     const f16* __restrict__ x, const f16* __restrict__ w, const float* __restrict__ scale,
@@ -248,7 +251,8 @@ __global__ __launch_bounds__(STATS ? kCuStatsThreads : 1024) void conv2d_bn_silu
         // Exact wait for block blk's two loads. Each iteration issues two
         // loads (after its MFMAs) and two stores, so they are followed by
         // 2*(PD-1-it) + 4*it operations while it < PD and 4*PD-2 afterwards.
-        if (it < PD) cu_wait_vmcnt<2 * (PD - 1)>(); else cu_wait_vmcnt<4 * PD - 2>();
+        // Without stores (STATS) only the other PD - 1 blocks' loads follow.
+        if (STATS || it < PD) cu_wait_vmcnt<2 * (PD - 1)>(); else cu_wait_vmcnt<4 * PD - 2>();
         const int buf = it % PD;
         const f16* xb = (const f16*)(lds + L.x_off) + (wave * PD + buf) * 1024;
         half8_t xc[KS];
@@ -303,6 +307,7 @@ __global__ __launch_bounds__(STATS ? kCuStatsThreads : 1024) void conv2d_bn_silu
 #pragma unroll
         for (int d = 0; d + 1 < PD; ++d) q[d] = q[d + 1];
         q[PD - 1] = nb;
+        if constexpr (STATS) continue;
 #pragma unroll
         for (int j = 0; j < NF / 2; ++j) {
             half8_t h;
@@ -449,7 +454,7 @@ int igemm_cu_stats_grid(const ConvGeom& g) {
 }
 
 hipError_t launch_igemm_cu_stats(const ConvGeom& g, int nwaves, int pd, const void* x,
-                                 const void* w, void* t1, double* stats, hipStream_t s) {
+                                 const void* w, double* stats, hipStream_t s) {
     if (!igemm_cu_serves(g) || g.out8 || g.res || nwaves < 1 || nwaves > kCuStatsThreads / 64 ||
         nwaves % (g.C_out / kCuCW) != 0)
         return hipErrorInvalidValue;
@@ -457,12 +462,14 @@ hipError_t launch_igemm_cu_stats(const ConvGeom& g, int nwaves, int pd, const vo
     if (grid == 0) return hipSuccess;
     if (pd <= 1)
         return launch_cu_t<EPI_IDENTITY, false, 1, false, false, true>(g, grid, nwaves, x, w,
-                                                                      nullptr, nullptr, t1, s, stats);
+                                                                      nullptr, nullptr, nullptr, s,
+                                                                      stats);
     if (pd == 2)
         return launch_cu_t<EPI_IDENTITY, false, 2, false, false, true>(g, grid, nwaves, x, w,
-                                                                      nullptr, nullptr, t1, s, stats);
+                                                                      nullptr, nullptr, nullptr, s,
+                                                                      stats);
     return launch_cu_t<EPI_IDENTITY, false, 3, false, false, true>(g, grid, nwaves, x, w, nullptr,
-                                                                  nullptr, t1, s, stats);
+                                                                  nullptr, nullptr, s, stats);
 }
 
 }  // namespace tg

@@ -125,12 +125,12 @@ hipError_t launch_silu_apply(bool f32, const void* t2, void* y, long long total,
 // t1 [M][C] into row-block partials, then scale/bias (and running estimates).
 void bn_train_grid(int M, int* R, int* GX);
 size_t bn_train_partial_bytes(int M, int C);
-// Training mode with the statistics in the 1x1 kernel's epilogue: t1 into y
-// and one (count, mean, M2) triple per workgroup and channel into stats
-// (igemm_cu_stats_grid(g) x C_out x 3 doubles); then the fixed-order merge.
+// Training mode, statistics pass of the 1x1 kernel: one (count, mean, M2)
+// triple per workgroup and channel into stats (igemm_cu_stats_grid(g) x
+// C_out x 3 doubles; the fixed-order merge follows); nothing else stored.
 int igemm_cu_stats_grid(const ConvGeom& g);
 hipError_t launch_igemm_cu_stats(const ConvGeom& g, int nwaves, int pd, const void* x,
-                                 const void* w, void* t1, double* stats, hipStream_t s);
+                                 const void* w, double* stats, hipStream_t s);
 size_t bn_train_chan_bytes(int G, int C);
 hipError_t launch_bn_train_finalize_chan(const double* stats, int G, int M, int C,
                                          const float* gamma, const float* beta, float eps,

@@ -131,14 +131,17 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan *plan, const void *x, c
  * are a reduction over every block's outputs, which "Kernel Fusion"
  * (cheatsheet page, passages on reductions and on synchronization
  * boundaries) says cannot be fused without a kernel boundary, so the call
- * runs in passes on `stream`: the plan's conv kernel writes the conv output
- * t1 into y; the 1x1 kernel forms the per-channel statistics in its own
- * epilogue from the fp32 accumulators (count, mean and squared deviations
- * per workgroup, fp64), the other kernels are followed by a reduction over
- * t1 (fp64 sums); a small kernel combines the partials in a fixed order
- * (results are deterministic) and folds them into one scale and one bias;
- * a streaming kernel applies BatchNorm and SiLU to y in place. t1 is
- * written once and read once. gamma, beta: device fp32 [C_out]. running_mean/running_var:
+ * runs in passes on `stream`. 1x1 layers (the one-workgroup-per-CU
+ * kernel): a pass of the conv that reads x and stores nothing forms the
+ * per-channel statistics from the fp32 accumulators (count, mean and
+ * squared deviations per workgroup, fp64); a small kernel combines them in
+ * a fixed order (results are deterministic) and folds them into one scale
+ * and one bias; the fused kernel then computes the conv again and writes y
+ * (the layer is bound by HBM: reading x twice costs less than writing and
+ * re-reading t1). Other layers: the plan's conv kernel writes the conv
+ * output t1 into y, a reduction over t1 forms fp64 partial sums, the same
+ * fixed-order combine and fold follow, and a streaming kernel applies
+ * BatchNorm and SiLU to y in place (t1 written once and read once). gamma, beta: device fp32 [C_out]. running_mean/running_var:
  * device fp32 [C_out] updated in place as r = (1-momentum)*r +
  * momentum*batch_value, with the unbiased variance var_k*M/(M-1); both NULL
  * for no update. batch_mean/batch_var: device fp32 [C_out] outputs (the

@@ -3,16 +3,18 @@
 
 Bars (no NaN anywhere): y as for the inference path, |gpu - oracle| <=
 1e-2 * max(1, |oracle|) for fp16 and 1e-4 * max(1, |oracle|) for fp32. A
-tighter bound follows from the arithmetic: the conv output t1 is stored in the
-plan's dtype before the statistics and the normalisation read it, so for fp16
-each normalised value carries t1's rounding (2^-11 relative of |t1|) scaled by
-gamma/sigma, plus y's own rounding; with the seeded data (|t1|/sigma below
-about 6, gamma <= 1.5) that is below 5e-3 * max(1, |oracle|). The batch mean
-and (biased) variance and the updated running estimates are fp32 results of
-fp64 sums over rounded t1 (over the fp32 accumulators for the 1x1 kernel,
-which forms them in its epilogue): within 1e-3 * max(1, |oracle|) for fp16
-and 1e-5 for fp32. The reductions combine their partials in a fixed order, so
-two calls give bit-identical results.
+tighter bound follows from the arithmetic: outside the 1x1 layer the conv
+output t1 is stored in the plan's dtype before the statistics and the
+normalisation read it, so for fp16 each normalised value carries t1's
+rounding (2^-11 relative of |t1|) scaled by gamma/sigma, plus y's own
+rounding; with the seeded data (|t1|/sigma below about 6, gamma <= 1.5) that
+is below 5e-3 * max(1, |oracle|) (the 1x1 layer normalises the fp32
+accumulators of a second conv pass and carries only y's rounding). The batch
+mean and (biased) variance and the updated running estimates are fp32
+results of fp64 sums over rounded t1 (over the fp32 accumulators for the 1x1
+kernel, which forms them in a statistics-only pass): within
+1e-3 * max(1, |oracle|) for fp16 and 1e-5 for fp32. The reductions combine
+their partials in a fixed order, so two calls give bit-identical results.
 """
 from __future__ import annotations
 
