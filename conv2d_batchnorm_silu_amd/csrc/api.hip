@@ -500,19 +500,25 @@ tg_status static_scratch(void** out) {
     return TG_OK;
 }
 
-// Training mode: the 1x1 layer takes its statistics from a conv pass that
-// stores nothing and then runs the fused kernel; the other layers keep t1 in
-// y (the BatchNorm+SiLU pass then works on y in place). Workspace: [scale
+// Training mode: the 1x1 and stem layers take their statistics from a conv
+// pass that stores nothing and then run the fused kernel; the other layers
+// keep t1 in y (the BatchNorm+SiLU pass then works on y in place). Workspace: [scale
 // fp32 [C]][bias fp32 [C]][statistics partials: fp64 row-block sums, or the
 // 1x1 kernel's per-workgroup triples], each piece 256-byte aligned.
 struct TrainWs {
     size_t scale, bias, partial, total;
 };
-TrainWs train_ws(const ConvGeom& g) {
+TrainWs train_ws(const tg_conv_bn_silu_plan* plan) {
+    const ConvGeom& g = plan->g;
     const size_t vec = round256((size_t)g.C_out * 4);
     size_t part = bn_train_partial_bytes(g.M, g.C_out);
     if (igemm_cu_serves(g)) {
         const size_t chan = bn_train_chan_bytes(igemm_cu_stats_grid(g), g.C_out);
+        if (chan > part) part = chan;
+    }
+    if (plan->stem_wpc > 0 && stem_stats_serves(g)) {
+        const size_t chan =
+            bn_train_chan_bytes(stem_grid(g, stem_stats_wpc(g), plan->stem_rows), g.C_out);
         if (chan > part) part = chan;
     }
     TrainWs t;
@@ -522,7 +528,6 @@ TrainWs train_ws(const ConvGeom& g) {
     t.total = t.partial + round256(part);
     return t;
 }
-TrainWs train_ws(const tg_conv_bn_silu_plan* plan) { return train_ws(plan->g); }
 
 // Argument checks shared by the training entry points.
 tg_status train_check(const tg_conv_bn_silu_plan* plan, const void* x, const void* w,
@@ -543,7 +548,7 @@ tg_status train_core(const tg_conv_bn_silu_plan* plan, const void* x, const void
                      float* running_mean, float* running_var, float* batch_mean,
                      float* batch_var, void* y, char* ws, hipStream_t s) {
     const ConvGeom& g = plan->g;
-    const TrainWs L = train_ws(g);
+    const TrainWs L = train_ws(plan);
     const bool f32 = plan->dtype == TG_F32;
     int kernel = plan->kernel;
     if (kernel != TG_KERNEL_SCALAR &&
@@ -571,6 +576,18 @@ tg_status train_core(const tg_conv_bn_silu_plan* plan, const void* x, const void
         e = launch_bn_train_finalize_chan(partial, igemm_cu_stats_grid(g), g.M, g.C_out, gamma,
                                           beta, eps, momentum, running_mean, running_var,
                                           batch_mean, batch_var, scale, bias, s);
+        if (e != hipSuccess) return TG_ERR_HIP;
+        e = launch_conv(plan, g, kernel, plan->epi, x, w, scale, bias, y, s);
+        return e == hipSuccess ? TG_OK : TG_ERR_HIP;
+    } else if (kernel == TG_KERNEL_TILED && plan->stem_wpc > 0 && stem_stats_serves(g) &&
+               !plan->unfused && !plan->split && !f32) {
+        // The stem (HBM-bound as well): the same two passes with the stem
+        // kernel's statistics instance.
+        e = launch_stem_stats(g, plan->stem_rows, x, w, partial, s);
+        if (e != hipSuccess) return TG_ERR_HIP;
+        e = launch_bn_train_finalize_chan(partial, stem_grid(g, stem_stats_wpc(g), plan->stem_rows),
+                                          g.M, g.C_out, gamma, beta, eps, momentum, running_mean,
+                                          running_var, batch_mean, batch_var, scale, bias, s);
         if (e != hipSuccess) return TG_ERR_HIP;
         e = launch_conv(plan, g, kernel, plan->epi, x, w, scale, bias, y, s);
         return e == hipSuccess ? TG_OK : TG_ERR_HIP;

@@ -115,30 +115,6 @@ __host__ __device__ inline CuLayout cu_layout(int C_out, int nwaves, int pd) {
     return L;
 }
 
-// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), left in every
-// lane of the row: pairs, quads (quad permutes), then the other quad of the
-// half row (half mirror) and the other half (mirror). Each step adds two
-// values in either order, so all 16 lanes end with the same bits.
-__device__ __forceinline__ float cu_row_sum16(float v) {
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)); // row_half_mirror
-    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)); // row_mirror
-    return v;
-}
-
-// (n, mean, M2) of the union of two disjoint sets; (0, 0, 0) is the empty set.
-__device__ __forceinline__ void cu_chan_merge(double& n, double& mean, double& m2, double nb,
-                                              double meanb, double m2b) {
-    const double nt = n + nb;
-    if (nt == 0.0) return;
-    const double d = meanb - mean;
-    const double f = nb / nt;
-    mean = mean + d * f;
-    m2 = m2 + m2b + d * d * n * f;
-    n = nt;
-}
-
 // STATS: the per-workgroup statistics into stats and nothing stored to y.
 template <int EPI, bool NT, int PD, bool OUT8, bool RES, bool STATS>
 __global__ __launch_bounds__(STATS ? kCuStatsThreads : 1024) void conv2d_bn_silu_igemm_cu(
@@ -334,13 +310,13 @@ __global__ __launch_bounds__(STATS ? kCuStatsThreads : 1024) void conv2d_bn_silu
         // The 16 lanes of a row share their shifts: add their counts and
         // sums across the row (every lane ends with the row's totals), then
         // form the row's (count, mean, squared deviations) in fp64.
-        const float nrow = cu_row_sum16((float)st_n);  // at most 16 x blocks: exact
+        const float nrow = row_sum16((float)st_n);  // at most 16 x blocks: exact
 #pragma unroll
         for (int f = 0; f < NF; ++f)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                st_s1[f][e] = cu_row_sum16(st_s1[f][e]);
-                st_s2[f][e] = cu_row_sum16(st_s2[f][e]);
+                st_s1[f][e] = row_sum16(st_s1[f][e]);
+                st_s2[f][e] = row_sum16(st_s2[f][e]);
             }
         double sn[NF][4], smean[NF][4], sm2[NF][4];
         const double n0 = (double)nrow;
@@ -378,7 +354,7 @@ __global__ __launch_bounds__(STATS ? kCuStatsThreads : 1024) void conv2d_bn_silu
             for (int r = 0; r < R; ++r) {
                 const double* src =
                     (const double*)(lds + L.x_off + (unsigned)(grp + r * ngroups) * PD * 2048u);
-                cu_chan_merge(n, mean, m2, src[lane * 3], src[lane * 3 + 1], src[lane * 3 + 2]);
+                chan_merge(n, mean, m2, src[lane * 3], src[lane * 3 + 1], src[lane * 3 + 2]);
             }
             double* dst = stats + ((size_t)blockIdx.x * C_out + c0 + lane) * 3;
             dst[0] = n;

@@ -77,10 +77,20 @@ __host__ __device__ inline int stem_band_bytes(int W, int R) {
     return (b + 1023) / 1024 * 1024;
 }
 
-template <int NB, int EPI, int LI>
+// STATS > 0 (training mode, one 32-channel slice; the number of 8-channel
+// blocks whose statistics a lane keeps, C_out / 8, so that no registers hold
+// channels past C_out): instead of the epilogue and the stores, each lane
+// sums d = acc - shift and d^2 over its pixels (one shift per channel: that
+// channel's conv output at the middle pixel of image 0, so that the sum of
+// squares does not cancel when the mean is far from 0), and the workgroup's
+// (count, mean, squared deviations) triple per channel goes to
+// stats[(blockIdx.x * C_out + c) * 3] after fixed-order merges (lanes, then
+// waves), as in the 1x1 kernel.
+template <int NB, int EPI, int LI, int STATS>
 __global__ __launch_bounds__(320) void conv2d_bn_silu_stem(
     const f16* __restrict__ x, const f16* __restrict__ w, const float* __restrict__ scale,
-    const float* __restrict__ bias, f16* __restrict__ y, ConvGeom g, int R, int nbands) {
+    const float* __restrict__ bias, f16* __restrict__ y, ConvGeom g, int R, int nbands,
+    double* __restrict__ stats) {
     static_assert(LI <= 31, "vmcnt range for two bands in flight");
     constexpr int kMaxC = 32 * NB;
     // Band buffers are LI KB each: every band load issues exactly LI 1 KB
@@ -187,6 +197,62 @@ __global__ __launch_bounds__(320) void conv2d_bn_silu_stem(
                             bi[f][i]);
 
     f16* tl = tiles + wave * 32 * kMaxC;
+    // Statistics (STATS): lane (lc, hl) sees pixel lc of each of its groups
+    // and channels 32f + 8(i/4) + 4hl + i%4 of accumulator f, element i.
+    constexpr int SI = STATS > 0 ? 4 * STATS : 1;  // accumulator elements with statistics
+    float st_shift[NB][SI], st_s1[NB][SI], st_s2[NB][SI];
+    int st_n = 0;
+    if constexpr (STATS) {
+        // Channel 32f + lc's shift is its conv output at the middle pixel
+        // of image 0: lane (lc, hl) multiplies its filter fragments A[f][r]
+        // with the same window halves the main loop would read for that
+        // pixel (three 16-byte windows from x, masked as there; four dword
+        // loads each, all in flight together), and the two halves add up.
+        // Images under 2 x 2 outputs take 0 (their values are few and the
+        // padding keeps them spread). Then every lane takes the shifts of its
+        // accumulators' channels.
+        float own[NB];
+#pragma unroll
+        for (int f = 0; f < NB; ++f) own[f] = 0.0f;
+        if (g.P >= 2 && g.Q >= 2) {
+            const int pm = g.P / 2, qm = g.Q / 2;  // input rows 2pm-1.. and columns 2qm-1.. lie inside
+            const long long xbytes = 6LL * g.N * g.H * g.W;
+            const unsigned hmk = hl ? ~0u : 0u;
+            const u32x4_t m = {hmk, hmk | 0xffff0000u, ~hmk, ~hmk};
+            half8_t win[3];
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                const int ih = 2 * pm - 1 + r;
+                const long long a = (long long)ih * rowb + 12 * qm - 12 + 16 * hl;  // image 0
+                u32x4_t u;
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const long long ad = a + 4 * d;
+                    const bool ok = ih < g.H && ad + 4 <= xbytes;
+                    u[d] = ((const unsigned*)x)[ok ? ad / 4 : 0];
+                    u[d] = ok ? u[d] : 0u;
+                }
+                win[r] = __builtin_bit_cast(half8_t, u & m);
+            }
+#pragma unroll
+            for (int f = 0; f < NB; ++f) {
+                float sum = 0.0f;
+#pragma unroll
+                for (int r = 0; r < 3; ++r)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        sum = __builtin_fmaf((float)win[r][e], (float)A[f][r][e], sum);
+                own[f] = sum + __shfl_xor(sum, 32);
+            }
+        }
+#pragma unroll
+        for (int f = 0; f < NB; ++f)
+#pragma unroll
+            for (int i = 0; i < SI; ++i) {
+                st_shift[f][i] = __shfl(own[f], 8 * (i / 4) + 4 * hl + (i % 4));
+                st_s1[f][i] = st_s2[f][i] = 0.0f;
+            }
+    }
     // Window dwords that always meet zero weights: half 0 holds pixel 2q-2
     // (halves 0-2) before 2q-1 and 2q; half 1 holds 2q, 2q+1 (halves 8-11)
     // and nothing of use in halves 12-15.
@@ -242,6 +308,23 @@ __global__ __launch_bounds__(320) void conv2d_bn_silu_stem(
                     acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[f][1], b[1], acc[f], 0, 0, 0);
                     acc[f] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[f][2], b[2], acc[f], 0, 0, 0);
                 }
+                if constexpr (STATS) {
+                    st_n += pok ? 1 : 0;
+                    // Lanes past the band (their window is any in-buffer
+                    // data, their sums may not be finite) add +0: a bit mask
+                    // rather than a select, which the compiler turned into a
+                    // branch per element.
+                    const unsigned pmask = pok ? ~0u : 0u;
+#pragma unroll
+                    for (int f = 0; f < NB; ++f)
+#pragma unroll
+                        for (int i = 0; i < SI; ++i) {
+                            const float d = __builtin_bit_cast(
+                                float, pmask & __builtin_bit_cast(unsigned, acc[f][i] - st_shift[f][i]));
+                            st_s1[f][i] += d;
+                            st_s2[f][i] = __builtin_fmaf(d, d, st_s2[f][i]);
+                        }
+                } else {
 #pragma unroll
                 for (int f = 0; f < NB; ++f)
 #pragma unroll
@@ -271,6 +354,7 @@ __global__ __launch_bounds__(320) void conv2d_bn_silu_stem(
                 asm volatile("" ::: "memory");
                 __builtin_amdgcn_wave_barrier();
                 asm volatile("" ::: "memory");
+                }  // !STATS
                 // Next group of this wave: 128 pixels on.
                 pix += 128;
                 q += 128;
@@ -288,6 +372,55 @@ __global__ __launch_bounds__(320) void conv2d_bn_silu_stem(
         else
             walk(std::false_type{});
         stem_barrier();  // band k consumed; band k+1 ready
+    }
+    if constexpr (STATS) {
+        // Sums over the 32 lanes of each half (the 16 lanes of a DPP row,
+        // then the other row of the half), every lane ending with its
+        // half's totals; then the (count, mean, squared deviations) triple
+        // in fp64.
+        auto sum32 = [](float v) {
+            v = row_sum16(v);
+            return v + __shfl_xor(v, 16);
+        };
+        const float nh = sum32((float)st_n);  // pixels of the half: exact in fp32
+        const double n0 = (double)nh;
+        const double inv_n = nh > 0.0f ? 1.0 / n0 : 0.0;
+        // Wave-local triples in the (now unused) output tiles: channel c of
+        // wave v at ((v * kMaxC + c) * 3).
+        double* wt = (double*)tiles;
+#pragma unroll
+        for (int f = 0; f < NB; ++f)
+#pragma unroll
+            for (int i = 0; i < SI; ++i) {
+                // One channel at a time (the empty asm statements keep their
+                // order): the sums and fp64 values of all of them would
+                // otherwise be live at once and cost the kernel occupancy.
+                asm volatile("" : "+v"(st_s1[f][i]), "+v"(st_s2[f][i]));
+                const double s1 = sum32(st_s1[f][i]), s2 = sum32(st_s2[f][i]);
+                const double mean = nh > 0.0f ? (double)st_shift[f][i] + s1 * inv_n : 0.0;
+                double m2 = s2 - s1 * s1 * inv_n;
+                m2 = m2 > 0.0 ? m2 : 0.0;
+                const int c = 32 * f + 8 * (i / 4) + 4 * hl + (i % 4);
+                if (lc == 0) {
+                    double* dst = wt + (wave * kMaxC + c) * 3;
+                    dst[0] = n0;
+                    dst[1] = mean;
+                    dst[2] = m2;
+                }
+                asm volatile("" ::"v"(mean), "v"(m2) : "memory");
+            }
+        stem_barrier();  // the loader wave has finished: the compute waves alone
+        if (wave == 0 && lane < g.C_out) {
+            double n = 0.0, mean = 0.0, m2 = 0.0;
+            for (int v = 0; v < 4; ++v) {
+                const double* src = wt + (v * kMaxC + lane) * 3;
+                chan_merge(n, mean, m2, src[0], src[1], src[2]);
+            }
+            double* dst = stats + ((size_t)blockIdx.x * g.C_out + lane) * 3;
+            dst[0] = n;
+            dst[1] = mean;
+            dst[2] = m2;
+        }
     }
 }
 
@@ -313,47 +446,84 @@ bool stem_serves(const ConvGeom& g) {
            6LL * g.N * g.H * g.W < (1LL << 31);
 }
 
+int stem_grid(const ConvGeom& g, int wg_per_cu, int R) {
+    const int bands = g.N * ((g.P + R - 1) / R);
+    long long grid = 256LL * (wg_per_cu < 1 ? 1 : wg_per_cu);
+    return grid > bands ? bands : (int)grid;
+}
+
+namespace {
+
+// The stem kernel for (NB, EPI, STATS) with the band buffer size chosen
+// from the image width and band rows.
+template <int NB, int EPI, int STATS>
+hipError_t stem_launch_li(const ConvGeom& g, int grid, int R, const void* x, const void* w,
+                          const float* scale, const float* bias, void* y, double* stats,
+                          hipStream_t s) {
+    const int bands = g.N * ((g.P + R - 1) / R);
+    const int li = stem_band_bytes(g.W, R) / 1024;
+#define TG_STEM_K(LIV)                                                                        \
+    do {                                                                                      \
+        auto k = conv2d_bn_silu_stem<NB, EPI, LIV, STATS>;                                    \
+        const size_t lds = 16 + (size_t)kStemBands * (LIV)*1024 + 4 * 32 * 32 * NB * 2;        \
+        hipError_t e = ensure_dynamic_lds((const void*)k, lds);                               \
+        if (e != hipSuccess) return e;                                                        \
+        hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(320), lds, s, (const f16*)x,         \
+                           (const f16*)w, scale, bias, (f16*)y, g, R, bands, stats);           \
+        return hipGetLastError();                                                             \
+    } while (0)
+    if (li <= 4) TG_STEM_K(4);
+    if (li <= 6) TG_STEM_K(6);
+    if (li <= 8) TG_STEM_K(8);
+    if (li <= 10) TG_STEM_K(10);
+    if (li <= 12) TG_STEM_K(12);
+    if (li <= 14) TG_STEM_K(14);
+    if (li <= 16) TG_STEM_K(16);
+    if (li <= 20) TG_STEM_K(20);
+    if (li <= 24) TG_STEM_K(24);
+    TG_STEM_K(31);
+#undef TG_STEM_K
+}
+
+}  // namespace
+
 hipError_t launch_stem(const ConvGeom& g, int wg_per_cu, int R, int epi, const void* x,
                        const void* w, const float* scale, const float* bias, void* y,
                        hipStream_t s) {
     if (!stem_serves(g) || !stem_rows_ok(g, R)) return hipErrorInvalidValue;
-    const int bands = g.N * ((g.P + R - 1) / R);
-    long long grid = 256LL * (wg_per_cu < 1 ? 1 : wg_per_cu);
-    if (grid > bands) grid = bands;
+    const int grid = stem_grid(g, wg_per_cu, R);
     const int nb = (g.C_out + 31) / 32;
-    const int li = stem_band_bytes(g.W, R) / 1024;
-#define TG_STEM_K(NBV, EPI, LIV)                                                              \
-    do {                                                                                      \
-        auto k = conv2d_bn_silu_stem<NBV, EPI, LIV>;                                          \
-        const size_t lds = 16 + (size_t)kStemBands * (LIV)*1024 + 4 * 32 * 32 * (NBV) * 2;     \
-        hipError_t e = ensure_dynamic_lds((const void*)k, lds);                               \
-        if (e != hipSuccess) return e;                                                        \
-        hipLaunchKernelGGL(k, dim3((unsigned)grid), dim3(320), lds, s, (const f16*)x,         \
-                           (const f16*)w, scale, bias, (f16*)y, g, R, bands);                  \
-        return hipGetLastError();                                                             \
-    } while (0)
-#define TG_STEM_LI(NBV, EPI)                   \
-    do {                                       \
-        if (li <= 4) TG_STEM_K(NBV, EPI, 4);   \
-        if (li <= 6) TG_STEM_K(NBV, EPI, 6);   \
-        if (li <= 8) TG_STEM_K(NBV, EPI, 8);   \
-        if (li <= 10) TG_STEM_K(NBV, EPI, 10); \
-        if (li <= 12) TG_STEM_K(NBV, EPI, 12); \
-        if (li <= 14) TG_STEM_K(NBV, EPI, 14); \
-        if (li <= 16) TG_STEM_K(NBV, EPI, 16); \
-        if (li <= 20) TG_STEM_K(NBV, EPI, 20); \
-        if (li <= 24) TG_STEM_K(NBV, EPI, 24); \
-        TG_STEM_K(NBV, EPI, 31);               \
-    } while (0)
-#define TG_STEM_1(E) TG_STEM_LI(1, E)
-#define TG_STEM_2(E) TG_STEM_LI(2, E)
+#define TG_STEM_1(E) return stem_launch_li<1, E, 0>(g, grid, R, x, w, scale, bias, y, nullptr, s)
+#define TG_STEM_2(E) return stem_launch_li<2, E, 0>(g, grid, R, x, w, scale, bias, y, nullptr, s)
     if (nb == 1) TG_EPI_DISPATCH(epi, TG_STEM_1);
     TG_EPI_DISPATCH(epi, TG_STEM_2);
     return hipErrorInvalidValue;
 #undef TG_STEM_2
 #undef TG_STEM_1
-#undef TG_STEM_LI
-#undef TG_STEM_K
+}
+
+bool stem_stats_serves(const ConvGeom& g) { return stem_serves(g) && g.C_out <= 32; }
+
+// The statistics instance holds up to 127 registers for C_out <= 24 (four
+// waves per SIMD: three workgroups per CU, as the inference kernel) and 151
+// for C_out = 32 (three: two workgroups).
+int stem_stats_wpc(const ConvGeom& g) { return g.C_out <= 24 ? 3 : 2; }
+
+hipError_t launch_stem_stats(const ConvGeom& g, int R, const void* x, const void* w,
+                             double* stats, hipStream_t s) {
+    if (!stem_stats_serves(g) || !stem_rows_ok(g, R) || g.out8 || g.res)
+        return hipErrorInvalidValue;
+    const int grid = stem_grid(g, stem_stats_wpc(g), R);
+#define TG_STEM_ST(CB)                                                                        \
+    return stem_launch_li<1, EPI_IDENTITY, CB>(g, grid, R, x, w, nullptr, nullptr, nullptr, \
+                                               stats, s)
+    switch (g.C_out / 8) {  // C_out % 8 == 0, at most 32
+        case 1: TG_STEM_ST(1);
+        case 2: TG_STEM_ST(2);
+        case 3: TG_STEM_ST(3);
+        default: TG_STEM_ST(4);
+    }
+#undef TG_STEM_ST
 }
 
 }  // namespace tg

@@ -178,4 +178,30 @@ __device__ __forceinline__ int xcd_contiguous_tile(int b, int total) {
     return xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
 }
 
+// Batch statistics (training-mode BatchNorm) of the kernels' epilogues.
+//
+// Sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15), left in every
+// lane of the row: pairs, quads (quad permutes), then the other quad of the
+// half row (half mirror) and the other half (mirror). Each step adds two
+// values in either order, so all 16 lanes end with the same bits.
+__device__ __forceinline__ float row_sum16(float v) {
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));  // quad_perm 1,0,3,2
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));  // quad_perm 2,3,0,1
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)); // row_half_mirror
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)); // row_mirror
+    return v;
+}
+
+// (n, mean, M2) of the union of two disjoint sets; (0, 0, 0) is the empty set.
+__device__ __forceinline__ void chan_merge(double& n, double& mean, double& m2, double nb,
+                                           double meanb, double m2b) {
+    const double nt = n + nb;
+    if (nt == 0.0) return;
+    const double d = meanb - mean;
+    const double f = nb / nt;
+    mean = mean + d * f;
+    m2 = m2 + m2b + d * d * n * f;
+    n = nt;
+}
+
 }  // namespace tg

@@ -108,6 +108,16 @@ bool stem_rows_ok(const ConvGeom& g, int R);
 hipError_t launch_stem(const ConvGeom& g, int wg_per_cu, int R, int epi, const void* x,
                        const void* w, const float* scale, const float* bias, void* y,
                        hipStream_t s);
+// Its workgroup count, and its training-mode statistics pass (C_out <= 32):
+// one (count, mean, M2) triple per workgroup and channel into stats
+// (stem_grid(g, stem_stats_wpc(g), R) x C_out x 3 doubles); nothing else
+// stored. The statistics instance may hold more registers than the
+// inference one and then runs fewer workgroups per CU (all resident).
+int stem_grid(const ConvGeom& g, int wg_per_cu, int R);
+bool stem_stats_serves(const ConvGeom& g);
+int stem_stats_wpc(const ConvGeom& g);
+hipError_t launch_stem_stats(const ConvGeom& g, int R, const void* x, const void* w,
+                             double* stats, hipStream_t s);
 // Tiled direct conv on MFMA (tiled_mfma.hip): K <= 32, C_out <= 32.
 bool tiled_mfma_serves(const ConvGeom& g);
 int tiled_mfma_rows(const ConvGeom& g);

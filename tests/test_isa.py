@@ -87,11 +87,15 @@ def test_nontemporal_y_stores_kept(listings):
     plain stores make the 1x1 layer about 25% slower). A store helper that
     took the hint as a run-time flag once let the compiler merge both
     branches into one plain store; every global store of the 1x1 kernel's
-    non-temporal instantiations and of the stem kernel must keep `nt`."""
+    non-temporal instantiations and of the stem kernel must keep `nt`. The
+    stem's training-statistics instances (last template argument nonzero) store
+    no y, only their per-workgroup statistics, and are not checked."""
     checked = 0
     for src, pat in (("igemm_cu.hip", "igemm_cuILi0ELb1E"), ("stem.hip", "conv2d_bn_silu_stem")):
         for name, body in _kernels(listings[src]):
             if pat not in name:
+                continue
+            if src == "stem.hip" and "ELi0EEEv" not in name:  # last argument: statistics blocks
                 continue
             stores = [l for l in body.splitlines() if l.strip().startswith("global_store")]
             assert stores, name

@@ -85,6 +85,12 @@ SHAPES = [
     Workload("train_large_values", 74, 2, 9, 9, 8, 16, 3, 3, 1, 1, "f16", ("normal", 30.0)),
     # more channels than the statistics block has lanes (640 > 512)
     Workload("train_wide_c640", 76, 2, 5, 6, 16, 640, 1, 1, 1, 0, "f16"),
+    # the stem's statistics pass keeps 1, 3 and 4 channel blocks of 8; 40
+    # channels take the t1 path
+    Workload("train_stem_c8", 77, 3, 22, 18, 3, 8, 3, 3, 2, 1, "f16", ("uniform", -1.0, 1.0)),
+    Workload("train_stem_c24_odd_h", 78, 2, 23, 30, 3, 24, 3, 3, 2, 1, "f16", ("uniform", -1.0, 1.0)),
+    Workload("train_stem_c32", 79, 2, 20, 26, 3, 32, 3, 3, 2, 1, "f16", ("uniform", -1.0, 1.0)),
+    Workload("train_stem_c40", 80, 2, 16, 16, 3, 40, 3, 3, 2, 1, "f16", ("uniform", -1.0, 1.0)),
 ]
 
 
@@ -99,7 +105,7 @@ def test_train_small(wl, kernel):
     check(wl, kernel)
 
 
-@pytest.mark.parametrize("name", ["conv1x1_c64_k256", "conv3x3_c128_k128"])
+@pytest.mark.parametrize("name", ["conv1x1_c64_k256", "conv3x3_c128_k128", "stem3x3s2_k16"])
 def test_train_full_size(name):
     """Full-size workloads in the launch configuration of the fused path:
     every output, and the statistics over all M rows."""
@@ -121,11 +127,11 @@ def test_train_constant_channel():
     assert float(_scaled(got, ref["y"]).max()) <= Y_TIGHT["f16"]
 
 
-@pytest.mark.parametrize("name", ["conv3x3_c128_k128", "conv1x1_c64_k256"])
+@pytest.mark.parametrize("name", ["conv3x3_c128_k128", "conv1x1_c64_k256", "stem3x3s2_k24"])
 def test_train_deterministic(name):
     """Two calls give identical y and batch statistics: the row-block sums
-    (3x3) and the 1x1 kernel's in-epilogue triples are merged in a fixed
-    order whatever the scheduling."""
+    (3x3) and the 1x1 and stem kernels' per-workgroup triples are merged in a
+    fixed order whatever the scheduling."""
     wl = WORKLOADS[name].scaled(N=4)
     d = make_inputs(wl)
     outs = [run_train(wl, d=d)[1] for _ in range(2)]
