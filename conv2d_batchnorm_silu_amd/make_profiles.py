@@ -467,7 +467,7 @@ def write_bench_table(path_json):
              "count (includes launch gaps); timed calls go straight to the C ABI",
              "# split = conv kernel + one BatchNorm+SiLU kernel; unfused = conv, BatchNorm, SiLU; "
              "nchw legs = x NCHW->NHWC + fused + y NHWC->NCHW; train = batch-statistics "
-             "BatchNorm (1x1: statistics-only conv, fold, fused conv; others: conv, statistics, "
+             "BatchNorm (1x1 and stems: statistics-only conv, fold, fused conv; others: conv, statistics, "
              "fold, BatchNorm+SiLU); packed = the fused kernel "
              "reading a filter packed once at load time into its tile order",
              "# cold = a 1 GiB cache flush before every single call, events around that call "

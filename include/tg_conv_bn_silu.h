@@ -132,7 +132,8 @@ tg_status tg_conv_bn_silu_run(const tg_conv_bn_silu_plan *plan, const void *x, c
  * (cheatsheet page, passages on reductions and on synchronization
  * boundaries) says cannot be fused without a kernel boundary, so the call
  * runs in passes on `stream`. 1x1 layers (the one-workgroup-per-CU
- * kernel): a pass of the conv that reads x and stores nothing forms the
+ * kernel) and stems with C_out <= 32: a pass of the conv that reads x and
+ * stores nothing forms the
  * per-channel statistics from the fp32 accumulators (count, mean and
  * squared deviations per workgroup, fp64); a small kernel combines them in
  * a fixed order (results are deterministic) and folds them into one scale
