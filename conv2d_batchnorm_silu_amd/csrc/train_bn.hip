@@ -206,16 +206,19 @@ __global__ __launch_bounds__(kFinChans * kFinPhases) void bn_train_finalize(
                      batch_mean, batch_var, scale, bias);
 }
 
-// Triples from the 1x1 kernel's statistics epilogue: stats[(b*C + c)*3] =
-// (count n_b, mean m_b, sum of squared deviations q_b) of workgroup b; four
-// channels per workgroup, so the loads spread over C/4 compute units. Two
+// Triples from the 1x1 and stem kernels' statistics passes: stats[(b*C + c)*3]
+// = (count n_b, mean m_b, sum of squared deviations q_b) of workgroup b; four
+// channels per workgroup, so the loads spread over C/4 compute units; up to
+// kChanHeld * kFinPhases = 1024 workgroups' triples are loaded at once and
+// kept in registers for the second pass (the stems' 768: one memory latency
+// per channel instead of one per further group of 64). Two
 // fixed-order passes (threads (ph, cl) take b = ph, ph + kFinPhases, ...;
 // phase 0 then adds the phases in order): the mean from sum(n_b*m_b)/M, then
 // the squared deviations as sum(q_b + n_b*(m_b - mean)^2), the exact
 // decomposition of the total about the mean. No term cancels and the result
 // does not depend on scheduling.
 constexpr int kChanChans = 4;   // channels per workgroup of the triple finalize
-constexpr int kChanHeld = 8;    // triples a thread keeps in registers between the passes
+constexpr int kChanHeld = 16;   // triples a thread keeps in registers between the passes
 __global__ __launch_bounds__(kChanChans * kFinPhases) void bn_train_finalize_chan(
     const double* __restrict__ stats, int G, int M, int C, const float* __restrict__ gamma,
     const float* __restrict__ beta, float eps, float momentum, float* __restrict__ running_mean,
