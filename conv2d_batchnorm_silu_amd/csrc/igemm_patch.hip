@@ -97,6 +97,37 @@ __device__ __forceinline__ half8_t pt_lds16(unsigned addr) {
     return r;
 }
 
+// s_waitcnt lgkmcnt(n) for a count known after unrolling (the counter field
+// holds 0..15; larger counts wait for 15, which is stricter).
+__device__ __forceinline__ void pt_wait_lgkm(int n) {
+    switch (n < 15 ? n : 15) {
+#define TG_LGKM(N)                                              \
+    case N:                                                     \
+        asm volatile("s_waitcnt lgkmcnt(" #N ")" ::: "memory"); \
+        break;
+        TG_LGKM(0) TG_LGKM(1) TG_LGKM(2) TG_LGKM(3) TG_LGKM(4) TG_LGKM(5) TG_LGKM(6) TG_LGKM(7)
+        TG_LGKM(8) TG_LGKM(9) TG_LGKM(10) TG_LGKM(11) TG_LGKM(12) TG_LGKM(13) TG_LGKM(14)
+        TG_LGKM(15)
+#undef TG_LGKM
+    }
+}
+
+// Fragment reads of one step are issued in order r = 0..NL-1 (per 32-deep
+// half kk: FN filter fragments, then FM pixel fragments); MFMA m reads
+// filter fragment (kk, i) and pixel fragment (kk, j). The highest read index
+// any of MFMAs 0..m uses:
+template <int FN, int FM>
+__host__ __device__ constexpr int pt_reads_needed(int m) {
+    int hi = 0;
+    for (int k = 0; k <= m; ++k) {
+        const int kk = k / (FN * FM), i = (k / FM) % FN, j = k % FM;
+        const int ra = kk * (FN + FM) + i, rb = kk * (FN + FM) + FN + j;
+        hi = hi > ra ? hi : ra;
+        hi = hi > rb ? hi : rb;
+    }
+    return hi;
+}
+
 template <int BM, int BN, int WM, int WN, int WK, int RING>
 struct PatchShape {
     static_assert(RING == 3 || RING == 4, "filter ring of three or four stages");
@@ -391,8 +422,33 @@ __global__ __launch_bounds__(64 * (WM * WN * WK + 1), 1) void conv2d_bn_silu_ige
     // The last step reads fragments too (one MFMA sequence in the code, not
     // two): at patch offset 0 and a ring stage that the trailing zero-filling
     // filter loads may be writing, values no MFMA uses. The fragment
-    // registers are kept live past the loop's last LDS wait (below), so that
-    // no other value is given a register a late LDS write would overwrite.
+    // registers are kept live past the LDS wait after the loop, so that no
+    // other value is given a register a late LDS write would overwrite.
+    // The fragments of `cur` were read during the previous step, and LDS
+    // operations complete in order: MFMA m waits only for the reads it uses
+    // (all but NL - 1 - pt_reads_needed(m) of them, plus the reads of `nxt`
+    // issued in this step before it), so the step's first MFMAs overlap the
+    // latency of its last fragment reads.
+    // Each fragment then passes through an empty asm statement that claims
+    // to modify it, right after the wait that completes its read: no copy
+    // or use of the register can be placed before that wait.
+    auto frag_ready = [&](Frags& F, int m) {
+        const int need = pt_reads_needed<S::FN, S::FM>(m);
+        const int prev = m == 0 ? -1 : pt_reads_needed<S::FN, S::FM>(m - 1);
+        if (need > prev) {
+            const int issued = m < 2 ? 0 : (m - 2 < NL ? m - 2 : NL);
+            pt_wait_lgkm(NL - 1 - need + issued);
+#pragma unroll
+            for (int r = 0; r < NL; ++r) {
+                if (r <= prev || r > need) continue;
+                const int kk = r / (S::FN + S::FM), q = r % (S::FN + S::FM);
+                if (q < S::FN)
+                    asm volatile("" : "+v"(F.a[kk][q]));
+                else
+                    asm volatile("" : "+v"(F.b[kk][q - S::FN]));
+            }
+        }
+    };
     auto step = [&](int kc, Frags& cur, Frags& nxt) {
         const bool more = kc + 1 < nk;
         const bool row_wait = more && tap_s == 0 && cc == 0;  // first chunk of a filter row
@@ -400,6 +456,7 @@ __global__ __launch_bounds__(64 * (WM * WN * WK + 1), 1) void conv2d_bn_silu_ige
         const unsigned delta = more ? (unsigned)((tap_r * PW + tap_s) * pstride + cc * 128) : 0u;
 #pragma unroll
         for (int m = 0; m < NM; ++m) {
+            frag_ready(cur, m);
             mfma(cur, m);
             if (m == 0) issue(kc + RING - 1);
             if (m == 1) {
@@ -411,7 +468,6 @@ __global__ __launch_bounds__(64 * (WM * WN * WK + 1), 1) void conv2d_bn_silu_ige
 #pragma unroll
         for (int r = NM - 2; r < NL; ++r) read(nxt, r > 0 ? r : 0, st, delta);
         advance();
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     };
     // Pairs of steps in straight-line code (the compiler's wait counts stay
     // exact across the back edge), then an odd last step.
@@ -421,10 +477,14 @@ __global__ __launch_bounds__(64 * (WM * WN * WK + 1), 1) void conv2d_bn_silu_ige
         step(kc + 1, F1, F0);
     }
     if (kc < nk) {  // odd last step: nothing left to fetch
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         issue(kc + RING - 1);
 #pragma unroll
         for (int m = 0; m < NM; ++m) mfma(F0, m);
     }
+    // The last step's fragment reads (values no MFMA uses) land before
+    // their registers are released.
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
     for (int kk = 0; kk < KSW; ++kk) {
 #pragma unroll
