@@ -503,7 +503,7 @@ def main():
     set_settle_ms(args.settle_ms)
     set_cold_reps(args.cold_reps)
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
