@@ -204,6 +204,9 @@ __global__ __launch_bounds__(STATS ? kCuStatsThreads : 1024) void conv2d_bn_silu
     f16* tl = (f16*)(lds + L.t_off) + wave * 16 * kCuTrow;
     const int ocs = (lane % 8) * 8;  // channel within the slice, store phase
     const int orow = lane / 8;       // first tile row, store phase
+    // Element offsets in y of this lane's two stores, less the block's
+    // (every element index of y fits 31 bits, checked at plan creation).
+    const int soff0 = orow * C_out + c0 + ocs, soff1 = soff0 + 8 * C_out;
     // Statistics: lane (lr, lg) sees pixel lr of each of its blocks and
     // channels c0 + 32*(f/2) + 8*lg + 4*(f%2) + e of accumulator f, element e.
     float st_shift[NF][4], st_s1[NF][4], st_s2[NF][4];
@@ -295,14 +298,15 @@ __global__ __launch_bounds__(STATS ? kCuStatsThreads : 1024) void conv2d_bn_silu
             *(half8_t*)(tl + lr * kCuTrow + 32 * j + 8 * lg) = h;
         }
         cu_wave_sync();
+        const int yb = blk * 16 * C_out;  // the block's first element of y
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int row = orow + 8 * i;
             const int m = blk * 16 + row;
             const half8_t v = *(const half8_t*)(tl + row * kCuTrow + ocs);
             if (m < M)
-                store_y8<NT>(y, (long long)m * C_out + c0 + ocs, v, OUT8 ? 1 : 0,
-                             RES ? (const void*)res : nullptr);
+                store_y8<NT>(y, (long long)(unsigned)(yb + (i == 0 ? soff0 : soff1)), v,
+                             OUT8 ? 1 : 0, RES ? (const void*)res : nullptr);
         }
         cu_wave_sync();
     }
